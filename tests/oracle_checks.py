@@ -1,0 +1,190 @@
+"""Checks that pin the oracle to things other than itself.
+
+Each ``check_*`` takes the oracle function(s) under test as arguments and
+raises AssertionError on a mismatch, so that the same check runs against the
+real oracle (must pass) and against a copy with a planted mistake (must fail,
+see test_oracle_controls.py).
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from paged_kv_attention_walk_amd import synth
+
+D = 256
+HQ = 24
+HKV = 4
+
+
+# ---------------------------------------------------------------- decoding
+
+def hand_q4_0_row():
+    """A Q4_0 row built byte by byte: block b has scale 2**(b-3) and code byte
+    j = j | (15 - j) << 4, so element j is j - 8 and element j + 16 is 7 - j."""
+    row = bytearray()
+    expect = []
+    for b in range(8):
+        d = 2.0 ** (b - 3)
+        row += np.float16(d).tobytes()
+        row += bytes((j | ((15 - j) << 4)) for j in range(16))
+        expect += [(j - 8) * d for j in range(16)] + [(7 - j) * d for j in range(16)]
+    return np.frombuffer(bytes(row), dtype=np.uint8), np.array(expect)
+
+
+def hand_q8_0_row():
+    """A Q8_0 row: every block has scale 2**-7 (fp16 bits 0x2000) and codes
+    walking through -127..127; value = code / 128 exactly."""
+    row = bytearray()
+    expect = []
+    codes = list(range(-127, 128))
+    k = 0
+    for b in range(8):
+        row += bytes([0x00, 0x20])                    # 2**-7, little-endian
+        for i in range(32):
+            c = codes[k % len(codes)]
+            k += 7
+            row += int(c & 0xFF).to_bytes(1, "little")
+            expect.append(c / 128.0)
+    return np.frombuffer(bytes(row), dtype=np.uint8), np.array(expect)
+
+
+def check_closed_forms(decode):
+    """decode(rows, kind) -> float64 values."""
+    r, e = hand_q4_0_row()
+    got = decode(r[None], "q4_0")[0]
+    assert np.array_equal(got, e), "Q4_0 hand-built row"
+    r, e = hand_q8_0_row()
+    got = decode(r[None], "q8_0")[0]
+    assert np.array_equal(got, e), "Q8_0 hand-built row"
+    # F16 bit patterns: 1, -2, 65504, smallest subnormal 2**-24, -0.
+    bits = np.zeros(256, dtype=np.uint16)
+    bits[:5] = [0x3C00, 0xC000, 0x7BFF, 0x0001, 0x8000]
+    got = decode(bits.view(np.uint8)[None], "f16")[0]
+    assert list(got[:5]) == [1.0, -2.0, 65504.0, 2.0 ** -24, 0.0] and np.signbit(got[4])
+    assert np.all(got[5:] == 0)
+    # BF16 bit patterns: 1, -5, 2**-133 (smallest subnormal), 3.0e38-ish.
+    bits = np.zeros(256, dtype=np.uint16)
+    bits[:4] = [0x3F80, 0xC0A0, 0x0001, 0x7F7F]
+    got = decode(bits.view(np.uint8)[None], "bf16")[0]
+    assert got[0] == 1.0 and got[1] == -5.0 and got[2] == 2.0 ** -133
+    assert got[3] == float(np.frombuffer(np.uint32(0x7F7F0000).tobytes(), dtype=np.float32)[0])
+
+
+def check_scale_position(decode, fixture):
+    """Q4_0 block v's scale sits at byte 18*v of the row (fixture).  Codes are
+    all 9 (value +1 * scale) so block v decodes to its scale; scales are
+    distinct powers of two."""
+    row = np.full(144, 0x99, dtype=np.uint8)           # both nibbles 9
+    for v, off in enumerate(fixture["scale_byte_in_row"]):
+        assert off == fixture["piece_bytes"] * v + 2 * v
+        row[off:off + 2] = np.frombuffer(np.float16(2.0 ** v).tobytes(), dtype=np.uint8)
+    got = decode(row[None], "q4_0")[0]
+    for v in range(8):
+        assert np.all(got[32 * v:32 * v + 32] == 2.0 ** v), f"block {v}"
+
+
+# ---------------------------------------------------------------- attention
+
+def sdpa_reference(q, k, v, seq_len, scale):
+    """torch.nn.functional.scaled_dot_product_attention in float64 on the CPU.
+    q [T][HQ][D]; k, v [HKV][L][D] float64.  Query head h reads KV head
+    h // 6 (expanded with repeat_interleave); token t sees keys <= L-T+t.
+    Rows with no visible key are returned as NaN (excluded by callers)."""
+    T = q.shape[0]
+    L = k.shape[1]
+    qt = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2))).double()      # [HQ][T][D]
+    kt = torch.from_numpy(k).double().repeat_interleave(HQ // HKV, dim=0)           # [HQ][L][D]
+    vt = torch.from_numpy(v).double().repeat_interleave(HQ // HKV, dim=0)
+    pos = torch.arange(L)[None, :]
+    last = (seq_len - T + torch.arange(T))[:, None]
+    mask = pos <= last                                                              # [T][L]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt[None], kt[None], vt[None], attn_mask=mask[None, None], scale=scale)[0]
+    out = out.numpy().transpose(1, 0, 2)                                            # [T][HQ][D]
+    empty = ~mask.any(dim=1).numpy()
+    out = out.copy()
+    out[empty] = np.nan
+    return out
+
+
+def brute_force(q, k, v, seq_len, scale):
+    """Pure-Python loops (tiny inputs only): returns out [T][HQ][D], lse [T][HQ]."""
+    T = q.shape[0]
+    out = np.zeros((T, HQ, D))
+    lse = np.full((T, HQ), -math.inf)
+    for t in range(T):
+        visible = [j for j in range(seq_len) if j <= seq_len - T + t]
+        for h in range(HQ):
+            kv = h // (HQ // HKV)
+            if not visible:
+                continue
+            logits = []
+            for j in visible:
+                acc = 0.0
+                for d in range(D):
+                    acc += float(q[t, h, d]) * float(k[kv, j, d])
+                logits.append(acc * scale)
+            m = max(logits)
+            w = [math.exp(x - m) for x in logits]
+            tot = math.fsum(w)
+            for d in range(D):
+                out[t, h, d] = math.fsum(w[i] * float(v[kv, j, d]) for i, j in enumerate(visible)) / tot
+            lse[t, h] = m + math.log(tot)
+    return out, lse
+
+
+def check_against_sdpa(decode_sequence, cases):
+    """cases: iterable of (q [T][HQ][D], k, v [HKV][L][D], L, scale)."""
+    for (q, k, v, L, scale) in cases:
+        got, _ = decode_sequence(q, k, v, L, scale)
+        ref = sdpa_reference(q, k, v, L, scale)
+        ok = ~np.isnan(ref)
+        assert np.all(got[~ok] == 0), "rows with no visible key must be 0"
+        denom = max(1e-300, np.abs(ref[ok]).max()) if ok.any() else 1.0
+        err = np.abs(got[ok] - ref[ok]).max() / denom if ok.any() else 0.0
+        assert err <= 1e-12, f"SDPA mismatch {err:.3e} (L={L}, T={q.shape[0]})"
+
+
+def check_against_brute_force(decode_sequence, cases):
+    for (q, k, v, L, scale) in cases:
+        got, glse = decode_sequence(q, k, v, L, scale)
+        ref, rlse = brute_force(q, k, v, L, scale)
+        denom = max(1e-300, np.abs(ref).max())
+        assert np.abs(got - ref).max() <= 1e-12 * denom, f"brute force out (L={L})"
+        fin = np.isfinite(rlse)
+        assert np.array_equal(fin, np.isfinite(glse)), "lse finiteness"
+        assert np.all(np.abs(glse[fin] - rlse[fin]) <= 1e-12 * (1 + np.abs(rlse[fin]))), "brute force lse"
+
+
+def random_sequence_case(rng, L, T, kind_k, kind_v, scale=1 / 16, q_scale=1.0, value_scale=1.0):
+    """Decoded-float test data for one sequence, made by encoding random values
+    and decoding with ``decode`` later by the caller.  Returns encoded rows."""
+    q = rng.standard_normal((T, HQ, D)).astype(np.float32) * np.float32(q_scale)
+    kx = rng.standard_normal((HKV, L, D)).astype(np.float32) * np.float32(value_scale)
+    vx = rng.standard_normal((HKV, L, D)).astype(np.float32) * np.float32(value_scale)
+    return q, synth.encode(kx, kind_k), synth.encode(vx, kind_v)
+
+
+# ---------------------------------------------------------------- paging
+
+def check_paged_equals_contiguous(paged_decode, contiguous_decode, pages=(16, 48, 128, 256, 512),
+                                  seed=0, kinds=("q4_0", "q8_0", "f16", "bf16")):
+    """Two or more sequences' pages shuffled through one pool: the paged result
+    must equal the contiguous result exactly (same float64 arithmetic on the
+    same logical rows)."""
+    rng = np.random.default_rng(seed)
+    for P in pages:
+        for kind in kinds:
+            lens = [int(x) for x in rng.integers(1, 3 * P, size=3)] + [0]
+            T = int(rng.integers(1, 5))
+            w = synth.make_workload("t", lens, T, kind, kind, P, table="shuffled",
+                                    seed=int(rng.integers(1 << 30)), n_blocks=sum(
+                                        synth.blocks_needed(L, P) for L in lens) + 3)
+            max_len = max(lens)
+            kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], lens, max_len)
+            vc = synth.contiguous_from_table(w["v_pool"], w["block_table"], lens, max_len)
+            a, al = paged_decode(w["q"], w["k_pool"], w["v_pool"], kind, kind, w["block_table"], lens, 1 / 16)
+            b, bl = contiguous_decode(w["q"], kc, vc, kind, kind, lens, 1 / 16)
+            assert np.array_equal(a, b) and np.array_equal(al, bl), f"paged != contiguous (P={P}, {kind})"
