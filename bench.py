@@ -1,0 +1,227 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ragged|uniform|f16]
+
+A step is one pa_decode call -- plan, block-table walk, K/V stream, dequant,
+QK^T, online softmax, PV, chunk epilogue, LSE merge -- over the ragged
+131072 + 7 x 8192 Q4_0 workload (16-token pages, interleaved table), with
+inputs resident in HBM.  The headline is cold: consecutive steps rotate over
+replicas of the pools whose total exceeds twice the 256 MB last-level cache,
+so K/V bytes come from HBM.  Prints one JSON line.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention-step ms, effective K/V GB/s (% HBM peak), paged÷contiguous ratio"
+HBM_PEAK_GBPS = 8000.0
+SPLIT_KERNEL = "split_valu_kernel"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ragged", choices=["ragged", "uniform", "f16"])
+    ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
+    ap.add_argument("--no-contiguous", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("pa_kernels.hip", "pa_internal.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_attention_walk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM traffic per launch measured with rocprofv3 counters, if the kernel
+    source is unchanged since the counters were taken (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload_name}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """The float64 oracle, as it stands, on a bounded sample of the workload:
+    one 8192-position sequence of it (all 24 query heads), repeated for about
+    `seconds`.  Reported in K/V GB/s like the GPU value."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import attention
+    s = 1 if len(w["seq_lens"]) > 1 else 0
+    L = int(w["seq_lens"][s])
+    bt = w["block_table"][s:s + 1]
+    lens = w["seq_lens"][s:s + 1]
+    q = w["q"][s:s + 1]
+    per = L * 4 * (144 if w["k_kind"] == "q4_0" else 512) * 2
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        attention.paged_decode(q, w["k_pool"], w["v_pool"], w["k_kind"], w["v_kind"], bt, lens, w["scale"])
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(per * n / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"sequence {s} of the workload ({L} positions, 24 query heads, 1 token), {n} runs in "
+                      f"{dt:.1f} s on the host; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from paged_kv_attention_walk_amd import binding as pb
+    from paged_kv_attention_walk_amd import synth
+
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    if args.workload == "ragged":
+        w = synth.config3()
+    elif args.workload == "uniform":
+        w = synth.config2()
+    else:
+        w = synth.config1()
+    print(f"[bench] workload {w['name']} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    n_seq, T, P = len(w["seq_lens"]), w["n_qtok"], w["page_size"]
+    kv = pb.kv_type(w["k_kind"], w["v_kind"])
+    kv_bytes = w.kv_bytes
+    pool_bytes = w["k_pool"].nbytes + w["v_pool"].nbytes
+    reps = args.replicas or max(1, min(16, int(np.ceil(2 * 2 * 256e6 / pool_bytes))))
+    dq = torch.from_numpy(w["q"]).cuda()
+    dlens = torch.from_numpy(w["seq_lens"]).cuda()
+    k0 = torch.from_numpy(w["k_pool"]).cuda()
+    v0 = torch.from_numpy(w["v_pool"]).cuda()
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
+    bts = [torch.from_numpy(w["block_table"]).cuda() for _ in range(reps)]
+    out = torch.empty((n_seq, T, 24, 256), device="cuda")
+    nbytes = pb.workspace_size(n_seq, T, 0)
+    ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda")
+    bt_stride = w["block_table"].shape[1]
+    nblocks = w["k_pool"].shape[0]
+
+    def timed(calls, steps, warmup):
+        """calls: list of callables taking an event pair; returns (ms/step, split-kernel ms avg)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:          # create the events on this stream
+            a.record()
+            b.record()
+        for i in range(warmup):
+            calls[i % len(calls)](None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            calls[i % len(calls)]((evs[i][0].cuda_event, evs[i][1].cuda_event))
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) * 1e3 / steps
+        ks = [a.elapsed_time(b) for a, b in evs]
+        return dt, float(np.mean(ks)), float(np.median(ks))
+
+    lib = pb.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def make_call(kp, vp, bt, nb):
+        """A step with every pointer and the ext struct prepared up front, so
+        that the timed loop is one ctypes call per step."""
+        ext = pb.make_ext(bt_stride, nb, w["scale"], None, ws, ws.numel() * 4)
+        ext_ref = ctypes.byref(ext)
+        a = (dq.data_ptr(), kp.data_ptr(), vp.data_ptr(), bt.data_ptr() if bt is not None else None,
+             dlens.data_ptr(), n_seq, T, kv, P, out.data_ptr(), stream)
+
+        def f(events):
+            ext.split_events[0], ext.split_events[1] = (events if events else (None, None))
+            st = lib.pa_decode(*a, ext_ref)
+            if st != pb.OK:
+                raise pb.PaError(st, "pa_decode")
+        f.keep = (ext, kp, vp, bt)
+        return f
+
+    def paged_call(r):
+        return make_call(pools[r][0], pools[r][1], bts[r], nblocks)
+
+    cold_ms, cold_k, cold_k_med = timed([paged_call(r) for r in range(reps)], args.steps, args.warmup)
+    hot_ms, hot_k, _ = timed([paged_call(0)], args.steps, args.warmup)
+    err = pb.device_error(ws)
+    if err:
+        raise RuntimeError(f"device error word {err}")
+    res_paged = out.clone()
+
+    contig = None
+    if not args.no_contiguous:
+        max_len = bt_stride * P
+        kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], w["seq_lens"], max_len)
+        vc = synth.contiguous_from_table(w["v_pool"], w["block_table"], w["seq_lens"], max_len)
+        creps = max(1, min(reps, int(np.ceil(2 * 2 * 256e6 / (kc.nbytes + vc.nbytes)))))
+        kc0 = torch.from_numpy(kc).cuda()
+        vc0 = torch.from_numpy(vc).cuda()
+        del kc, vc
+        cpools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(creps - 1)]
+
+        def contig_call(r):
+            return make_call(cpools[r][0], cpools[r][1], None, 0)
+        c_ms, c_k, _ = timed([contig_call(r) for r in range(creps)], args.steps, args.warmup)
+        same = bool(torch.equal(out.view(torch.int32), res_paged.view(torch.int32)))
+        contig = {"ms_per_step": round(c_ms, 4), "split_kernel_ms": round(c_k, 4), "replicas": creps,
+                  "bitwise_equal_to_paged": same}
+        del cpools, kc0, vc0
+
+    gbps = kv_bytes / (cold_ms * 1e-3) / 1e9
+    achieved = kv_bytes / (cold_k * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(cold_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "n_seq": n_seq, "seq_lens": "131072+7x8192" if args.workload == "ragged"
+                   else ",".join(str(int(x)) for x in w["seq_lens"]), "n_qtok": T, "kv": w["k_kind"],
+                   "page_size": P, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "kv_bytes": int(kv_bytes)},
+        "attention_step_ms": round(cold_ms, 4),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "paged_over_contiguous": (round(contig["ms_per_step"] / cold_ms, 4) if contig else None),
+        "contiguous": contig,
+        "hot": {"ms_per_step": round(hot_ms, 4), "split_kernel_ms": round(hot_k, 4),
+                "gbps": round(kv_bytes / (hot_ms * 1e-3) / 1e9, 2)},
+        "replicas": reps,
+        "roofline": {"kernel": SPLIT_KERNEL, "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(w["name"]), "split_kernel_ms_mean": round(cold_k, 5),
+                     "split_kernel_ms_median": round(cold_k_med, 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

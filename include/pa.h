@@ -1,0 +1,281 @@
+/*
+ * pa.h -- C ABI of the paged K/V split-K decode attention library for
+ * MI355X (gfx950), libpa_walk.so.
+ *
+ * The method (Luce-Org/lucebox pull 555, "feat(qwen35): add paged-attention
+ * monolithic decode-only AR foundation", Summary): decode attention with head
+ * size 256 and grouped queries -- 24 query heads over 4 KV heads, so one KV
+ * head serves 6 query heads -- for 1 to 4 new query tokens per sequence, with
+ * K and V stored as F16, BF16, Q8_0 or Q4_0 rows in fixed-size pages that a
+ * per-sequence block table scatters through one pool.  Each sequence's
+ * context is split into chunks; every chunk produces a normalised partial
+ * output and its log-sum-exp, and a stable merge combines them.
+ *
+ * Conventions for every call:
+ *  - the return value is a pa_status: PA_OK (0) or a negative error code;
+ *    no C++ exception crosses the ABI;
+ *  - errors the host can detect are returned before anything is enqueued,
+ *    so a failed call has no effect on the device or on the pool
+ *    (lucebox pull 555, Scope: unsupported combinations fail explicitly);
+ *  - device work is enqueued on the given HIP stream and the call returns
+ *    without waiting for it, unless the description says otherwise;
+ *  - pointers documented as "device" must point to device memory of the
+ *    pool's / stream's device; "host" pointers are read before the call
+ *    returns and may be reused afterwards;
+ *  - a pa_pool is safe to use from several host threads (one mutex per
+ *    pool); device work on different streams is ordered only as stated.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+
+typedef int32_t pa_status;
+
+#define PA_OK               0
+#define PA_ERR_INVALID     (-1) /* an argument is out of range or inconsistent   */
+#define PA_ERR_NOMEM       (-2) /* not enough free pool blocks / device memory     */
+#define PA_ERR_STALE       (-3) /* a handle is stale, already free or repeated     */
+#define PA_ERR_UNSUPPORTED (-4) /* a type, page size or shape this build lacks     */
+#define PA_ERR_HIP         (-5) /* a HIP runtime call failed                       */
+#define PA_ERR_NOT_FOUND   (-6) /* a K/V pointer is not the base of a live pool    */
+
+/* Static text for a status code. */
+const char *pa_status_string(pa_status s);
+
+/* Library version, "major.minor.patch". */
+const char *pa_version(void);
+
+/* ------------------------------------------------------------------ types */
+
+/* K/V row encodings.  A row is one KV head's 256 values at one position.
+ *  PA_F16 / PA_BF16: 256 little-endian 2-byte values, 512 bytes
+ *    (F16: lucebox pull 555, Summary; bf16 K/V: ashhart/TensorFold issue 1156,
+ *    "CUDA: Qwen3.5/3.6 attention caches on the core KV pool", Summary).
+ *  PA_Q8_0: 8 blocks of 34 bytes: fp16 scale d, then 32 int8 codes c;
+ *    value = c*d (block size: achyudh/llama.cpp pull 2, "hip: add RDNA2 gfx1030
+ *    paged attention fallback for adaptive KV streaming", commit on the LDS
+ *    reads of K/V dequantization).  272 bytes.
+ *  PA_Q4_0: 8 blocks of 18 bytes: fp16 scale d, then 16 bytes whose byte j
+ *    holds code c_j in its low nibble and c_{j+16} in its high nibble;
+ *    value = (c-8)*d (size: lucebox pull 555, K/V capacity table; scale
+ *    position: llama.cpp pull 2, same commit).  144 bytes.
+ * A kv_type argument packs the K encoding in bits 0-7 and the V encoding in
+ * bits 8-15; a V field of 0 means "same as K".  This build decodes pairs with
+ * K == V; other pairs return PA_ERR_UNSUPPORTED. */
+enum { PA_F16 = 1, PA_BF16 = 2, PA_Q8_0 = 3, PA_Q4_0 = 4 };
+#define PA_KV_TYPE(k, v) ((int32_t)((k) | ((v) << 8)))
+
+#define PA_HEAD_DIM   256
+#define PA_N_Q_HEADS  24
+#define PA_N_KV_HEADS 4
+#define PA_MAX_QTOK   4
+
+/* Bytes of one row of encoding t (0 for an unknown t). */
+size_t pa_row_bytes(int32_t t);
+
+/* -------------------------------------------------------------- the pool */
+
+/* Pool layout in device memory (K and V pools alike, each with its own row
+ * size): [n_blocks][4 KV heads][page_size][row_bytes] -- inside a page, one
+ * KV head's rows are contiguous.  A block-table entry is a page index.
+ * The layout inside a page is this library's choice; the pages say only that
+ * K and V are pools of fixed-size pages (llama.cpp pull 2, page-table commit). */
+typedef struct pa_pool pa_pool;
+
+/* A block handle: (generation << 32) | page index. */
+typedef uint64_t pa_block;
+
+#define PA_POOL_HOST_ONLY 1u /* allocator only: no device memory, no decode */
+
+typedef struct pa_pool_desc {
+    int32_t  n_blocks;           /* pages in the pool, >= 1                                  */
+    int32_t  page_size;          /* positions per page: a multiple of 16 in [16, 512]        */
+    int32_t  n_kv_heads;         /* must be 4                                                */
+    int32_t  head_dim;           /* must be 256                                              */
+    int32_t  kv_type;            /* PA_KV_TYPE(k, v)                                         */
+    int32_t  device;             /* HIP device ordinal of the pool                           */
+    int32_t  max_seqs;           /* n_seq bound for pa_decode without a caller workspace;
+                                    0 => 512                                                 */
+    int32_t  max_blocks_per_seq; /* block-table row length pa_decode assumes when it is
+                                    given no pa_decode_ext; 0 => n_blocks                    */
+    int32_t  max_append_rows;    /* rows per staging batch of pa_append_kv; 0 => 1024       */
+    uint32_t flags;              /* PA_POOL_HOST_ONLY or 0                                   */
+    void    *k_pool;             /* device memory of the K pool, or NULL: the library
+                                    allocates it (and frees it in pa_pool_destroy).  A
+                                    caller-given pool stays caller-owned, must be 16-byte
+                                    aligned and hold n_blocks pages                          */
+    void    *v_pool;             /* likewise for V                                           */
+} pa_pool_desc;
+
+typedef struct pa_pool_info {
+    void    *k_pool, *v_pool;       /* device base pointers (NULL for a host-only pool)       */
+    void    *workspace;             /* the pool's own decode workspace (device), or NULL       */
+    size_t   workspace_bytes;
+    size_t   k_row_bytes, v_row_bytes;
+    size_t   k_page_bytes, v_page_bytes; /* bytes of one page, all 4 KV heads               */
+    int32_t  n_blocks, n_free, page_size, kv_type, max_blocks_per_seq, max_seqs, device;
+} pa_pool_info;
+
+/* Creates a pool and its block allocator; all blocks start free.  With NULL
+ * k_pool / v_pool the library allocates them (hipMalloc, not zeroed).  Unless
+ * the pool is host-only it also allocates a decode workspace sized for
+ * max_seqs sequences of up to 4 query tokens, pinned and device staging for
+ * pa_append_kv, and registers k_pool so that pa_decode can find the pool from
+ * the pointer.  Errors: PA_ERR_INVALID (null out/desc, n_blocks < 1, bad
+ * head count / head_dim, a K/V pointer already registered), PA_ERR_UNSUPPORTED
+ * (page size, kv_type), PA_ERR_HIP / PA_ERR_NOMEM (device allocation); on
+ * error nothing is allocated and *out is untouched. */
+pa_status pa_pool_create(const pa_pool_desc *desc, pa_pool **out);
+
+/* Waits for the pool's staging copies, frees what the library allocated and
+ * unregisters the pool.  Caller-owned K/V memory is not freed.  NULL is a
+ * no-op.  The caller must not destroy a pool that enqueued decode work still
+ * reads. */
+pa_status pa_pool_destroy(pa_pool *pool);
+
+pa_status pa_pool_get_info(const pa_pool *pool, pa_pool_info *info);
+
+/* Exact transactional allocation (lucebox pull 555, Summary: exact fixed-block
+ * allocator, transactional allocation).  Allocates n blocks, all or none,
+ * always the n lowest free page indices in increasing order (pages come from
+ * the bottom of the pool, as TensorFold issue 1156, Design / Host, takes K/V
+ * pages).  handles[i] (host, may be NULL) receives the handle and indices[i]
+ * (host, may be NULL) the page index to put in block tables.  n == 0 is a
+ * no-op.  Errors: PA_ERR_INVALID (n < 0, n > 0 with both outputs NULL),
+ * PA_ERR_NOMEM (fewer than n free; nothing changes).  Host only. */
+pa_status pa_alloc_blocks(pa_pool *pool, int32_t n, pa_block *handles, int32_t *indices);
+
+/* Frees n blocks, all or none (lucebox pull 555, Summary: stale-handle
+ * detection, immediate release).  Every handle is checked before anything is
+ * released: a page index out of range gives PA_ERR_INVALID; a generation that
+ * is not the page's current one, a page that is not allocated, or the same
+ * page twice in the call gives PA_ERR_STALE; either way nothing is freed.
+ * On success each page's generation advances (so every earlier handle of it
+ * turns stale) and the pages are free at once in host bookkeeping.  Release
+ * is not ordered with device work: blocks that work enqueued on a stream
+ * still reads may be reallocated and then rewritten by pa_append_kv on the
+ * same stream safely (stream order), but not from another stream until that
+ * work has finished (ashhart/TensorFold issue 1156, Activity, returns pages
+ * only once the stream has drained).  Host only. */
+pa_status pa_free_blocks(pa_pool *pool, int32_t n, const pa_block *handles);
+
+/* Writes n_rows new K/V rows into pages (JustVugg/colibri pull 372, "cuda: keep
+ * paged ragged KV resident across decode steps", Summary: only the newly
+ * appended rows are uploaded, in one packed transfer, and a scatter kernel
+ * puts them in place).  Row i goes to page dst_block[i], slot dst_slot[i], for
+ * all 4 KV heads.  k_rows / v_rows (host) are [n_rows][4][row_bytes], already
+ * encoded in the pool's K / V encodings.  dst_block / dst_slot are host
+ * arrays.  The call copies indices and rows into pinned staging, enqueues one
+ * host-to-device copy per staging batch (max_append_rows rows) and one
+ * scatter kernel per batch on `stream`, and returns.  A caller appending
+ * position L of a sequence passes the page holding L and slot L % page_size:
+ * the new row's position is the committed length (lucebox pull 555, Summary,
+ * first-token bookkeeping fix).  Two rows with the same destination leave
+ * the later one.  Errors: PA_ERR_INVALID (n_rows < 0, null arrays with
+ * n_rows > 0, a page index outside the pool or not allocated, a slot outside
+ * [0, page_size)), PA_ERR_HIP; nothing is enqueued on error. */
+pa_status pa_append_kv(pa_pool *pool, int32_t n_rows, const int32_t *dst_block,
+                       const int32_t *dst_slot, const void *k_rows, const void *v_rows,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------ decode */
+
+/* Device-side error bits, ORed into the workspace's error word. */
+#define PA_DEVERR_TABLE  1 /* a block-table entry outside [0, n_pool_blocks)         */
+#define PA_DEVERR_LENGTH 2 /* a seq_len < 0, or beyond the table row / contiguous rows */
+
+typedef struct pa_decode_ext {
+    int32_t  bt_stride;      /* int32 entries per block-table row; in contiguous mode the
+                                rows per sequence are bt_stride * page_size              */
+    int32_t  n_pool_blocks;  /* pages in the pool (bounds for table entries)            */
+    float    scale;          /* softmax scale; 0 => 1/sqrt(256) = 1/16                   */
+    int32_t  reserved;       /* must be 0                                                */
+    float   *lse_out;        /* optional device [n_seq][n_qtok][24] float: natural-log
+                                log-sum-exp of each row's scaled, masked logits; -inf
+                                for a row with no visible key                           */
+    void    *workspace;      /* device scratch of pa_decode_workspace_size() bytes, or
+                                NULL for the pool's own workspace                       */
+    size_t   workspace_bytes;
+    void    *split_events[2];/* optional hipEvent_t pair, recorded on `stream` just
+                                before and after the split kernel (profiling)           */
+} pa_decode_ext;
+
+/* One decode step (lucebox pull 555, Summary; achyudh/llama.cpp pull 2,
+ * split-K decode and page-table commits).
+ *
+ * q        device float [n_seq][n_qtok][24][256]: the new tokens' queries.
+ * k_pool,
+ * v_pool   device pools of the layout above, or, when block_table is NULL,
+ *          contiguous storage [n_seq][4][bt_stride*page_size][row_bytes]
+ *          (the no-table case of one row-address helper: ashhart/TensorFold
+ *          issue 1156, Design / Kernels).
+ * block_table device int32 [n_seq][bt_stride]; entry p of row s is the pool
+ *          page of the sequence's positions [p*page_size, (p+1)*page_size).
+ *          Entries past ceil(seq_len/page_size) are never read.
+ * seq_lens device int32 [n_seq]: stored rows of each sequence, including the
+ *          n_qtok new tokens.  New token t sits at position
+ *          seq_len - n_qtok + t and attends to positions 0..seq_len-n_qtok+t.
+ * n_seq    >= 0 (0 is a no-op).   n_qtok  1..4.
+ * kv_type  PA_KV_TYPE(k, v), matching the pool.   page_size: as the pool.
+ * out      device float [n_seq][n_qtok][24][256]; query head h reads KV head
+ *          h / 6.  A row with no visible key is 0.  All rows of a sequence
+ *          whose length or table entries are out of range are NaN and the
+ *          workspace error word gets PA_DEVERR_* bits; nothing outside the
+ *          pool or table row is ever read (lucebox pull 555, Validation:
+ *          corrupt block-table bounds guards).
+ * stream   HIP stream for the kernels.
+ * ext      NULL: k_pool must be the K base of a live pool (pa_pool_create);
+ *          bt_stride is its max_blocks_per_seq, the scale 1/16, the pool's
+ *          own workspace is used (so calls sharing a pool must not overlap on
+ *          different streams) and n_seq must not exceed its max_seqs.
+ *          Non-NULL: every field as documented; k_pool need not be a pool.
+ *
+ * Two kernels run: a split kernel over (sequence, KV head, context chunk)
+ * work items, whose count and chunk sizes depend only on seq_lens, n_qtok and
+ * the device's compute-unit count (so paged and contiguous storage give
+ * bitwise-equal outputs), and a merge kernel for sequences split in several
+ * chunks.  Errors: PA_ERR_INVALID (null pointers, n_qtok outside 1..4,
+ * misaligned K/V (16 bytes) or q/out (16 bytes), workspace too small,
+ * page_size or kv_type different from the pool's), PA_ERR_UNSUPPORTED,
+ * PA_ERR_NOT_FOUND (ext NULL and k_pool not a pool), PA_ERR_HIP. */
+pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
+                    const int32_t *block_table, const int32_t *seq_lens,
+                    int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                    float *out, hipStream_t stream, const pa_decode_ext *ext);
+
+/* Bytes of decode workspace for n_seq sequences of n_qtok tokens on `device`
+ * (reserved up front, as llama.cpp pull 2 does for its split partials in the
+ * commit that moved them out of run-time pool allocations). */
+pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t *bytes);
+
+/* Reads the error word of a workspace after the work on `stream` finishes
+ * (this call waits for the stream) and, if clear != 0, zeroes it (enqueued on
+ * `stream`).  Pass NULL to read the pool's own workspace through `pool`. */
+pa_status pa_get_device_error(pa_pool *pool, void *workspace, hipStream_t stream,
+                              int32_t clear, int32_t *err);
+
+/* Test hook: copies the logical rows [0, seq_len) of sequence `seq` of one
+ * pool (K or V, row size row_bytes) through its block-table row into dst
+ * (device, [4][seq_len][row_bytes]), using the same row-address helper as the
+ * decode kernels.  block_table NULL selects contiguous storage as in
+ * pa_decode.  Out-of-range table entries leave the affected rows of dst
+ * 0xFF-filled and set PA_DEVERR_TABLE in *err_word (device int32, may be
+ * NULL). */
+pa_status pa_debug_gather(const void *pool, int32_t row_bytes, const int32_t *block_table,
+                          int32_t bt_stride, int32_t n_pool_blocks, int32_t seq, int32_t seq_len,
+                          int32_t page_size, void *dst, int32_t *err_word, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -67,14 +67,16 @@ def gather_rows(pool: np.ndarray, table_row, seq_len: int) -> np.ndarray:
     n_blocks, n_kv_heads, page_size, rb = pool.shape
     out = np.empty((n_kv_heads, seq_len, rb), dtype=np.uint8)
     table_row = np.asarray(table_row)
-    for pos in range(seq_len):
-        lp = pos // page_size
+    # Logical page lp holds positions [lp*P, lp*P + P): slot = pos - lp*P.
+    for lp in range(-(-seq_len // page_size)):
         if lp >= table_row.shape[0]:
-            raise IndexError(f"position {pos} needs table entry {lp}, row has {table_row.shape[0]}")
+            raise IndexError(f"position {lp * page_size} needs table entry {lp}, row has {table_row.shape[0]}")
         b = int(table_row[lp])
         if not (0 <= b < n_blocks):
             raise IndexError(f"table entry {lp} = {b} outside a pool of {n_blocks} pages")
-        out[:, pos, :] = pool[b, :, pos % page_size, :]
+        first = lp * page_size
+        n = min(page_size, seq_len - first)
+        out[:, first:first + n, :] = pool[b, :, 0:n, :]
     return out
 
 

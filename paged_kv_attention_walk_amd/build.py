@@ -1,0 +1,67 @@
+"""Builds libpa_walk.so in-tree with hipcc for gfx950.
+
+    python -m paged_kv_attention_walk_amd.build
+
+Every call compiles from source; nothing is cached between calls.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpa_walk.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+# Packed FP32 instructions are turned off for all device code.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print("+", " ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in r.stdout.splitlines()
+                    if "is not a recognized feature for this target" not in line)
+    if r.returncode != 0:
+        sys.stderr.write(out + "\n")
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = True) -> str:
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    cxx = shutil.which("g++") or "g++"
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I", INCLUDE, "-I", CSRC]
+    hip_inc = ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]
+    objs = []
+    o = os.path.join(BUILD_DIR, "pa_alloc.o")
+    _run([cxx, *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "pa_alloc.cpp"), "-o", o], verbose)
+    objs.append(o)
+    o = os.path.join(BUILD_DIR, "pa_host.o")
+    _run([cxx, *HOST_FLAGS, *inc, *hip_inc, "-c", os.path.join(CSRC, "pa_host.cpp"), "-o", o], verbose)
+    objs.append(o)
+    o = os.path.join(BUILD_DIR, "pa_kernels.o")
+    _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "pa_kernels.hip"), "-o", o], verbose)
+    objs.append(o)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)
+    print(LIB)

@@ -1,0 +1,469 @@
+// Host side of the C ABI declared in include/pa.h: argument checks, pools and
+// their allocator, the pointer registry used by pa_decode without an
+// extension struct, append staging, and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+#include "pa_alloc.h"
+#include "pa_internal.h"
+
+namespace {
+
+using pa::BlockAllocator;
+
+constexpr int kTargetPerCu = 4;      // work items per compute unit the chunk plan aims at
+constexpr int kDefaultMaxSeqs = 512;
+constexpr int kDefaultAppendRows = 1024;
+constexpr int kStagingSlots = 2;
+
+struct Staging {
+  void* host = nullptr;    // pinned
+  void* dev = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;  // recorded after the slot's scatter kernel
+  bool used = false;
+};
+
+}  // namespace
+
+struct pa_pool {
+  pa_pool_desc desc{};
+  int k_type = 0, v_type = 0;
+  int rb_k = 0, rb_v = 0;
+  bool own_k = false, own_v = false;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  Staging staging[kStagingSlots];
+  int next_slot = 0;
+  BlockAllocator alloc;
+  std::mutex mu;
+  explicit pa_pool(int32_t n) : alloc(n) {}
+};
+
+namespace {
+
+std::mutex g_registry_mu;
+std::map<const void*, pa_pool*> g_registry;   // K base pointer -> pool
+
+std::mutex g_cu_mu;
+std::unordered_map<int, int> g_cu_count;
+
+// Compute units of `device` (cached).  0 on failure.
+int cu_count(int device) {
+  std::lock_guard<std::mutex> lk(g_cu_mu);
+  auto it = g_cu_count.find(device);
+  if (it != g_cu_count.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) return 0;
+  g_cu_count[device] = n;
+  return n;
+}
+
+int target_items(int device) {
+  const int cu = cu_count(device);
+  return (cu > 0 ? cu : 256) * kTargetPerCu;
+}
+
+bool type_ok(int t) { return t >= PA_F16 && t <= PA_Q4_0; }
+
+// Splits and checks a kv_type.  Returns PA_OK and the two encodings.
+pa_status parse_kv_type(int32_t kv_type, int* k, int* v) {
+  if (kv_type & ~0xFFFF) return PA_ERR_INVALID;
+  const int kt = kv_type & 0xFF;
+  int vt = (kv_type >> 8) & 0xFF;
+  if (vt == 0) vt = kt;
+  if (!type_ok(kt) || !type_ok(vt)) return PA_ERR_INVALID;
+  if (kt != vt) return PA_ERR_UNSUPPORTED;
+  *k = kt;
+  *v = vt;
+  return PA_OK;
+}
+
+bool page_size_ok(int P) { return P >= 16 && P <= 512 && P % 16 == 0; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+pa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  if (e == hipErrorOutOfMemory) return PA_ERR_NOMEM;
+  return PA_ERR_HIP;
+}
+
+// Sets the device for the current thread and restores the previous one.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+void free_pool_resources(pa_pool* p) {
+  for (auto& s : p->staging) {
+    if (s.done) {
+      (void)hipEventSynchronize(s.done);
+      (void)hipEventDestroy(s.done);
+    }
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    s = Staging{};
+  }
+  if (p->workspace) (void)hipFree(p->workspace);
+  p->workspace = nullptr;
+  if (p->own_k && p->desc.k_pool) (void)hipFree(p->desc.k_pool);
+  if (p->own_v && p->desc.v_pool) (void)hipFree(p->desc.v_pool);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID: return "invalid argument";
+    case PA_ERR_NOMEM: return "out of memory (pool blocks or device memory)";
+    case PA_ERR_STALE: return "stale, already free or repeated block handle";
+    case PA_ERR_UNSUPPORTED: return "unsupported type, page size or shape";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NOT_FOUND: return "pointer is not the base of a live pool";
+    default: return "unknown status";
+  }
+}
+
+const char* pa_version(void) { return "0.1.0"; }
+
+size_t pa_row_bytes(int32_t t) { return static_cast<size_t>(pa::row_bytes_of(t)); }
+
+pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
+  if (!bytes || n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_QTOK) return PA_ERR_INVALID;
+  *bytes = pa::workspace_layout(n_seq, n_qtok, target_items(device)).total;
+  return PA_OK;
+}
+
+pa_status pa_pool_create(const pa_pool_desc* d, pa_pool** out) {
+  if (!d || !out) return PA_ERR_INVALID;
+  if (d->n_blocks < 1 || d->n_kv_heads != PA_N_KV_HEADS || d->head_dim != PA_HEAD_DIM) return PA_ERR_INVALID;
+  if (d->max_seqs < 0 || d->max_blocks_per_seq < 0 || d->max_append_rows < 0) return PA_ERR_INVALID;
+  if (d->flags & ~PA_POOL_HOST_ONLY) return PA_ERR_INVALID;
+  if (!page_size_ok(d->page_size)) return PA_ERR_UNSUPPORTED;
+  int kt = 0, vt = 0;
+  const pa_status ts = parse_kv_type(d->kv_type, &kt, &vt);
+  if (ts != PA_OK) return ts;
+  const bool host_only = (d->flags & PA_POOL_HOST_ONLY) != 0;
+  if (!host_only && ((d->k_pool && !aligned(d->k_pool, 16)) || (d->v_pool && !aligned(d->v_pool, 16))))
+    return PA_ERR_INVALID;
+
+  pa_pool* p = new (std::nothrow) pa_pool(d->n_blocks);
+  if (!p) return PA_ERR_NOMEM;
+  p->desc = *d;
+  p->k_type = kt;
+  p->v_type = vt;
+  p->rb_k = pa::row_bytes_of(kt);
+  p->rb_v = pa::row_bytes_of(vt);
+  if (p->desc.max_seqs == 0) p->desc.max_seqs = kDefaultMaxSeqs;
+  if (p->desc.max_blocks_per_seq == 0) p->desc.max_blocks_per_seq = d->n_blocks;
+  if (p->desc.max_append_rows == 0) p->desc.max_append_rows = kDefaultAppendRows;
+  if (host_only) {
+    p->desc.k_pool = p->desc.v_pool = nullptr;
+    *out = p;
+    return PA_OK;
+  }
+
+  DeviceGuard dg(d->device);
+  if (!dg.ok) {
+    delete p;
+    return PA_ERR_INVALID;
+  }
+  pa_status st = PA_OK;
+  const size_t kbytes = static_cast<size_t>(d->n_blocks) * PA_N_KV_HEADS * d->page_size * p->rb_k;
+  const size_t vbytes = static_cast<size_t>(d->n_blocks) * PA_N_KV_HEADS * d->page_size * p->rb_v;
+  if (!p->desc.k_pool) {
+    st = hip_status(hipMalloc(&p->desc.k_pool, kbytes));
+    p->own_k = st == PA_OK;
+  }
+  if (st == PA_OK && !p->desc.v_pool) {
+    st = hip_status(hipMalloc(&p->desc.v_pool, vbytes));
+    p->own_v = st == PA_OK;
+  }
+  if (st == PA_OK) {
+    p->workspace_bytes = pa::workspace_layout(p->desc.max_seqs, PA_MAX_QTOK, target_items(d->device)).total;
+    st = hip_status(hipMalloc(&p->workspace, p->workspace_bytes));
+    if (st == PA_OK) st = hip_status(hipMemset(p->workspace, 0, 256));
+  }
+  const size_t sbytes = pa::staging_bytes(p->desc.max_append_rows, p->rb_k, p->rb_v);
+  for (int i = 0; st == PA_OK && i < kStagingSlots; ++i) {
+    Staging& s = p->staging[i];
+    s.bytes = sbytes;
+    st = hip_status(hipHostMalloc(&s.host, sbytes, hipHostMallocDefault));
+    if (st == PA_OK) st = hip_status(hipMalloc(&s.dev, sbytes));
+    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&s.done, hipEventDisableTiming));
+  }
+  if (st == PA_OK) {
+    std::lock_guard<std::mutex> lk(g_registry_mu);
+    if (g_registry.count(p->desc.k_pool)) st = PA_ERR_INVALID;
+    else g_registry[p->desc.k_pool] = p;
+  }
+  if (st != PA_OK) {
+    free_pool_resources(p);
+    delete p;
+    return st;
+  }
+  *out = p;
+  return PA_OK;
+}
+
+pa_status pa_pool_destroy(pa_pool* p) {
+  if (!p) return PA_OK;
+  if (p->desc.k_pool) {
+    std::lock_guard<std::mutex> lk(g_registry_mu);
+    auto it = g_registry.find(p->desc.k_pool);
+    if (it != g_registry.end() && it->second == p) g_registry.erase(it);
+  }
+  if (!(p->desc.flags & PA_POOL_HOST_ONLY)) {
+    DeviceGuard dg(p->desc.device);
+    free_pool_resources(p);
+  }
+  delete p;
+  return PA_OK;
+}
+
+pa_status pa_pool_get_info(const pa_pool* p, pa_pool_info* info) {
+  if (!p || !info) return PA_ERR_INVALID;
+  pa_pool* mp = const_cast<pa_pool*>(p);
+  std::lock_guard<std::mutex> lk(mp->mu);
+  std::memset(info, 0, sizeof(*info));
+  info->k_pool = p->desc.k_pool;
+  info->v_pool = p->desc.v_pool;
+  info->workspace = p->workspace;
+  info->workspace_bytes = p->workspace_bytes;
+  info->k_row_bytes = p->rb_k;
+  info->v_row_bytes = p->rb_v;
+  info->k_page_bytes = static_cast<size_t>(PA_N_KV_HEADS) * p->desc.page_size * p->rb_k;
+  info->v_page_bytes = static_cast<size_t>(PA_N_KV_HEADS) * p->desc.page_size * p->rb_v;
+  info->n_blocks = p->desc.n_blocks;
+  info->n_free = p->alloc.n_free();
+  info->page_size = p->desc.page_size;
+  info->kv_type = PA_KV_TYPE(p->k_type, p->v_type);
+  info->max_blocks_per_seq = p->desc.max_blocks_per_seq;
+  info->max_seqs = p->desc.max_seqs;
+  info->device = p->desc.device;
+  return PA_OK;
+}
+
+pa_status pa_alloc_blocks(pa_pool* p, int32_t n, pa_block* handles, int32_t* indices) {
+  if (!p || n < 0) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  if (!handles && !indices) return PA_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(p->mu);
+  switch (p->alloc.alloc(n, handles, indices)) {
+    case BlockAllocator::kOk: return PA_OK;
+    case BlockAllocator::kNoMem: return PA_ERR_NOMEM;
+    default: return PA_ERR_INVALID;
+  }
+}
+
+pa_status pa_free_blocks(pa_pool* p, int32_t n, const pa_block* handles) {
+  if (!p || n < 0 || (n > 0 && !handles)) return PA_ERR_INVALID;
+  if (n == 0) return PA_OK;
+  std::lock_guard<std::mutex> lk(p->mu);
+  switch (p->alloc.free(n, handles)) {
+    case BlockAllocator::kOk: return PA_OK;
+    case BlockAllocator::kStale: return PA_ERR_STALE;
+    default: return PA_ERR_INVALID;
+  }
+}
+
+pa_status pa_append_kv(pa_pool* p, int32_t n_rows, const int32_t* dst_block, const int32_t* dst_slot,
+                       const void* k_rows, const void* v_rows, hipStream_t stream) {
+  if (!p || n_rows < 0) return PA_ERR_INVALID;
+  if (n_rows == 0) return PA_OK;
+  if (!dst_block || !dst_slot || !k_rows || !v_rows) return PA_ERR_INVALID;
+  if (p->desc.flags & PA_POOL_HOST_ONLY) return PA_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(p->mu);
+  const int P = p->desc.page_size;
+  // Validate everything before enqueueing anything; keep only the last row of
+  // each destination so that the later row wins whatever the kernel order.
+  std::unordered_map<int64_t, int32_t> last;
+  last.reserve(static_cast<size_t>(n_rows) * 2);
+  for (int32_t i = 0; i < n_rows; ++i) {
+    const int32_t b = dst_block[i], s = dst_slot[i];
+    if (b < 0 || b >= p->desc.n_blocks || s < 0 || s >= P || !p->alloc.is_allocated(b)) return PA_ERR_INVALID;
+    last[static_cast<int64_t>(b) * P + s] = i;
+  }
+  std::vector<int32_t> order;
+  order.reserve(last.size());
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (last[static_cast<int64_t>(dst_block[i]) * P + dst_slot[i]] == i) order.push_back(i);
+
+  DeviceGuard dg(p->desc.device);
+  if (!dg.ok) return PA_ERR_HIP;
+  const size_t krow = static_cast<size_t>(PA_N_KV_HEADS) * p->rb_k;
+  const size_t vrow = static_cast<size_t>(PA_N_KV_HEADS) * p->rb_v;
+  const int cap = p->desc.max_append_rows;
+  for (size_t first = 0; first < order.size(); first += cap) {
+    const int n = static_cast<int>(std::min(order.size() - first, static_cast<size_t>(cap)));
+    Staging& sl = p->staging[p->next_slot];
+    p->next_slot = (p->next_slot + 1) % kStagingSlots;
+    if (sl.used) {
+      const hipError_t e = hipEventSynchronize(sl.done);   // the slot's previous batch has been consumed
+      if (e != hipSuccess) return hip_status(e);
+    }
+    uint8_t* h = static_cast<uint8_t*>(sl.host);
+    int32_t* hb = reinterpret_cast<int32_t*>(h);
+    const size_t koff = pa::staging_k_off(n), voff = pa::staging_v_off(n, p->rb_k);
+    for (int r = 0; r < n; ++r) {
+      const int32_t i = order[first + r];
+      hb[r] = dst_block[i];
+      hb[n + r] = dst_slot[i];
+      std::memcpy(h + koff + r * krow, static_cast<const uint8_t*>(k_rows) + i * krow, krow);
+      std::memcpy(h + voff + r * vrow, static_cast<const uint8_t*>(v_rows) + i * vrow, vrow);
+    }
+    const size_t bytes = pa::staging_bytes(n, p->rb_k, p->rb_v);
+    hipError_t e = hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+      e = pa::launch_scatter(static_cast<const uint8_t*>(sl.dev), n, static_cast<uint8_t*>(p->desc.k_pool),
+                             static_cast<uint8_t*>(p->desc.v_pool), p->rb_k, p->rb_v, P, stream);
+    if (e == hipSuccess) e = hipEventRecord(sl.done, stream);
+    if (e != hipSuccess) return hip_status(e);
+    sl.used = true;
+  }
+  return PA_OK;
+}
+
+pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                    const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                    float* out, hipStream_t stream, const pa_decode_ext* ext) {
+  if (n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_QTOK) return PA_ERR_INVALID;
+  int kt = 0, vt = 0;
+  const pa_status ts = parse_kv_type(kv_type, &kt, &vt);
+  if (ts != PA_OK) return ts;
+  if (!page_size_ok(page_size)) return PA_ERR_UNSUPPORTED;
+  if (!k_pool || !v_pool) return PA_ERR_INVALID;
+  if (n_seq == 0) return PA_OK;
+  if (!q || !out || !seq_lens) return PA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
+    return PA_ERR_INVALID;
+
+  int device = 0;
+  int32_t bt_stride = 0, n_pool_blocks = 0;
+  float scale = 0.f;
+  float* lse_out = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (ext) {
+    if (ext->reserved != 0 || ext->bt_stride < 1) return PA_ERR_INVALID;
+    if (block_table && ext->n_pool_blocks < 1) return PA_ERR_INVALID;
+    if (ext->lse_out && !aligned(ext->lse_out, 4)) return PA_ERR_INVALID;
+    if (!std::isfinite(ext->scale)) return PA_ERR_INVALID;
+    bt_stride = ext->bt_stride;
+    n_pool_blocks = ext->n_pool_blocks;
+    scale = ext->scale;
+    lse_out = ext->lse_out;
+    ws = ext->workspace;
+    ws_bytes = ext->workspace_bytes;
+    ev0 = static_cast<hipEvent_t>(ext->split_events[0]);
+    ev1 = static_cast<hipEvent_t>(ext->split_events[1]);
+    if (hipGetDevice(&device) != hipSuccess) return PA_ERR_HIP;
+  }
+  pa_pool* pool = nullptr;
+  if (!ext || !ws) {
+    std::lock_guard<std::mutex> lk(g_registry_mu);
+    auto it = g_registry.find(k_pool);
+    if (it == g_registry.end()) return ext ? PA_ERR_INVALID : PA_ERR_NOT_FOUND;
+    pool = it->second;
+  }
+  if (pool) {
+    if (pool->desc.v_pool != v_pool || pool->desc.page_size != page_size ||
+        PA_KV_TYPE(pool->k_type, pool->v_type) != PA_KV_TYPE(kt, vt))
+      return PA_ERR_INVALID;
+    if (!ext) {
+      if (!block_table) return PA_ERR_INVALID;
+      bt_stride = pool->desc.max_blocks_per_seq;
+      n_pool_blocks = pool->desc.n_blocks;
+      device = pool->desc.device;
+    }
+    if (!ws) {
+      if (n_seq > pool->desc.max_seqs) return PA_ERR_INVALID;
+      ws = pool->workspace;
+      ws_bytes = pool->workspace_bytes;
+      device = pool->desc.device;
+    }
+  }
+  if (static_cast<int64_t>(bt_stride) * page_size > (1ll << 30)) return PA_ERR_INVALID;
+  const int target = target_items(device);
+  const pa::WorkspaceLayout wl = pa::workspace_layout(n_seq, n_qtok, target);
+  if (!ws || ws_bytes < wl.total || !aligned(ws, 256)) return PA_ERR_INVALID;
+  const int64_t items = pa::max_work_items(n_seq, target);
+  if (items > (1ll << 31) - 1) return PA_ERR_UNSUPPORTED;
+
+  pa::DecodeParams prm{};
+  prm.q = q;
+  prm.k = static_cast<const uint8_t*>(k_pool);
+  prm.v = static_cast<const uint8_t*>(v_pool);
+  prm.bt = block_table;
+  prm.seq_lens = seq_lens;
+  prm.out = out;
+  prm.lse_out = lse_out;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  prm.err = reinterpret_cast<uint32_t*>(wsb);
+  prm.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
+  prm.part_o = reinterpret_cast<float*>(wsb + wl.o_off);
+  prm.n_seq = n_seq;
+  prm.n_qtok = n_qtok;
+  prm.bt_stride = bt_stride;
+  prm.page_size = page_size;
+  prm.n_pool_blocks = block_table ? n_pool_blocks : 0;
+  prm.target_items = target;
+  prm.max_items = static_cast<int32_t>(items);
+  prm.k_type = kt;
+  prm.v_type = vt;
+  const float sc = (scale == 0.f) ? 1.0f / 16.0f : scale;
+  prm.scale_log2 = sc * 1.4426950408889634f;
+  return hip_status(pa::launch_decode(prm, stream, ev0, ev1));
+}
+
+pa_status pa_get_device_error(pa_pool* pool, void* workspace, hipStream_t stream, int32_t clear, int32_t* err) {
+  if (!err) return PA_ERR_INVALID;
+  void* ws = workspace;
+  if (!ws) {
+    if (!pool || !pool->workspace) return PA_ERR_INVALID;
+    ws = pool->workspace;
+  }
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && clear) e = hipMemsetAsync(ws, 0, sizeof(int32_t), stream);
+  if (e != hipSuccess) return hip_status(e);
+  *err = v;
+  return PA_OK;
+}
+
+pa_status pa_debug_gather(const void* pool, int32_t row_bytes, const int32_t* block_table, int32_t bt_stride,
+                          int32_t n_pool_blocks, int32_t seq, int32_t seq_len, int32_t page_size, void* dst,
+                          int32_t* err_word, hipStream_t stream) {
+  if (!pool || !dst || seq < 0 || seq_len < 0 || bt_stride < 1 || row_bytes <= 0 || row_bytes % 16) return PA_ERR_INVALID;
+  if (!page_size_ok(page_size)) return PA_ERR_UNSUPPORTED;
+  if (block_table && n_pool_blocks < 1) return PA_ERR_INVALID;
+  if (static_cast<int64_t>(seq_len) > static_cast<int64_t>(bt_stride) * page_size) return PA_ERR_INVALID;
+  if (!aligned(pool, 16) || !aligned(dst, 16)) return PA_ERR_INVALID;
+  return hip_status(pa::launch_gather(static_cast<const uint8_t*>(pool), row_bytes, block_table, bt_stride,
+                                      n_pool_blocks, seq, seq_len, page_size, static_cast<uint8_t*>(dst), err_word,
+                                      stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal interface between the C ABI (pa_host.cpp) and the kernels
+// (pa_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+#define PA_HD __host__ __device__
+
+namespace pa {
+
+constexpr int kHeadDim = 256;
+constexpr int kQHeads = 24;
+constexpr int kKvHeads = 4;
+constexpr int kGroup = kQHeads / kKvHeads;  // query heads per KV head
+constexpr int kMaxQtok = 4;
+constexpr int kChunkGranule = 64;           // chunk lengths are multiples of this
+
+enum KvType { kF16 = 1, kBF16 = 2, kQ8_0 = 3, kQ4_0 = 4 };
+
+inline int row_bytes_of(int t) {
+  switch (t) {
+    case kF16: case kBF16: return 512;
+    case kQ8_0: return 8 * 34;
+    case kQ4_0: return 8 * 18;
+    default: return 0;
+  }
+}
+
+// Everything one decode launch needs.  Device pointers unless noted.
+struct DecodeParams {
+  const float* q;          // [n_seq][n_qtok][24][256]
+  const uint8_t* k;        // pool or contiguous storage
+  const uint8_t* v;
+  const int32_t* bt;       // [n_seq][bt_stride], or nullptr (contiguous)
+  const int32_t* seq_lens; // [n_seq]
+  float* out;              // [n_seq][n_qtok][24][256]
+  float* lse_out;          // [n_seq][n_qtok][24] or nullptr
+  float* part_o;           // [max_items][6*n_qtok][256]
+  float* part_lse;         // [max_items][6*n_qtok]   (log2 units)
+  uint32_t* err;           // error word
+  int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
+  int32_t target_items;    // occupancy target of the chunk plan
+  int32_t max_items;       // work items the grid covers
+  int32_t k_type, v_type;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+// Upper bound on work items for n_seq sequences (see the plan in the kernels).
+inline int64_t max_work_items(int64_t n_seq, int64_t target_items) {
+  return target_items + kKvHeads * n_seq;
+}
+
+struct WorkspaceLayout {
+  size_t lse_off, o_off, total;
+};
+
+PA_HD inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WorkspaceLayout workspace_layout(int64_t n_seq, int64_t n_qtok, int64_t target_items) {
+  const int64_t items = max_work_items(n_seq, target_items);
+  const int64_t rows = 6 * n_qtok;
+  WorkspaceLayout w;
+  w.lse_off = 256;
+  w.o_off = align_up(w.lse_off + static_cast<size_t>(items * rows) * sizeof(float), 256);
+  w.total = align_up(w.o_off + static_cast<size_t>(items * rows * kHeadDim) * sizeof(float), 256);
+  return w;
+}
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin,
+                         hipEvent_t ev_end);
+
+// Staging layout for append: int32 block[n], int32 slot[n], then (16-byte
+// aligned) K rows [n][4][rb_k], then V rows [n][4][rb_v].
+PA_HD inline size_t staging_k_off(int64_t n) { return align_up(static_cast<size_t>(8 * n), 16); }
+PA_HD inline size_t staging_v_off(int64_t n, int rb_k) { return staging_k_off(n) + static_cast<size_t>(n) * kKvHeads * rb_k; }
+PA_HD inline size_t staging_bytes(int64_t n, int rb_k, int rb_v) {
+  return staging_v_off(n, rb_k) + static_cast<size_t>(n) * kKvHeads * rb_v;
+}
+
+hipError_t launch_scatter(const uint8_t* staging, int32_t n_rows, uint8_t* k_pool, uint8_t* v_pool,
+                          int32_t rb_k, int32_t rb_v, int32_t page_size, hipStream_t stream);
+
+hipError_t launch_gather(const uint8_t* pool, int32_t row_bytes, const int32_t* bt, int32_t bt_stride,
+                         int32_t n_pool_blocks, int32_t seq, int32_t seq_len, int32_t page_size,
+                         uint8_t* dst, int32_t* err_word, hipStream_t stream);
+
+}  // namespace pa

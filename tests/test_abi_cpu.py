@@ -1,0 +1,141 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol,
+its allocator matches the allocator model bit for bit, and host-side argument
+checks fail before anything reaches the device.  No compute call is made."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import alloc_model as am
+from paged_kv_attention_walk_amd import binding as pb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "pa_decode" in names and "pa_append_kv" in names and len(names) >= 13
+    lib = pb.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(pb.EXPORTS) == set(names)
+    assert pb.version().count(".") == 2
+
+
+def test_row_bytes_and_status_strings():
+    lib = pb.lib()
+    assert [lib.pa_row_bytes(t) for t in (1, 2, 3, 4, 5)] == [512, 512, 272, 144, 0]
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.pa_status_string(s)
+
+
+def _host_pool(n, P=16, kv="q4_0"):
+    return pb.Pool(n, P, kv, host_only=True)
+
+
+def test_allocator_matches_model_random_histories():
+    rng = np.random.default_rng(5)
+    for n_blocks in (1, 63, 64, 65, 300):
+        pool = _host_pool(n_blocks)
+        model = am.AllocModel(n_blocks)
+        live = []
+        for step in range(1500):
+            r = rng.random()
+            if r < 0.45:
+                n = int(rng.integers(0, 9))
+                st, h, ix = pool.alloc_status(n)
+                mst, mh, mix = model.alloc(n)
+                assert {pb.OK: am.OK, pb.ERR_NOMEM: am.NOMEM}[st] == mst
+                if st == pb.OK:
+                    assert list(h) == mh and list(ix) == mix
+                    live += mh
+            elif r < 0.9 and live:
+                k = int(rng.integers(1, min(5, len(live)) + 1))
+                pick = [live[i] for i in rng.choice(len(live), size=k, replace=False)]
+                if rng.random() < 0.15:
+                    pick.append(pick[0])
+                if rng.random() < 0.1:
+                    pick.append(am.handle(7, int(rng.integers(0, n_blocks))))   # forged generation
+                st = pool.free_status(pick)
+                mst = model.free_handles(pick)
+                assert {pb.OK: am.OK, pb.ERR_STALE: am.STALE, pb.ERR_INVALID: am.INVALID}[st] == mst
+                if st == pb.OK:
+                    for x in pick:
+                        live.remove(x)
+            else:
+                # stale handle: an old generation of an index that is live or free
+                if live:
+                    g, i = am.split(live[0])
+                    st = pool.free_status([am.handle(g + 1 if g < 0xFFFFFFFF else 1, i)])
+                    assert st == pb.ERR_STALE
+            assert pool.info().n_free == model.n_free
+        pool.destroy()
+
+
+def test_allocator_edge_cases():
+    pool = _host_pool(4)
+    assert pool.alloc_status(0)[0] == pb.OK
+    assert pool.alloc_status(-1)[0] == pb.ERR_INVALID
+    assert pool.alloc_status(2, handles=False, indices=False)[0] == pb.ERR_INVALID
+    st, h, ix = pool.alloc_status(2, handles=False)
+    assert st == pb.OK and list(ix) == [0, 1]
+    assert pool.alloc_status(3)[0] == pb.ERR_NOMEM and pool.info().n_free == 2
+    assert pool.free_status([am.handle(1, 4)]) == pb.ERR_INVALID      # index out of range
+    assert pool.free_status([am.handle(1, 2)]) == pb.ERR_STALE        # not allocated
+    assert pool.free_status([am.handle(1, 0), am.handle(1, 1)]) == pb.OK
+    assert pool.free_status([am.handle(1, 0)]) == pb.ERR_STALE        # double free
+    assert pool.info().n_free == 4
+    pool.destroy()
+
+
+def test_pool_create_rejects_bad_descriptors():
+    for kwargs, status in [(dict(n_blocks=0, page_size=16, kv="f16"), pb.ERR_INVALID),
+                           (dict(n_blocks=4, page_size=24, kv="f16"), pb.ERR_UNSUPPORTED),
+                           (dict(n_blocks=4, page_size=1024, kv="f16"), pb.ERR_UNSUPPORTED),
+                           (dict(n_blocks=4, page_size=16, kv=9), pb.ERR_INVALID),
+                           (dict(n_blocks=4, page_size=16, kv=pb.kv_type("q8_0", "q4_0")), pb.ERR_UNSUPPORTED)]:
+        with pytest.raises(pb.PaError) as e:
+            pb.Pool(kwargs["n_blocks"], kwargs["page_size"], kwargs["kv"], host_only=True)
+        assert e.value.status == status
+    p = pb.Pool(4, 48, "bf16", host_only=True)                         # 48: non-power-of-two page
+    assert p.info().page_size == 48
+    p.destroy()
+
+
+def test_decode_host_checks_fail_before_device_work():
+    # Fake, never-dereferenced addresses: every call must fail in host checks.
+    a = 1 << 20
+    kvq4 = pb.kv_type("q4_0")
+    st = lambda **kw: pb.decode_status(**{**dict(q=a, k_pool=a, v_pool=a, block_table=a, seq_lens=a, n_seq=1,
+                                                  n_qtok=1, kv=kvq4, page_size=16, out=a, stream=0), **kw})
+    assert st(n_qtok=0) == pb.ERR_INVALID
+    assert st(n_qtok=5) == pb.ERR_INVALID
+    assert st(n_seq=-1) == pb.ERR_INVALID
+    assert st(kv=0x10000 | 4) == pb.ERR_INVALID
+    assert st(kv=pb.kv_type("q4_0", "f16")) == pb.ERR_UNSUPPORTED
+    assert st(page_size=40) == pb.ERR_UNSUPPORTED
+    assert st(q=a + 4) == pb.ERR_INVALID                  # misaligned
+    assert st(k_pool=a + 8) == pb.ERR_INVALID
+    assert st(out=None) == pb.ERR_INVALID
+    assert st() == pb.ERR_NOT_FOUND                        # no ext and not a pool's K pointer
+    assert st(n_seq=0) == pb.OK                            # nothing to do
+    e = pb.make_ext(bt_stride=0)
+    assert st(ext=e) == pb.ERR_INVALID
+    e = pb.make_ext(bt_stride=4, n_pool_blocks=8)
+    e.reserved = 1
+    assert st(ext=e) == pb.ERR_INVALID
+
+
+def test_append_host_checks():
+    pool = _host_pool(8)
+    z = np.zeros((1, 4, 144), np.uint8)
+    assert pool.append_kv([0], [0], z, z, stream=0) == pb.ERR_INVALID       # host-only pool
+    pool.destroy()

@@ -1,0 +1,134 @@
+"""GPU parity of pa_decode against the float64 oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention
+from paged_kv_attention_walk_amd import binding as pb
+from paged_kv_attention_walk_amd import synth
+from gpu_util import TOL, dev, log, parity, run, workspace
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("f16", "bf16", "q8_0", "q4_0")
+
+
+def _oracle(w, scale=None, bt=None, lens=None):
+    return attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], w["k_kind"], w["v_kind"],
+                                  w["block_table"] if bt is None else bt,
+                                  w["seq_lens"] if lens is None else lens,
+                                  w["scale"] if scale is None else scale)
+
+
+def test_config1_parity():
+    w = synth.config1()
+    log("[case] config1 f16 1x1024 p16 shuffled")
+    out, lse, err = run(w, lse=True)
+    ref, rlse = _oracle(w)
+    assert err == 0
+    parity(out, ref, what="config1")
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_small_ragged_parity(kind, T):
+    # several chunks per sequence (the plan's granule is 64 keys), ragged
+    # tails, empty and shorter-than-T sequences, pages of 48 positions
+    lens = [0, 2, 63, 64, 65, 700, 1500, 3001]
+    w = synth.make_workload(f"small_{kind}_{T}", lens, T, kind, kind, 48, table="shuffled", seed=11 + T)
+    log(f"[case] small ragged {kind} T={T} P=48 lens={lens}")
+    out, lse, err = run(w, lse=True)
+    ref, rlse = _oracle(w)
+    assert err == 0
+    parity(out, ref, what=f"small {kind} T={T}")
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-3
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_unscaled_data_scale_one(kind):
+    # logits of order 16 exercise the max subtraction (config 1 data barely do)
+    w = synth.make_workload(f"unscaled_{kind}", [333, 2048, 17], 2, kind, kind, 16, seed=21, scale=1.0)
+    log(f"[case] unscaled {kind}")
+    out, _, err = run(w)
+    ref, _ = _oracle(w)
+    parity(out, ref, what=f"unscaled {kind}")
+
+
+@pytest.mark.parametrize("P", [16, 48, 128, 256, 512])
+def test_paged_equals_contiguous_bitwise(P):
+    lens = [5 * P + 3, 2 * P, 1, 9 * P - 1]
+    for kind in ("q4_0", "bf16"):
+        w = synth.make_workload(f"pc_{kind}_{P}", lens, 3, kind, kind, P, table="shuffled", seed=P)
+        log(f"[case] paged==contiguous {kind} P={P}")
+        kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], lens, w["block_table"].shape[1] * P)
+        vc = synth.contiguous_from_table(w["v_pool"], w["block_table"], lens, w["block_table"].shape[1] * P)
+        a, al, _ = run(w, lse=True)
+        b, bl, _ = run(w, contiguous=True, kc=kc, vc=vc, lse=True)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        assert np.array_equal(al.view(np.uint32), bl.view(np.uint32))
+        # three repeats are identical
+        for _ in range(2):
+            c, _, _ = run(w)
+            assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+def test_round_robin_vs_shuffled_bitwise():
+    lens = [4096, 1000, 2500]
+    a = synth.make_workload("rr", lens, 1, "q4_0", "q4_0", 16, table="round_robin", seed=3)
+    log("[case] round robin vs shuffled placement")
+    # same logical rows, different page placement
+    kc = synth.contiguous_from_table(a["k_pool"], a["block_table"], lens, 4096)
+    vc = synth.contiguous_from_table(a["v_pool"], a["block_table"], lens, 4096)
+    oa, _, _ = run(a)
+    ob, _, _ = run(a, contiguous=True, kc=kc, vc=vc)
+    assert np.array_equal(oa.view(np.uint32), ob.view(np.uint32))
+    parity(oa, _oracle(a)[0], what="round robin")
+
+
+def test_corrupt_table_and_length():
+    w = synth.make_workload("corrupt", [100, 900, 40, 3000], 2, "q8_0", "q8_0", 16, seed=31)
+    log("[case] corrupt table entry / length")
+    bt = w["block_table"].copy()
+    bt[1, 3] = w["n_blocks"] + 7          # out of range
+    bt[3, 100] = -5
+    out, _, err = run(w, dbt=dev(bt))
+    assert err & pb.DEVERR_TABLE
+    ref, _ = _oracle(w, bt=bt)
+    assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[3]))
+    parity(out[[0, 2]], ref[[0, 2]], what="intact sequences")
+    lens = w["seq_lens"].copy()
+    lens[2] = 16 * w["block_table"].shape[1] + 1
+    lens[0] = -3
+    out, _, err = run(w, dlens=dev(lens))
+    assert err & pb.DEVERR_LENGTH
+    assert np.all(np.isnan(out[0])) and np.all(np.isnan(out[2]))
+    parity(out[[1, 3]], _oracle(w)[0][[1, 3]], what="intact after bad lengths")
+
+
+def test_registered_pool_path_without_ext():
+    # pa_decode with ext == NULL: the pool is found from k_pool
+    w = synth.make_workload("noext", [777, 64, 1], 1, "q4_0", "q4_0", 16, seed=41, n_blocks=80)
+    log("[case] pa_decode without ext")
+    dk, dv = dev(w["k_pool"]), dev(w["v_pool"])
+    nb = w["k_pool"].shape[0]
+    pool = pb.Pool(nb, 16, "q4_0", k_pool=dk, v_pool=dv, max_seqs=8, max_blocks_per_seq=w["block_table"].shape[1])
+    out = torch.empty((3, 1, 24, 256), device="cuda")
+    pb.decode(dev(w["q"]), dk, dv, dev(w["block_table"]), dev(w["seq_lens"]), 1, "q4_0", 16, out)
+    assert pool.device_error() == 0
+    torch.cuda.synchronize()
+    parity(out.cpu().numpy(), _oracle(w)[0], what="no-ext path")
+    pool.destroy()
+
+
+def test_lse_matches_oracle_and_merge_of_halves():
+    w = synth.make_workload("lse", [5000, 130], 4, "f16", "f16", 64, seed=51)
+    log("[case] lse output")
+    out, lse, _ = run(w, lse=True)
+    ref, rlse = _oracle(w)
+    parity(out, ref, what="lse case out")
+    fin = np.isfinite(rlse)
+    assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-4 * max(1.0, np.abs(rlse[fin]).max())
