@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention-step ms, effective K/V GB/s (% HBM peak), paged÷contiguous ratio"
 HBM_PEAK_GBPS = 8000.0
-SPLIT_KERNEL = "split_valu_kernel"
+SPLIT_KERNEL = "split_mfma_kernel"
 
 
 def parse():

@@ -189,6 +189,10 @@ pa_status pa_append_kv(pa_pool *pool, int32_t n_rows, const int32_t *dst_block,
 
 /* ------------------------------------------------------------------ decode */
 
+/* pa_decode_ext.flags: run the fp32 vector-ALU path instead of the matrix-core
+ * path (same plan and merge; a second implementation for cross-checks). */
+#define PA_DECODE_VECTOR_REFERENCE 1u
+
 /* Device-side error bits, ORed into the workspace's error word. */
 #define PA_DEVERR_TABLE  1 /* a block-table entry outside [0, n_pool_blocks)         */
 #define PA_DEVERR_LENGTH 2 /* a seq_len < 0, or beyond the table row / contiguous rows */
@@ -198,12 +202,16 @@ typedef struct pa_decode_ext {
                                 rows per sequence are bt_stride * page_size              */
     int32_t  n_pool_blocks;  /* pages in the pool (bounds for table entries)            */
     float    scale;          /* softmax scale; 0 => 1/sqrt(256) = 1/16                   */
-    int32_t  reserved;       /* must be 0                                                */
+    uint32_t flags;          /* 0, or PA_DECODE_VECTOR_REFERENCE                         */
     float   *lse_out;        /* optional device [n_seq][n_qtok][24] float: natural-log
                                 log-sum-exp of each row's scaled, masked logits; -inf
                                 for a row with no visible key                           */
-    void    *workspace;      /* device scratch of pa_decode_workspace_size() bytes, or
-                                NULL for the pool's own workspace                       */
+    void    *workspace;      /* device scratch of at least pa_decode_workspace_size()
+                                bytes, 256-byte aligned, or NULL for the pool's own
+                                workspace.  Its first pa_decode must find it zeroed
+                                (e.g. one hipMemset); every call leaves its internal
+                                counters at zero again.  Pass the same workspace_bytes
+                                with every call that uses it                            */
     size_t   workspace_bytes;
     void    *split_events[2];/* optional hipEvent_t pair, recorded on `stream` just
                                 before and after the split kernel (profiling)           */
@@ -252,9 +260,11 @@ pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
                     int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
                     float *out, hipStream_t stream, const pa_decode_ext *ext);
 
-/* Bytes of decode workspace for n_seq sequences of n_qtok tokens on `device`
+/* Bytes of decode workspace for n_seq sequences of up to 4 tokens on `device`
  * (reserved up front, as llama.cpp pull 2 does for its split partials in the
- * commit that moved them out of run-time pool allocations). */
+ * commit that moved them out of run-time pool allocations).  n_qtok is
+ * checked (1..4) but the size covers 4 tokens, so one workspace serves every
+ * n_qtok. */
 pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t *bytes);
 
 /* Reads the error word of a workspace after the work on `stream` finishes

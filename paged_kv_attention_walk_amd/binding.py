@@ -25,6 +25,7 @@ HEAD_DIM, N_Q_HEADS, N_KV_HEADS, MAX_QTOK = 256, 24, 4, 4
 
 OK, ERR_INVALID, ERR_NOMEM, ERR_STALE, ERR_UNSUPPORTED, ERR_HIP, ERR_NOT_FOUND = 0, -1, -2, -3, -4, -5, -6
 DEVERR_TABLE, DEVERR_LENGTH = 1, 2
+DECODE_VECTOR_REFERENCE = 1
 POOL_HOST_ONLY = 1
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "pa_pool_destroy",
@@ -63,7 +64,7 @@ class PoolInfo(ctypes.Structure):
 
 class DecodeExt(ctypes.Structure):
     _fields_ = [("bt_stride", ctypes.c_int32), ("n_pool_blocks", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("reserved", ctypes.c_int32), ("lse_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32), ("lse_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("split_events", ctypes.c_void_p * 2)]
 
 
@@ -220,8 +221,8 @@ class Pool:
 
 
 def make_ext(bt_stride, n_pool_blocks=0, scale=0.0, lse_out=None, workspace=None, workspace_bytes=None,
-             split_events=None) -> DecodeExt:
-    e = DecodeExt(bt_stride=int(bt_stride), n_pool_blocks=int(n_pool_blocks), scale=float(scale), reserved=0,
+             split_events=None, flags=0) -> DecodeExt:
+    e = DecodeExt(bt_stride=int(bt_stride), n_pool_blocks=int(n_pool_blocks), scale=float(scale), flags=int(flags),
                   lse_out=_ptr(lse_out), workspace=_ptr(workspace),
                   workspace_bytes=int(workspace_bytes if workspace_bytes is not None else
                                       (workspace.numel() * workspace.element_size() if workspace is not None else 0)))

@@ -53,9 +53,10 @@ def build(verbose: bool = True) -> str:
     o = os.path.join(BUILD_DIR, "pa_host.o")
     _run([cxx, *HOST_FLAGS, *inc, *hip_inc, "-c", os.path.join(CSRC, "pa_host.cpp"), "-o", o], verbose)
     objs.append(o)
-    o = os.path.join(BUILD_DIR, "pa_kernels.o")
-    _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "pa_kernels.hip"), "-o", o], verbose)
-    objs.append(o)
+    for name in ("pa_kernels", "pa_mfma"):
+        o = os.path.join(BUILD_DIR, name + ".o")
+        _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o], verbose)
+        objs.append(o)
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

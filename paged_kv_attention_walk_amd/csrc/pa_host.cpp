@@ -149,7 +149,7 @@ size_t pa_row_bytes(int32_t t) { return static_cast<size_t>(pa::row_bytes_of(t))
 
 pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
   if (!bytes || n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_QTOK) return PA_ERR_INVALID;
-  *bytes = pa::workspace_layout(n_seq, n_qtok, target_items(device)).total;
+  *bytes = pa::workspace_layout(n_seq, target_items(device)).total;
   return PA_OK;
 }
 
@@ -199,9 +199,10 @@ pa_status pa_pool_create(const pa_pool_desc* d, pa_pool** out) {
     p->own_v = st == PA_OK;
   }
   if (st == PA_OK) {
-    p->workspace_bytes = pa::workspace_layout(p->desc.max_seqs, PA_MAX_QTOK, target_items(d->device)).total;
+    const pa::WorkspaceLayout wl = pa::workspace_layout(p->desc.max_seqs, target_items(d->device));
+    p->workspace_bytes = wl.total;
     st = hip_status(hipMalloc(&p->workspace, p->workspace_bytes));
-    if (st == PA_OK) st = hip_status(hipMemset(p->workspace, 0, 256));
+    if (st == PA_OK) st = hip_status(hipMemset(p->workspace, 0, wl.lse_off));   // error word + counters
   }
   const size_t sbytes = pa::staging_bytes(p->desc.max_append_rows, p->rb_k, p->rb_v);
   for (int i = 0; st == PA_OK && i < kStagingSlots; ++i) {
@@ -365,8 +366,10 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   void* ws = nullptr;
   size_t ws_bytes = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  int engine = 0;
   if (ext) {
-    if (ext->reserved != 0 || ext->bt_stride < 1) return PA_ERR_INVALID;
+    engine = (ext->flags & PA_DECODE_VECTOR_REFERENCE) ? 1 : 0;
+    if ((ext->flags & ~PA_DECODE_VECTOR_REFERENCE) || ext->bt_stride < 1) return PA_ERR_INVALID;
     if (block_table && ext->n_pool_blocks < 1) return PA_ERR_INVALID;
     if (ext->lse_out && !aligned(ext->lse_out, 4)) return PA_ERR_INVALID;
     if (!std::isfinite(ext->scale)) return PA_ERR_INVALID;
@@ -378,7 +381,9 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
     ws_bytes = ext->workspace_bytes;
     ev0 = static_cast<hipEvent_t>(ext->split_events[0]);
     ev1 = static_cast<hipEvent_t>(ext->split_events[1]);
-    if (hipGetDevice(&device) != hipSuccess) return PA_ERR_HIP;
+    // Without a usable device the launch below reports the HIP error; the
+    // remaining host checks still run first.
+    if (hipGetDevice(&device) != hipSuccess) device = 0;
   }
   pa_pool* pool = nullptr;
   if (!ext || !ws) {
@@ -406,9 +411,10 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   }
   if (static_cast<int64_t>(bt_stride) * page_size > (1ll << 30)) return PA_ERR_INVALID;
   const int target = target_items(device);
-  const pa::WorkspaceLayout wl = pa::workspace_layout(n_seq, n_qtok, target);
-  if (!ws || ws_bytes < wl.total || !aligned(ws, 256)) return PA_ERR_INVALID;
+  if (!ws || !aligned(ws, 256)) return PA_ERR_INVALID;
+  const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes);
   const int64_t items = pa::max_work_items(n_seq, target);
+  if (wl.items < items) return PA_ERR_INVALID;
   if (items > (1ll << 31) - 1) return PA_ERR_UNSUPPORTED;
 
   pa::DecodeParams prm{};
@@ -421,6 +427,8 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   prm.lse_out = lse_out;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   prm.err = reinterpret_cast<uint32_t*>(wsb);
+  prm.cnt1 = reinterpret_cast<uint32_t*>(wsb + wl.cnt1_off);
+  prm.cnt2 = reinterpret_cast<uint32_t*>(wsb + wl.cnt2_off);
   prm.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
   prm.part_o = reinterpret_cast<float*>(wsb + wl.o_off);
   prm.n_seq = n_seq;
@@ -432,6 +440,7 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   prm.max_items = static_cast<int32_t>(items);
   prm.k_type = kt;
   prm.v_type = vt;
+  prm.engine = engine;
   const float sc = (scale == 0.f) ? 1.0f / 16.0f : scale;
   prm.scale_log2 = sc * 1.4426950408889634f;
   return hip_status(pa::launch_decode(prm, stream, ev0, ev1));

@@ -37,13 +37,16 @@ struct DecodeParams {
   const int32_t* seq_lens; // [n_seq]
   float* out;              // [n_seq][n_qtok][24][256]
   float* lse_out;          // [n_seq][n_qtok][24] or nullptr
-  float* part_o;           // [max_items][6*n_qtok][256]
-  float* part_lse;         // [max_items][6*n_qtok]   (log2 units)
+  float* part_o;           // [item capacity][24][256]
+  float* part_lse;         // [item capacity][24]   (log2 units)
   uint32_t* err;           // error word
+  uint32_t* cnt1;          // [max_items] arrival counters of 16-chunk groups (zero between calls)
+  uint32_t* cnt2;          // [max_items] arrival counters of (sequence, KV head) groups
   int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
   int32_t target_items;    // occupancy target of the chunk plan
   int32_t max_items;       // work items the grid covers
   int32_t k_type, v_type;
+  int32_t engine;          // 0: matrix-core path, 1: fp32 vector reference path
   float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -53,23 +56,46 @@ inline int64_t max_work_items(int64_t n_seq, int64_t target_items) {
 }
 
 struct WorkspaceLayout {
-  size_t lse_off, o_off, total;
+  int64_t items;       // work-item capacity
+  size_t cnt1_off, cnt2_off, lse_off, o_off, total;
 };
 
 PA_HD inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline WorkspaceLayout workspace_layout(int64_t n_seq, int64_t n_qtok, int64_t target_items) {
-  const int64_t items = max_work_items(n_seq, target_items);
-  const int64_t rows = 6 * n_qtok;
+constexpr int kRowsPerItem = 6 * kMaxQtok;   // partial rows reserved per work item
+
+// Workspace: [0, 256) header (error word at 0); two arrays of arrival
+// counters; chunk log-sum-exps; chunk outputs.  The layout depends only on
+// the item capacity, never on the call's n_seq or n_qtok, so one workspace can
+// serve calls of any shape it has room for without partials ever landing on
+// counters.  Counters and the error word must be zero before the first call;
+// every call leaves the counters at zero.
+inline WorkspaceLayout workspace_layout_items(int64_t items) {
   WorkspaceLayout w;
-  w.lse_off = 256;
-  w.o_off = align_up(w.lse_off + static_cast<size_t>(items * rows) * sizeof(float), 256);
-  w.total = align_up(w.o_off + static_cast<size_t>(items * rows * kHeadDim) * sizeof(float), 256);
+  w.items = items;
+  w.cnt1_off = 256;
+  w.cnt2_off = w.cnt1_off + static_cast<size_t>(items) * 4;
+  w.lse_off = align_up(w.cnt2_off + static_cast<size_t>(items) * 4, 256);
+  w.o_off = align_up(w.lse_off + static_cast<size_t>(items) * kRowsPerItem * sizeof(float), 256);
+  w.total = align_up(w.o_off + static_cast<size_t>(items) * kRowsPerItem * kHeadDim * sizeof(float), 256);
   return w;
+}
+
+inline WorkspaceLayout workspace_layout(int64_t n_seq, int64_t target_items) {
+  return workspace_layout_items(max_work_items(n_seq, target_items));
+}
+
+// The largest item capacity whose layout fits in `bytes`.
+inline WorkspaceLayout workspace_layout_for_bytes(size_t bytes) {
+  const size_t per = 8 + kRowsPerItem * sizeof(float) * (1 + kHeadDim);
+  int64_t items = static_cast<int64_t>(bytes / per) + 1;   // an upper bound; step down to the largest fit
+  while (items > 0 && workspace_layout_items(items).total > bytes) --items;
+  return workspace_layout_items(items);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin,
                          hipEvent_t ev_end);
+hipError_t launch_split_mfma(const DecodeParams& p, hipStream_t stream);
 
 // Staging layout for append: int32 block[n], int32 slot[n], then (16-byte
 // aligned) K rows [n][4][rb_k], then V rows [n][4][rb_v].

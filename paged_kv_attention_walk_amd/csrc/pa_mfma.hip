@@ -1,0 +1,748 @@
+// Matrix-core split kernel of the paged decode (gfx950).
+//
+// Same work items, plan and fused merge as the vector path; the per-chunk
+// math runs on v_mfma_f32_16x16x32_{f16,bf16}.  One workgroup = one
+// (sequence, KV head, chunk); its 4 waves take 32-key tiles of the chunk in
+// turn, each wave with its own running max / sum / output.
+//
+// Per 32-key tile (two 16-key halves, each inside one page, so the block
+// table is read once per half -- llama.cpp pull 2, page-table commit, resolves
+// its table once per chunk of keys rather than per key):
+//  * QK^T as S^T = K Q^T: the A operand is 16 keys x 32 dims of one
+//    quantisation block, loaded straight from HBM into registers (a lane
+//    holds 8 dims of one key) and converted in-register to exact f16 values
+//    (codes for Q8_0 / Q4_0); the B operand is the 6*T query rows of the
+//    KV head (padded to 16 or 32), split as q = q_hi + q_lo in f16 (bf16 for
+//    BF16 K) so the products carry ~22 bits.  For Q8_0 / Q4_0 the block scale
+//    is applied per key to the fp32 result of each block's MFMA, so codes
+//    stay exact (llama.cpp pull 2, LDS-read commit, converts quants in
+//    registers; here the fp16 scale never touches an f16 operand).
+//  * online softmax in base 2 (log2 e folded into q), rows spread over the
+//    4 lanes that hold them;
+//  * PV as O^T = V^T P^T: V rows are staged in the wave's LDS (codes and
+//    scales split apart), and the gfx950 LDS transpose reads
+//    (ds_read_b64_tr_b4 / _b8 / _b16) deliver the V^T operand -- 8 keys of one
+//    dim per lane -- in one read per block (Q4_0), per 16 dims (Q8_0) or two
+//    per 16 dims (F16 / BF16); the per-key V scale is folded into the
+//    probabilities, P' = p * d_v, split hi + lo like q.
+// Accumulation is fp32 throughout.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+using namespace dev;
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef int32_t i2 __attribute__((ext_vector_type(2)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+// dword-aligned multi-dword loads from rows whose start is 4-byte aligned
+typedef uint32_t u4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u2a __attribute__((ext_vector_type(2), aligned(4)));
+
+typedef __attribute__((address_space(3))) i2 lds_i2;
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+template <int KT>
+struct Fmt {
+  static constexpr bool kQuant = (KT == kQ8_0 || KT == kQ4_0);
+  static constexpr bool kBf = (KT == kBF16);
+  static constexpr int kRow = (KT == kQ8_0) ? 272 : (KT == kQ4_0) ? 144 : 512;   // bytes per row
+  static constexpr int kBlk = (KT == kQ8_0) ? 34 : 18;                           // bytes per quant block
+  static constexpr int kCodes = (KT == kQ8_0) ? 32 : 16;                         // code bytes per block
+  // LDS stride of one staged V key: codes (quant) or the row, plus 16 bytes
+  // so that keys 4 apart fall in different banks.
+  static constexpr int kVks = kQuant ? 8 * kCodes + 16 : 512 + 16;
+  static constexpr int kVtile = 32 * kVks;                                     // 32 keys
+  static constexpr int kWave = kVtile + (kQuant ? 2048 : 0);                   // + V and K scales (f32)
+};
+
+__device__ inline f4 mma(u4 a, u4 b, f4 c, bool bf) {
+  if (bf)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+
+// f16 pair (a, b) -> packed bits
+__device__ inline uint32_t pack_h(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b)) << 16);
+}
+__device__ inline uint32_t pack_bf(__bf16 a, __bf16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b)) << 16);
+}
+
+// Splits 8 floats into hi + lo 16-bit operands (f16, or bf16 when bf).
+__device__ inline void split8(const float (&x)[8], u4& hi, u4& lo, bool bf) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = x[2 * k], b = x[2 * k + 1];
+    if (bf) {
+      const __bf16 ha = static_cast<__bf16>(a), hb = static_cast<__bf16>(b);
+      hi[k] = pack_bf(ha, hb);
+      lo[k] = pack_bf(static_cast<__bf16>(a - static_cast<float>(ha)), static_cast<__bf16>(b - static_cast<float>(hb)));
+    } else {
+      const _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
+      hi[k] = pack_h(ha, hb);
+      lo[k] = pack_h(static_cast<_Float16>(a - static_cast<float>(ha)), static_cast<_Float16>(b - static_cast<float>(hb)));
+    }
+  }
+}
+
+// (x & mask) | 0x64006400 read as two f16 (1024 + field), minus `sub` each.
+__device__ inline uint32_t nib2h(uint32_t x, uint32_t mask, float sub) {
+  const uint32_t u = (x & mask) | 0x64006400u;
+  h2 v = __builtin_bit_cast(h2, u);
+  const h2 s = {static_cast<_Float16>(sub), static_cast<_Float16>(sub)};
+  v = v - s;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 nibbles (bits 4k, k = 0..7) -> f16 operand, element order k = 0,4,1,5,2,6,3,7;
+// elements of odd k carry a factor 16 (the partner operand holds 1/16).
+__device__ inline u4 q4_operand(uint32_t x) {
+  const uint32_t y = x >> 8;
+  u4 a;
+  a[0] = nib2h(x, 0x000F000Fu, 1032.f);   // k = 0, 4:  c - 8
+  a[1] = nib2h(x, 0x00F000F0u, 1152.f);   // k = 1, 5:  16 (c - 8)
+  a[2] = nib2h(y, 0x000F000Fu, 1032.f);   // k = 2, 6
+  a[3] = nib2h(y, 0x00F000F0u, 1152.f);   // k = 3, 7
+  return a;
+}
+
+// 8 signed bytes (two dwords) -> f16 operand, element order 0,2,1,3,4,6,5,7.
+__device__ inline u4 q8_operand(uint32_t x0, uint32_t x1) {
+  const uint32_t y0 = x0 ^ 0x80808080u, y1 = x1 ^ 0x80808080u;
+  u4 a;
+  a[0] = nib2h(y0, 0x00FF00FFu, 1152.f);
+  a[1] = nib2h(y0 >> 8, 0x00FF00FFu, 1152.f);
+  a[2] = nib2h(y1, 0x00FF00FFu, 1152.f);
+  a[3] = nib2h(y1 >> 8, 0x00FF00FFu, 1152.f);
+  return a;
+}
+
+__device__ inline uint32_t funnel16(uint32_t lo, uint32_t hi) { return (lo >> 16) | (hi << 16); }
+
+// Registers of one tile: K operands (per half, per block), K scales, raw V.
+template <int KT>
+struct Tile {
+  static constexpr int kKw = (KT == kQ4_0) ? 1 : (KT == kQ8_0) ? 2 : 4;   // dwords of K per block per lane
+  static constexpr int kVw = (KT == kQ4_0) ? 9 : (KT == kQ8_0) ? 17 : 32; // dwords of V per lane per half
+  uint32_t k[2][8][kKw];
+  uint32_t ks[2];
+  uint32_t v[2][kVw];
+  bool half_ok[2];
+};
+
+// Loads tile registers.  lane = (m, g) for K, (j, seg) for V.  Halves past
+// the chunk end are not read.  Sets bad on an out-of-range table entry.
+template <int KT>
+__device__ inline void load_tile(const DecodeParams& p, int s, int h, int tb, int k1, Tile<KT>& t, bool& bad) {
+  using F = Fmt<KT>;
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int j = lane >> 2, seg = lane & 3;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int pos0 = tb + 16 * hf;
+    t.half_ok[hf] = false;
+    if (pos0 < k1) {
+      bool ok;
+      const size_t r0 = kv_row(p.bt, p.bt_stride, p.n_pool_blocks, p.page_size, s, h, pos0, ok);
+      if (!ok) bad = true;
+      t.half_ok[hf] = ok;
+      if (ok) {
+        const uint8_t* rk = p.k + (r0 + m) * F::kRow;
+        if constexpr (KT == kF16 || KT == kBF16) {
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const u4 x = *reinterpret_cast<const u4*>(rk + 64 * b + 16 * g);
+            t.k[hf][b][0] = x[0]; t.k[hf][b][1] = x[1]; t.k[hf][b][2] = x[2]; t.k[hf][b][3] = x[3];
+          }
+        } else if constexpr (KT == kQ8_0) {
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const int off = 34 * b + 2 + 8 * g;
+            if (b & 1) {
+              const u2a x = *reinterpret_cast<const u2a*>(rk + off);
+              t.k[hf][b][0] = x[0]; t.k[hf][b][1] = x[1];
+            } else {
+              const u2a x = *reinterpret_cast<const u2a*>(rk + off - 2);
+              const uint32_t x2 = *reinterpret_cast<const uint32_t*>(rk + off + 6);
+              t.k[hf][b][0] = funnel16(x[0], x[1]);
+              t.k[hf][b][1] = funnel16(x[1], x2);
+            }
+          }
+          t.ks[hf] = (*reinterpret_cast<const uint32_t*>(rk + 68 * g) & 0xFFFFu) |
+                     (*reinterpret_cast<const uint32_t*>(rk + 68 * g + 32) & 0xFFFF0000u);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const int off = 18 * b + 2 + 4 * g;
+            if (b & 1) {
+              t.k[hf][b][0] = *reinterpret_cast<const uint32_t*>(rk + off);
+            } else {
+              const u2a x = *reinterpret_cast<const u2a*>(rk + off - 2);
+              t.k[hf][b][0] = funnel16(x[0], x[1]);
+            }
+          }
+          t.ks[hf] = (*reinterpret_cast<const uint32_t*>(rk + 36 * g) & 0xFFFFu) |
+                     (*reinterpret_cast<const uint32_t*>(rk + 36 * g + 16) & 0xFFFF0000u);
+        }
+        const uint8_t* rv = p.v + (r0 + j) * F::kRow;
+        if constexpr (KT == kF16 || KT == kBF16) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const u4 x = *reinterpret_cast<const u4*>(rv + 128 * seg + 16 * i);
+            t.v[hf][4 * i] = x[0]; t.v[hf][4 * i + 1] = x[1]; t.v[hf][4 * i + 2] = x[2]; t.v[hf][4 * i + 3] = x[3];
+          }
+        } else {
+          constexpr int W = Tile<KT>::kVw;
+          const uint8_t* src = rv + (W * 4) * seg;
+#pragma unroll
+          for (int i = 0; i + 4 <= W; i += 4) {
+            const u4a x = *reinterpret_cast<const u4a*>(src + 4 * i);
+            t.v[hf][i] = x[0]; t.v[hf][i + 1] = x[1]; t.v[hf][i + 2] = x[2]; t.v[hf][i + 3] = x[3];
+          }
+          t.v[hf][W - 1] = *reinterpret_cast<const uint32_t*>(src + 4 * (W - 1));
+        }
+      }
+    }
+  }
+}
+
+// Writes the tile's V rows (and, for quant, V and K scales as f32) into the
+// wave's LDS region.  Keys at or past k1 are written as zeros.
+template <int KT>
+__device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1) {
+  using F = Fmt<KT>;
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const int j = lane >> 2, seg = lane & 3;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int key = 16 * hf + j;
+    const bool valid = t.half_ok[hf] && (tb + key < k1);
+    if constexpr (KT == kF16 || KT == kBF16) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        u4 x = {t.v[hf][4 * i], t.v[hf][4 * i + 1], t.v[hf][4 * i + 2], t.v[hf][4 * i + 3]};
+        if (!valid) x = u4{0, 0, 0, 0};
+        *reinterpret_cast<u4*>(w + key * F::kVks + 128 * seg + 16 * i) = x;
+      }
+    } else {
+      float* vsc = reinterpret_cast<float*>(w + F::kVtile);              // [8 blocks][32 keys]
+      float* ksc = reinterpret_cast<float*>(w + F::kVtile + 1024);       // [2 halves][8 blocks][16 keys]
+      const uint32_t* v = t.v[hf];
+      u4 c0, c1, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
+      uint32_t sa, sb;
+      if constexpr (KT == kQ4_0) {
+        c0 = u4{funnel16(v[0], v[1]), funnel16(v[1], v[2]), funnel16(v[2], v[3]), funnel16(v[3], v[4])};
+        c1 = u4{v[5], v[6], v[7], v[8]};
+        sa = v[0] & 0xFFFFu;
+        sb = v[4] >> 16;
+      } else {
+        c0 = u4{funnel16(v[0], v[1]), funnel16(v[1], v[2]), funnel16(v[2], v[3]), funnel16(v[3], v[4])};
+        c1 = u4{funnel16(v[4], v[5]), funnel16(v[5], v[6]), funnel16(v[6], v[7]), funnel16(v[7], v[8])};
+        c2 = u4{v[9], v[10], v[11], v[12]};
+        c3 = u4{v[13], v[14], v[15], v[16]};
+        sa = v[0] & 0xFFFFu;
+        sb = v[8] >> 16;
+      }
+      float fa = half_bits(sa), fb = half_bits(sb);
+      if constexpr (KT == kQ4_0) {
+        if (key & 1) {      // odd keys: their V operand carries 16 (c - 8)
+          fa *= 0.0625f;
+          fb *= 0.0625f;
+        }
+      }
+      if (!valid) {
+        c0 = c1 = c2 = c3 = u4{0, 0, 0, 0};
+        fa = fb = 0.f;
+      }
+      uint8_t* row = w + key * F::kVks;
+      if constexpr (KT == kQ4_0) {
+        *reinterpret_cast<u4*>(row + 16 * (2 * seg)) = c0;
+        *reinterpret_cast<u4*>(row + 16 * (2 * seg + 1)) = c1;
+      } else {
+        *reinterpret_cast<u4*>(row + 32 * (2 * seg)) = c0;
+        *reinterpret_cast<u4*>(row + 32 * (2 * seg) + 16) = c1;
+        *reinterpret_cast<u4*>(row + 32 * (2 * seg + 1)) = c2;
+        *reinterpret_cast<u4*>(row + 32 * (2 * seg + 1) + 16) = c3;
+      }
+      vsc[(2 * seg) * 32 + key] = fa;
+      vsc[(2 * seg + 1) * 32 + key] = fb;
+      // K scales: lane (m, g) holds blocks 2g, 2g+1 of key m of this half
+      float ka = half_bits(t.ks[hf] & 0xFFFFu), kb = half_bits(t.ks[hf] >> 16);
+      if (!t.half_ok[hf]) ka = kb = 0.f;
+      ksc[(hf * 8 + 2 * g) * 16 + m] = ka;
+      ksc[(hf * 8 + 2 * g + 1) * 16 + m] = kb;
+    }
+  }
+}
+
+// Key of k-slot k (0..7) of lane group g in a 32-key tile: the layout of the
+// QK result (lane (r, g) holds keys 4g..4g+3 of each 16-key half).
+__device__ inline int sigma(int g, int k) { return (k < 4) ? 4 * g + k : 16 + 4 * g + (k - 4); }
+
+// Query-row columns of the 16-wide B tiles.  With one token (6 rows) the hi
+// and lo halves share one tile: lane n < 8 carries the hi part of row n, lane
+// n + 8 the lo part of the same row, and the two partial results are added
+// across lanes n, n ^ 8.  With more tokens hi and lo take separate tiles.
+template <int T>
+struct Cols {
+  static constexpr bool kPack = (T == 1);
+  static constexpr int R = 6 * T;
+  static constexpr int NT = kPack ? 1 : (R + 15) / 16;   // B tiles per part
+  static constexpr int kParts = kPack ? 1 : 2;          // hi / lo in separate MFMAs
+};
+
+// Source of the QK^T B operands: registers for one token; for more tokens an
+// LDS copy laid out per (tile, part, block) as 64 lanes x 16 bytes, so each
+// operand is one conflict-free 16-byte read per lane.
+template <int T>
+struct QSrc {
+  static constexpr bool kRegs = Cols<T>::kPack;
+  u4 q[kRegs ? 8 : 1];
+  const uint8_t* base;
+  __device__ inline u4 get(int nt, int part, int b) const {
+    if constexpr (kRegs) {
+      return q[b];
+    } else {
+      return *reinterpret_cast<const u4*>(base + ((nt * 2 + part) * 8 + b) * 1024 + (threadIdx.x & 63) * 16);
+    }
+  }
+};
+
+// One tile's QK^T, online-softmax update and PV on the registers of `t` and
+// the V rows staged in the wave's LDS region `wl`.
+template <int KT, int T>
+__device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int k1,
+                                    const int (&lim)[Cols<T>::NT], const QSrc<T>& qs,
+                                    f4 (&o)[Cols<T>::NT][16], float (&m_run)[Cols<T>::NT],
+                                    float (&l_run)[Cols<T>::NT]) {
+  using F = Fmt<KT>;
+  using C = Cols<T>;
+  constexpr int NT = C::NT;
+  constexpr bool BF = F::kBf;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const bool lo_lane = (n & 8) != 0;      // packed case: this lane carries lo parts
+
+  // ---- S^T = K Q^T (lane (n, g) gets rows 4g..4g+3 = keys of each half, column n)
+  f4 sacc[NT][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sacc[nt][hf] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      u4 a;
+      if constexpr (KT == kQ4_0) a = q4_operand(t.k[hf][b][0]);
+      else if constexpr (KT == kQ8_0) a = q8_operand(t.k[hf][b][0], t.k[hf][b][1]);
+      else a = u4{t.k[hf][b][0], t.k[hf][b][1], t.k[hf][b][2], t.k[hf][b][3]};
+      if constexpr (F::kQuant) {
+        const f4 dk = *reinterpret_cast<const f4*>(wl + F::kVtile + 1024 + ((hf * 8 + b) * 16 + 4 * g) * 4);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f4 cb = mma(a, qs.get(nt, 0, b), f4{0.f, 0.f, 0.f, 0.f}, false);
+          if constexpr (C::kParts == 2) cb = mma(a, qs.get(nt, 1, b), cb, false);
+          sacc[nt][hf] += dk * cb;       // per-key block scale on the exact-code product
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          sacc[nt][hf] = mma(a, qs.get(nt, 0, b), sacc[nt][hf], BF);
+          if constexpr (C::kParts == 2) sacc[nt][hf] = mma(a, qs.get(nt, 1, b), sacc[nt][hf], BF);
+        }
+      }
+    }
+  }
+  if constexpr (C::kPack) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sacc[0][hf][i] += __shfl_xor(sacc[0][hf][i], 8, 64);
+  }
+
+  // ---- online softmax (base 2); p[nt][k] is the weight of key sigma(g, k)
+  float p[NT][8];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float sv[8];
+    float mx = kNegInf;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = tb + 16 * hf + 4 * g + i;
+        const bool ok = t.half_ok[hf] && pos < k1 && pos <= lim[nt];
+        const float x = ok ? sacc[nt][hf][i] : kNegInf;
+        sv[4 * hf + i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m_run[nt], mx);
+    const float alpha = (mn == kNegInf) ? 1.f : exp2f(m_run[nt] - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[nt][k] = (sv[k] == kNegInf) ? 0.f : exp2f(sv[k] - mn);
+      rs += p[nt][k];
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    l_run[nt] = l_run[nt] * alpha + rs;
+    m_run[nt] = mn;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) o[nt][mt] *= alpha;
+    }
+  }
+
+  // B operands of PV from 8 weights: hi and lo parts (packed: this lane's part)
+  auto make_b = [&](const float (&x)[8], u4& bh, u4& bl, bool bf) {
+    split8(x, bh, bl, bf);
+    if constexpr (C::kPack) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bh[k] = lo_lane ? bl[k] : bh[k];
+    }
+  };
+
+  // ---- O^T += V^T P'^T
+  if constexpr (F::kQuant) {
+    const float* vsc = reinterpret_cast<const float*>(wl + F::kVtile);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const f4 d0 = *reinterpret_cast<const f4*>(vsc + b * 32 + 4 * g);
+      const f4 d1 = *reinterpret_cast<const f4*>(vsc + b * 32 + 16 + 4 * g);
+      const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      u4 bh[NT], bl[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float x[8];
+        if constexpr (KT == kQ4_0) {
+          constexpr int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]] * dv[pi[e]];
+        } else {
+          constexpr int pi[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]] * dv[pi[e]];
+        }
+        make_b(x, bh[nt], bl[nt], false);
+      }
+      if constexpr (KT == kQ4_0) {
+        // source lane n supplies key sigma(g, n % 8), code bytes [8 (n / 8), +8) of block b
+        const uint8_t* src = wl + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
+        const i2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2*)(src));
+        const u4 a0 = q4_operand(static_cast<uint32_t>(r[0]));
+        const u4 a1 = q4_operand(static_cast<uint32_t>(r[1]));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          o[nt][2 * b] = mma(a0, bh[nt], o[nt][2 * b], false);
+          o[nt][2 * b + 1] = mma(a1, bh[nt], o[nt][2 * b + 1], false);
+          if constexpr (C::kParts == 2) {
+            o[nt][2 * b] = mma(a0, bl[nt], o[nt][2 * b], false);
+            o[nt][2 * b + 1] = mma(a1, bl[nt], o[nt][2 * b + 1], false);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int hm = 0; hm < 2; ++hm) {
+          // source lane n supplies key sigma(g, n / 2), code bytes [16 hm + 8 (n % 2), +8)
+          const uint8_t* src = wl + sigma(g, n >> 1) * F::kVks + 32 * b + 16 * hm + 8 * (n & 1);
+          const i2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(src));
+          const u4 a = q8_operand(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1]));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            o[nt][2 * b + hm] = mma(a, bh[nt], o[nt][2 * b + hm], false);
+            if constexpr (C::kParts == 2) o[nt][2 * b + hm] = mma(a, bl[nt], o[nt][2 * b + hm], false);
+          }
+        }
+      }
+    }
+  } else {
+    u4 bh[NT], bl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) make_b(p[nt], bh[nt], bl[nt], BF);
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) {
+      // source lane n supplies key sigma(g, n / 4) (then sigma(g, 4 + n / 4)), halves [16 mt + 4 (n % 4), +4)
+      const uint8_t* s0 = wl + sigma(g, n >> 2) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
+      const uint8_t* s1 = wl + sigma(g, 4 + (n >> 2)) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
+      const s4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s0));
+      const s4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s1));
+      const u2 ua = __builtin_bit_cast(u2, ra), ub = __builtin_bit_cast(u2, rb);
+      const u4 a = {ua[0], ua[1], ub[0], ub[1]};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        o[nt][mt] = mma(a, bh[nt], o[nt][mt], BF);
+        if constexpr (C::kParts == 2) o[nt][mt] = mma(a, bl[nt], o[nt][mt], BF);
+      }
+    }
+  }
+}
+
+// Output dim of accumulator element (M-tile mt, lane group g, element i).
+template <int KT>
+__device__ inline int out_dim(int mt, int g, int i) {
+  const int m = 4 * g + i;
+  if constexpr (KT == kQ4_0) return 32 * (mt >> 1) + 16 * (m & 1) + 8 * (mt & 1) + (m >> 1);
+  return 16 * mt + m;
+}
+
+// Register double-buffering of the next tile pays for the compact quant rows;
+// the 16-bit rows use a single buffer (their loads are large enough that the
+// other waves cover the latency).
+template <int KT, int T>
+constexpr bool kDoubleBuffer = (KT == kQ4_0) || (KT == kQ8_0 && T != 2);
+
+template <int KT, int T>
+__global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(DecodeParams p) {
+  using F = Fmt<KT>;
+  using C = Cols<T>;
+  constexpr int R = C::R;
+  constexpr int NT = C::NT;
+  constexpr bool BF = F::kBf;
+  constexpr int kRed = 4 * R * kHeadDim * 4;
+  constexpr int kLds = (4 * F::kWave > kRed) ? 4 * F::kWave : kRed;
+  constexpr int kQLds = C::kPack ? 16 : NT * 2 * 8 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
+  __shared__ float ml_lds[4][R][2];
+  __shared__ long long sh_sum[4];
+  __shared__ int sh_loc[2];
+  __shared__ int sh_bad[4];
+  __shared__ MergeShared msh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int cap = p.bt_stride * p.page_size;
+  const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum);
+  const int jj = blockIdx.x / kKvHeads, h = blockIdx.x % kKvHeads;
+  plan_locate(p.seq_lens, p.n_seq, cap, chunk, jj, sh_loc);
+  const int s = sh_loc[0], c = sh_loc[1];
+  if (s < 0) return;
+  const int L = p.seq_lens[s];
+  const int nc = n_chunks_of(L, cap, chunk);
+  const size_t item = blockIdx.x;
+
+  if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
+    const float nan = __builtin_nanf("");
+    for (int i = tid; i < R * kHeadDim; i += kThreads) {
+      const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, gq = r % 6;
+      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + d] = nan;
+    }
+    if (p.lse_out && tid < R)
+      p.lse_out[(static_cast<size_t>(s) * T + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
+    if (tid == 0) atomicOr(p.err, 2u);
+    return;
+  }
+  const int k0 = c * chunk;
+  const int k1 = min(L, k0 + chunk);
+
+  // ---- query operands (B of QK^T): q * scale * log2 e split hi + lo.  The
+  // element order matches the K operand's dim order of each type.  One token:
+  // registers; more: an LDS copy built by the 4 waves (2 blocks each).
+  QSrc<T> qs;
+  qs.base = q_lds;
+  int lim[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = C::kPack ? (n & 7) : 16 * nt + n;    // query row of this lane's column
+    lim[nt] = L - T + r / 6;                           // its token sees positions <= lim
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = C::kPack ? (n & 7) : 16 * nt + n;
+    const bool live = r < R;
+    const float* qrow = p.q + ((static_cast<size_t>(s) * T + (live ? r / 6 : 0)) * kQHeads + h * kGroup +
+                               (live ? r % 6 : 0)) * kHeadDim;
+#pragma unroll
+    for (int bb = 0; bb < (C::kPack ? 8 : 2); ++bb) {
+      const int b = C::kPack ? bb : 2 * wave + bb;
+      float x[8];
+      if constexpr (KT == kQ4_0) {
+        const float4 lo = *reinterpret_cast<const float4*>(qrow + 32 * b + 4 * g);
+        const float4 hi = *reinterpret_cast<const float4*>(qrow + 32 * b + 16 + 4 * g);
+        x[0] = lo.x; x[1] = lo.z; x[2] = hi.x * 0.0625f; x[3] = hi.z * 0.0625f;
+        x[4] = lo.y; x[5] = lo.w; x[6] = hi.y * 0.0625f; x[7] = hi.w * 0.0625f;
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * g);
+        const float4 bq = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * g + 4);
+        if constexpr (KT == kQ8_0) {
+          x[0] = a.x; x[1] = a.z; x[2] = a.y; x[3] = a.w; x[4] = bq.x; x[5] = bq.z; x[6] = bq.y; x[7] = bq.w;
+        } else {
+          x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = bq.x; x[5] = bq.y; x[6] = bq.z; x[7] = bq.w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = live ? x[i] * p.scale_log2 : 0.f;
+      u4 hi, lo;
+      split8(x, hi, lo, BF);
+      if constexpr (C::kPack) {
+        qs.q[b] = (n & 8) ? lo : hi;
+      } else {
+        *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 0) * 8 + b) * 1024 + lane * 16) = hi;
+        *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 1) * 8 + b) * 1024 + lane * 16) = lo;
+      }
+    }
+  }
+  if constexpr (!C::kPack) __syncthreads();
+
+  f4 o[NT][16];
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = kNegInf;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  uint8_t* wl = lds + wave * F::kWave;
+  bool bad = false;
+  const int n_tiles = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
+  if constexpr (kDoubleBuffer<KT, T>) {
+    // the next tile's loads are in flight while the current one is computed
+    Tile<KT> ta, tb2;
+    int ti = wave;
+    if (ti < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * ti, k1, ta, bad);
+    while (ti < n_tiles) {
+      stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
+      wave_lds_sync();
+      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k1, tb2, bad);
+      compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
+      wave_lds_sync();
+      ti += 4;
+      if (ti >= n_tiles) break;
+      stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
+      wave_lds_sync();
+      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k1, ta, bad);
+      compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
+      wave_lds_sync();
+      ti += 4;
+    }
+  } else {
+    for (int ti = wave; ti < n_tiles; ti += 4) {
+      Tile<KT> tt;
+      load_tile<KT>(p, s, h, k0 + 32 * ti, k1, tt, bad);
+      stage_tile<KT>(wl, tt, k0 + 32 * ti, k1);
+      wave_lds_sync();
+      compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
+      wave_lds_sync();
+    }
+  }
+  if constexpr (C::kPack) {     // add the lo-part columns into the hi-part columns
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[0][mt][i] += __shfl_xor(o[0][mt][i], 8, 64);
+  }
+
+  // ---- combine the 4 waves, write this chunk's rows, then merge
+  __syncthreads();                       // every wave is done with its LDS tile region
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = 16 * nt + n;
+      if (r < R) {
+        ml_lds[wave][r][0] = m_run[nt];
+        ml_lds[wave][r][1] = l_run[nt];
+      }
+    }
+  }
+  if (lane == 0) sh_bad[wave] = __ballot(bad) ? 1 : 0;
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);       // [4 waves][R][256]
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = 16 * nt + n;
+    if (r < R) {
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
+      const float a = (m_run[nt] == kNegInf) ? 0.f : exp2f(m_run[nt] - M);
+      float* dst = red + (wave * R + r) * kHeadDim;
+#pragma unroll
+      for (int mt = 0; mt < 16; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[out_dim<KT>(mt, g, i)] = o[nt][mt][i] * a;
+      }
+    }
+  }
+  __syncthreads();
+  const bool any_bad = (sh_bad[0] | sh_bad[1] | sh_bad[2] | sh_bad[3]) != 0;
+  const float nan = __builtin_nanf("");
+  for (int r = 0; r < R; ++r) {
+    const int t = r / 6, gq = r % 6;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
+    float ltot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = ml_lds[w][r][0];
+      ltot += (mw == kNegInf) ? 0.f : ml_lds[w][r][1] * exp2f(mw - M);
+    }
+    const float sum = red[(0 * R + r) * kHeadDim + tid] + red[(1 * R + r) * kHeadDim + tid] +
+                      red[(2 * R + r) * kHeadDim + tid] + red[(3 * R + r) * kHeadDim + tid];
+    float val = ltot > 0.f ? sum / ltot : 0.f;
+    float lse2 = ltot > 0.f ? M + __log2f(ltot) : kNegInf;
+    if (any_bad) {
+      val = nan;
+      lse2 = nan;
+    }
+    if (nc == 1) {
+      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + tid] = val;
+      if (p.lse_out && tid == 0)
+        p.lse_out[(static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq] = lse2 * kLn2;
+    } else {
+      p.part_o[(item * kRowsPerItem + r) * kHeadDim + tid] = val;
+      if (tid == 0) p.part_lse[item * kRowsPerItem + r] = lse2;
+    }
+  }
+  if (any_bad && tid == 0) atomicOr(p.err, 1u);
+  if (nc > 1) fused_merge<T>(p, s, h, c, nc, jj - c, msh);
+}
+
+template <int KT>
+hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.max_items), block(kThreads);
+  switch (p.n_qtok) {
+    case 1: hipLaunchKernelGGL((split_mfma_kernel<KT, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((split_mfma_kernel<KT, 2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((split_mfma_kernel<KT, 3>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((split_mfma_kernel<KT, 4>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_split_mfma(const DecodeParams& p, hipStream_t stream) {
+  switch (p.k_type) {
+    case kF16: return launch_kt<kF16>(p, stream);
+    case kBF16: return launch_kt<kBF16>(p, stream);
+    case kQ8_0: return launch_kt<kQ8_0>(p, stream);
+    case kQ4_0: return launch_kt<kQ4_0>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -32,8 +32,11 @@ def workspace(n_seq, n_qtok):
     return ws
 
 
+ENGINES = {"mfma": 0, "valu": pb.DECODE_VECTOR_REFERENCE}
+
+
 def run(w, *, contiguous=False, kc=None, vc=None, scale=None, lse=False, ws=None, dq=None, dk=None, dv=None,
-        dbt=None, dlens=None, out=None, events=None, stream=None):
+        dbt=None, dlens=None, out=None, events=None, stream=None, engine="mfma"):
     """Decode workload ``w`` (synth.Workload) through pa_decode with an ext.
     Returns (out np.float32, lse np.float32 or None, error word)."""
     n_seq = len(w["seq_lens"])
@@ -58,7 +61,7 @@ def run(w, *, contiguous=False, kc=None, vc=None, scale=None, lse=False, ws=None
     lse_t = torch.empty((n_seq, T, 24), dtype=torch.float32, device="cuda") if lse else None
     ws = workspace(n_seq, T) if ws is None else ws
     ext = pb.make_ext(bt_stride, nblocks, w["scale"] if scale is None else scale, lse_t, ws, ws.numel() * 4,
-                      split_events=events)
+                      split_events=events, flags=ENGINES[engine])
     pb.decode(dq, dk, dv, bt, dlens, T, kv, P, out, ext=ext, stream=stream)
     err = pb.device_error(ws, stream=stream)
     torch.cuda.synchronize()

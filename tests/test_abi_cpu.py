@@ -130,7 +130,7 @@ def test_decode_host_checks_fail_before_device_work():
     e = pb.make_ext(bt_stride=0)
     assert st(ext=e) == pb.ERR_INVALID
     e = pb.make_ext(bt_stride=4, n_pool_blocks=8)
-    e.reserved = 1
+    e.flags = 2                                             # unknown flag
     assert st(ext=e) == pb.ERR_INVALID
 
 
@@ -139,3 +139,21 @@ def test_append_host_checks():
     z = np.zeros((1, 4, 144), np.uint8)
     assert pool.append_kv([0], [0], z, z, stream=0) == pb.ERR_INVALID       # host-only pool
     pool.destroy()
+
+
+def test_workspace_size_is_accepted_and_needed():
+    # pa_decode must accept a workspace of exactly pa_decode_workspace_size()
+    # bytes for every n_seq / n_qtok, and refuse one a work item (24,680 bytes)
+    # smaller.  On a
+    # machine without a GPU a call that passes every host check fails at the
+    # launch with PA_ERR_HIP, never with PA_ERR_INVALID.
+    a = 1 << 20
+    for n_seq in list(range(1, 70)) + [127, 128, 129, 500, 512, 1000]:
+        for T in (1, 4):
+            n = pb.workspace_size(n_seq, T, 0)
+            ok = pb.make_ext(8, 64, 0.0, None, 1 << 30, n)
+            st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q8_0"), 16, a, 0, ok)
+            assert st != pb.ERR_INVALID, (n_seq, T, n)
+            small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 24680)
+            st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q8_0"), 16, a, 0, small)
+            assert st == pb.ERR_INVALID, (n_seq, T, n)

@@ -21,25 +21,30 @@ def _oracle(w, scale=None, bt=None, lens=None):
                                   w["scale"] if scale is None else scale)
 
 
-def test_config1_parity():
+ENGINES = ["mfma", "valu"]
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+def test_config1_parity(engine):
     w = synth.config1()
-    log("[case] config1 f16 1x1024 p16 shuffled")
-    out, lse, err = run(w, lse=True)
+    log(f"[case] config1 f16 1x1024 p16 shuffled, {engine}")
+    out, lse, err = run(w, lse=True, engine=engine)
     ref, rlse = _oracle(w)
     assert err == 0
     parity(out, ref, what="config1")
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-4)
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
-def test_small_ragged_parity(kind, T):
+def test_small_ragged_parity(kind, T, engine):
     # several chunks per sequence (the plan's granule is 64 keys), ragged
     # tails, empty and shorter-than-T sequences, pages of 48 positions
     lens = [0, 2, 63, 64, 65, 700, 1500, 3001]
     w = synth.make_workload(f"small_{kind}_{T}", lens, T, kind, kind, 48, table="shuffled", seed=11 + T)
-    log(f"[case] small ragged {kind} T={T} P=48 lens={lens}")
-    out, lse, err = run(w, lse=True)
+    log(f"[case] small ragged {kind} T={T} P=48 lens={lens} {engine}")
+    out, lse, err = run(w, lse=True, engine=engine)
     ref, rlse = _oracle(w)
     assert err == 0
     parity(out, ref, what=f"small {kind} T={T}")
@@ -48,31 +53,35 @@ def test_small_ragged_parity(kind, T):
     assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-3
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("kind", KINDS)
-def test_unscaled_data_scale_one(kind):
+def test_unscaled_data_scale_one(kind, engine):
     # logits of order 16 exercise the max subtraction (config 1 data barely do)
     w = synth.make_workload(f"unscaled_{kind}", [333, 2048, 17], 2, kind, kind, 16, seed=21, scale=1.0)
-    log(f"[case] unscaled {kind}")
-    out, _, err = run(w)
+    log(f"[case] unscaled {kind} {engine}")
+    out, _, err = run(w, engine=engine)
     ref, _ = _oracle(w)
     parity(out, ref, what=f"unscaled {kind}")
 
 
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("P", [16, 48, 128, 256, 512])
-def test_paged_equals_contiguous_bitwise(P):
+def test_paged_equals_contiguous_bitwise(P, engine):
     lens = [5 * P + 3, 2 * P, 1, 9 * P - 1]
-    for kind in ("q4_0", "bf16"):
-        w = synth.make_workload(f"pc_{kind}_{P}", lens, 3, kind, kind, P, table="shuffled", seed=P)
-        log(f"[case] paged==contiguous {kind} P={P}")
+    for kind in ("q4_0", "bf16", "q8_0", "f16"):
+        T = 1 + (P // 16) % 4
+        w = synth.make_workload(f"pc_{kind}_{P}", lens, T, kind, kind, P, table="shuffled", seed=P)
+        log(f"[case] paged==contiguous {kind} P={P} T={T} {engine}")
         kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], lens, w["block_table"].shape[1] * P)
         vc = synth.contiguous_from_table(w["v_pool"], w["block_table"], lens, w["block_table"].shape[1] * P)
-        a, al, _ = run(w, lse=True)
-        b, bl, _ = run(w, contiguous=True, kc=kc, vc=vc, lse=True)
+        a, al, _ = run(w, lse=True, engine=engine)
+        b, bl, _ = run(w, contiguous=True, kc=kc, vc=vc, lse=True, engine=engine)
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
         assert np.array_equal(al.view(np.uint32), bl.view(np.uint32))
+        parity(a, _oracle(w)[0], what=f"pc {kind} P={P}")
         # three repeats are identical
         for _ in range(2):
-            c, _, _ = run(w)
+            c, _, _ = run(w, engine=engine)
             assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
 
 
@@ -89,13 +98,14 @@ def test_round_robin_vs_shuffled_bitwise():
     parity(oa, _oracle(a)[0], what="round robin")
 
 
-def test_corrupt_table_and_length():
+@pytest.mark.parametrize("engine", ENGINES)
+def test_corrupt_table_and_length(engine):
     w = synth.make_workload("corrupt", [100, 900, 40, 3000], 2, "q8_0", "q8_0", 16, seed=31)
-    log("[case] corrupt table entry / length")
+    log(f"[case] corrupt table entry / length {engine}")
     bt = w["block_table"].copy()
     bt[1, 3] = w["n_blocks"] + 7          # out of range
     bt[3, 100] = -5
-    out, _, err = run(w, dbt=dev(bt))
+    out, _, err = run(w, dbt=dev(bt), engine=engine)
     assert err & pb.DEVERR_TABLE
     ref, _ = _oracle(w, bt=bt)
     assert np.all(np.isnan(out[1])) and np.all(np.isnan(out[3]))
@@ -103,7 +113,7 @@ def test_corrupt_table_and_length():
     lens = w["seq_lens"].copy()
     lens[2] = 16 * w["block_table"].shape[1] + 1
     lens[0] = -3
-    out, _, err = run(w, dlens=dev(lens))
+    out, _, err = run(w, dlens=dev(lens), engine=engine)
     assert err & pb.DEVERR_LENGTH
     assert np.all(np.isnan(out[0])) and np.all(np.isnan(out[2]))
     parity(out[[1, 3]], _oracle(w)[0][[1, 3]], what="intact after bad lengths")
