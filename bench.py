@@ -36,7 +36,29 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only time a plain 2 GiB device-to-device copy (read-bandwidth ceiling; also the "
+                         "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_ceiling(steps=20, nbytes=2 << 30):
+    """Bandwidth of torch's device copy over `nbytes` (read nbytes + write nbytes)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes, "ms_per_copy": round(ms, 4),
+            "read_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1), "read_plus_write_gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def kernel_source_hash():
@@ -97,6 +119,9 @@ def main():
     from paged_kv_attention_walk_amd import synth
 
     torch.cuda.set_device(0)
+    if args.ceiling:
+        print(json.dumps({"copy_ceiling": copy_ceiling()}), flush=True)
+        return
     t_gen = time.perf_counter()
     if args.workload == "ragged":
         w = synth.config3()

@@ -208,10 +208,8 @@ typedef struct pa_decode_ext {
                                 for a row with no visible key                           */
     void    *workspace;      /* device scratch of at least pa_decode_workspace_size()
                                 bytes, 256-byte aligned, or NULL for the pool's own
-                                workspace.  Its first pa_decode must find it zeroed
-                                (e.g. one hipMemset); every call leaves its internal
-                                counters at zero again.  Pass the same workspace_bytes
-                                with every call that uses it                            */
+                                workspace.  Its first 4 bytes are the device error
+                                word: zero them before the first use (e.g. hipMemset) */
     size_t   workspace_bytes;
     void    *split_events[2];/* optional hipEvent_t pair, recorded on `stream` just
                                 before and after the split kernel (profiling)           */

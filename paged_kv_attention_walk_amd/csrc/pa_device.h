@@ -264,79 +264,99 @@ __device__ inline void v_dims4(const uint8_t* __restrict__ row, int lane, float 
   }
 }
 
-// ------------------------------------------------------------ fused merge
+// ------------------------------------------------------------------ merge
 //
-// Chunks of one (sequence, KV head) are merged inside the split kernel, in a
-// fixed order, by whichever workgroup arrives last:
-//  level 1: chunks are grouped 16 at a time; the last of a group to finish
-//           merges the group's partials (chunk order) into the slot of the
-//           group's first chunk;
-//  level 2: the last group to finish merges the group results (group order)
-//           into the output.
-// The arithmetic and its order do not depend on which workgroup runs it, so
-// results are bitwise repeatable.  Arrival counters live in the workspace and
-// are reset by the workgroup that consumes them.  Visibility of partials
-// across workgroups (and across the per-XCD L2 caches) comes from
-// device-scope fences around the counter updates: every writer fences before
-// arriving, the consumer fences after it sees it is last.
-//
-// M = max lse; all -inf merges to 0 with lse -inf (llama.cpp pull 2,
-// pd_combine fix); a NaN partial (corrupt table) gives NaN; otherwise
+// Chunks of one (sequence, KV head) are combined by a second kernel, one
+// workgroup per (sequence, KV head, query row).  M = max lse; all -inf gives
+// 0 with lse -inf (llama.cpp pull 2, pd_combine fix: an all-masked row is 0,
+// not 0/0); a NaN partial (corrupt table) gives NaN; otherwise
 // out = sum_c w_c o_c / sum_c w_c with w_c = 2^(lse_c - M) (lse in base 2).
-constexpr int kGroupChunks = 16;
-constexpr int kMaxMergeParts = 64;
+// The 4 waves take chunks c = w, w+4, ... (lane = 4 dims, float4 loads) and
+// are added in wave order, so the result is bitwise repeatable.
+constexpr int kMaxMergeChunks = 2048;
 
 struct MergeShared {
-  float w[kMaxMergeParts * 6 * kMaxQtok];
-  float M[6 * kMaxQtok];
-  float ws[6 * kMaxQtok];
-  int flag;
+  float w[kMaxMergeChunks];
+  float4 part[4][64];
+  long long sum[4];
+  float red[8];
 };
 
-// Merges np partials at item slots slot(k) = first_item + k * stride (k in
-// order) for all R rows.  Writes the result to the output (final) or over
-// slot(0).  All threads of the workgroup call it.
+// Number of (sequence, chunk) pairs before sequence s.
+__device__ inline int plan_prefix(const int32_t* __restrict__ lens, int s, int cap, int chunk, long long* sh) {
+  long long acc = 0;
+  for (int i = threadIdx.x; i < s; i += kThreads) acc += n_chunks_of(lens[i], cap, chunk);
+  return static_cast<int>(block_sum(acc, sh));
+}
+
+__device__ inline float block_max_f(float v, float* sh) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+}
+
+__device__ inline float block_sum_f(float v, float* sh) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[4 + (threadIdx.x >> 6)] = v;
+  __syncthreads();
+  return (sh[4] + sh[5]) + (sh[6] + sh[7]);
+}
+
 template <int T>
-__device__ void merge_parts(const DecodeParams& p, int s, int h, size_t first_item, int stride, int np, bool final,
-                            MergeShared& sh) {
+__device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   constexpr int R = 6 * T;
+  const int row_id = blockIdx.x;
+  const int r = row_id % R;
+  const int sh_id = row_id / R;
+  const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < np * R; i += kThreads) {
-    const int k = i / R, r = i % R;
-    sh.w[i] = p.part_lse[(first_item + static_cast<size_t>(k) * stride) * kRowsPerItem + r];
+  const int cap = p.bt_stride * p.page_size;
+  const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh.sum);
+  const int nc = n_chunks_of(p.seq_lens[s], cap, chunk);
+  if (nc <= 1) return;                                   // written by the split kernel
+  const int base = plan_prefix(p.seq_lens, s, cap, chunk, sh.sum);
+  const size_t item0 = static_cast<size_t>(base) * kKvHeads + h;   // chunk c at item0 + c * 4
+  // weights
+  float mx = kNegInf;
+  bool nan = false;
+  for (int c = tid; c < nc; c += kThreads) {
+    const float x = p.part_lse[(item0 + static_cast<size_t>(c) * kKvHeads) * kRowsPerItem + r];
+    sh.w[c] = x;
+    nan |= (x != x);
+    mx = fmaxf(mx, x);
   }
-  __syncthreads();
-  if (tid < R) {
-    float M = kNegInf;
-    bool nan = false;
-    for (int k = 0; k < np; ++k) {
-      const float x = sh.w[k * R + tid];
-      nan |= (x != x);
-      M = fmaxf(M, x);
-    }
-    float ws = 0.f;
-    for (int k = 0; k < np; ++k) {
-      const float x = sh.w[k * R + tid];
-      const float wk = (M == kNegInf || x == kNegInf) ? 0.f : exp2f(x - M);
-      sh.w[k * R + tid] = wk;
-      ws += wk;
-    }
-    sh.M[tid] = nan ? __builtin_nanf("") : M;
-    sh.ws[tid] = ws;
+  const bool any_nan = __syncthreads_or(nan);
+  const float M = block_max_f(mx, sh.red);
+  float ws = 0.f;
+  for (int c = tid; c < nc; c += kThreads) {
+    const float x = sh.w[c];
+    const float wc = (M == kNegInf || x == kNegInf) ? 0.f : exp2f(x - M);
+    sh.w[c] = wc;
+    ws += wc;
   }
+  ws = block_sum_f(ws, sh.red);          // ends with a barrier: sh.w is complete
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = wave; c < nc; c += 4) {
+    const float wc = sh.w[c];
+    const float4 o = *reinterpret_cast<const float4*>(
+        p.part_o + ((item0 + static_cast<size_t>(c) * kKvHeads) * kRowsPerItem + r) * kHeadDim + 4 * lane);
+    acc.x += wc * o.x; acc.y += wc * o.y; acc.z += wc * o.z; acc.w += wc * o.w;
+  }
+  sh.part[wave][lane] = acc;
   __syncthreads();
-  for (int r = wave; r < R; r += 4) {
-    const float M = sh.M[r], ws = sh.ws[r];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < np; ++k) {
-      const float wk = sh.w[k * R + r];
-      const float4 o = *reinterpret_cast<const float4*>(
-          p.part_o + ((first_item + static_cast<size_t>(k) * stride) * kRowsPerItem + r) * kHeadDim + 4 * lane);
-      acc.x += wk * o.x; acc.y += wk * o.y; acc.z += wk * o.z; acc.w += wk * o.w;
+  if (wave == 0) {
+    float4 t = sh.part[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 u = sh.part[w][lane];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
     }
     float4 val;
     float lse2;
-    if (M != M) {
+    if (any_nan) {
       val = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
       lse2 = __builtin_nanf("");
     } else if (M == kNegInf) {
@@ -344,54 +364,14 @@ __device__ void merge_parts(const DecodeParams& p, int s, int h, size_t first_it
       lse2 = kNegInf;
     } else {
       const float inv = 1.f / ws;
-      val = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      val = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
       lse2 = M + __log2f(ws);
     }
-    const int t = r / 6, g = r % 6;
-    if (final) {
-      *reinterpret_cast<float4*>(p.out + ((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + g) * kHeadDim +
-                                 4 * lane) = val;
-      if (p.lse_out && lane == 0) p.lse_out[(static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + g] = lse2 * kLn2;
-    } else {
-      *reinterpret_cast<float4*>(p.part_o + (first_item * kRowsPerItem + r) * kHeadDim + 4 * lane) = val;
-      if (lane == 0) p.part_lse[first_item * kRowsPerItem + r] = lse2;
-    }
+    const int tt = r / 6, g = r % 6;
+    *reinterpret_cast<float4*>(p.out + ((static_cast<size_t>(s) * T + tt) * kQHeads + h * kGroup + g) * kHeadDim +
+                               4 * lane) = val;
+    if (p.lse_out && lane == 0) p.lse_out[(static_cast<size_t>(s) * T + tt) * kQHeads + h * kGroup + g] = lse2 * kLn2;
   }
-}
-
-// Arrives at counter *cnt of a group of `expected` members; returns true in
-// every thread of the last arriving workgroup, which also resets the counter.
-__device__ inline bool arrive_last(uint32_t* cnt, int expected, MergeShared& sh) {
-  __threadfence();      // this thread's partial writes are visible device-wide before arriving
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(cnt, 1u);
-    const bool last = old == static_cast<uint32_t>(expected - 1);
-    if (last) atomicExch(cnt, 0u);
-    sh.flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = sh.flag != 0;
-  if (last) __threadfence();   // see every member's writes
-  return last;
-}
-
-// After the workgroup of chunk c (of nc) of (s, h) has written its partial
-// to item slot (base + c) * 4 + h: runs the two merge levels when it arrives
-// last.  base = index of chunk 0 of sequence s among all (sequence, chunk) pairs.
-template <int T>
-__device__ void fused_merge(const DecodeParams& p, int s, int h, int c, int nc, int base, MergeShared& sh) {
-  const int g = c / kGroupChunks;
-  const int n_groups = (nc + kGroupChunks - 1) / kGroupChunks;
-  const int g_first = g * kGroupChunks;
-  const int g_size = min(kGroupChunks, nc - g_first);
-  const size_t g_item = static_cast<size_t>(base + g_first) * kKvHeads + h;
-  if (!arrive_last(p.cnt1 + g_item, g_size, sh)) return;
-  merge_parts<T>(p, s, h, g_item, kKvHeads, g_size, n_groups == 1, sh);
-  if (n_groups == 1) return;
-  const size_t first_item = static_cast<size_t>(base) * kKvHeads + h;
-  if (!arrive_last(p.cnt2 + first_item, n_groups, sh)) return;
-  merge_parts<T>(p, s, h, first_item, kKvHeads * kGroupChunks, n_groups, true, sh);
 }
 
 }  // namespace dev

@@ -202,7 +202,7 @@ pa_status pa_pool_create(const pa_pool_desc* d, pa_pool** out) {
     const pa::WorkspaceLayout wl = pa::workspace_layout(p->desc.max_seqs, target_items(d->device));
     p->workspace_bytes = wl.total;
     st = hip_status(hipMalloc(&p->workspace, p->workspace_bytes));
-    if (st == PA_OK) st = hip_status(hipMemset(p->workspace, 0, wl.lse_off));   // error word + counters
+    if (st == PA_OK) st = hip_status(hipMemset(p->workspace, 0, wl.lse_off));   // error word
   }
   const size_t sbytes = pa::staging_bytes(p->desc.max_append_rows, p->rb_k, p->rb_v);
   for (int i = 0; st == PA_OK && i < kStagingSlots; ++i) {
@@ -427,8 +427,6 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   prm.lse_out = lse_out;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   prm.err = reinterpret_cast<uint32_t*>(wsb);
-  prm.cnt1 = reinterpret_cast<uint32_t*>(wsb + wl.cnt1_off);
-  prm.cnt2 = reinterpret_cast<uint32_t*>(wsb + wl.cnt2_off);
   prm.part_lse = reinterpret_cast<float*>(wsb + wl.lse_off);
   prm.part_o = reinterpret_cast<float*>(wsb + wl.o_off);
   prm.n_seq = n_seq;

@@ -40,8 +40,6 @@ struct DecodeParams {
   float* part_o;           // [item capacity][24][256]
   float* part_lse;         // [item capacity][24]   (log2 units)
   uint32_t* err;           // error word
-  uint32_t* cnt1;          // [max_items] arrival counters of 16-chunk groups (zero between calls)
-  uint32_t* cnt2;          // [max_items] arrival counters of (sequence, KV head) groups
   int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
   int32_t target_items;    // occupancy target of the chunk plan
   int32_t max_items;       // work items the grid covers
@@ -57,25 +55,21 @@ inline int64_t max_work_items(int64_t n_seq, int64_t target_items) {
 
 struct WorkspaceLayout {
   int64_t items;       // work-item capacity
-  size_t cnt1_off, cnt2_off, lse_off, o_off, total;
+  size_t lse_off, o_off, total;
 };
 
 PA_HD inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kRowsPerItem = 6 * kMaxQtok;   // partial rows reserved per work item
 
-// Workspace: [0, 256) header (error word at 0); two arrays of arrival
-// counters; chunk log-sum-exps; chunk outputs.  The layout depends only on
-// the item capacity, never on the call's n_seq or n_qtok, so one workspace can
-// serve calls of any shape it has room for without partials ever landing on
-// counters.  Counters and the error word must be zero before the first call;
-// every call leaves the counters at zero.
+// Workspace: [0, 256) header (error word at 0); chunk log-sum-exps; chunk
+// outputs.  The layout depends only on the item capacity, never on the call's
+// n_seq or n_qtok, so one workspace serves calls of any shape it has room
+// for.  The error word must be zero before the first call.
 inline WorkspaceLayout workspace_layout_items(int64_t items) {
   WorkspaceLayout w;
   w.items = items;
-  w.cnt1_off = 256;
-  w.cnt2_off = w.cnt1_off + static_cast<size_t>(items) * 4;
-  w.lse_off = align_up(w.cnt2_off + static_cast<size_t>(items) * 4, 256);
+  w.lse_off = 256;
   w.o_off = align_up(w.lse_off + static_cast<size_t>(items) * kRowsPerItem * sizeof(float), 256);
   w.total = align_up(w.o_off + static_cast<size_t>(items) * kRowsPerItem * kHeadDim * sizeof(float), 256);
   return w;
@@ -87,7 +81,7 @@ inline WorkspaceLayout workspace_layout(int64_t n_seq, int64_t target_items) {
 
 // The largest item capacity whose layout fits in `bytes`.
 inline WorkspaceLayout workspace_layout_for_bytes(size_t bytes) {
-  const size_t per = 8 + kRowsPerItem * sizeof(float) * (1 + kHeadDim);
+  const size_t per = kRowsPerItem * sizeof(float) * (1 + kHeadDim);
   int64_t items = static_cast<int64_t>(bytes / per) + 1;   // an upper bound; step down to the largest fit
   while (items > 0 && workspace_layout_items(items).total > bytes) --items;
   return workspace_layout_items(items);

@@ -14,8 +14,8 @@
 //    by every workgroup from seq_lens on the device (no host round trip), and
 //    identical for paged and contiguous storage;
 //  * each chunk writes its normalised output and log-sum-exp; a sequence with
-//    one chunk writes the final output directly, the others are combined in
-//    the same kernel by the last-arriving workgroups (see the fused merge).
+//    one chunk writes the final output directly, the others are combined by
+//    the merge kernel.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -49,7 +49,6 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
   __shared__ long long sh_sum[4];
   __shared__ int sh_loc[2];
   __shared__ int sh_bad[4];
-  __shared__ MergeShared msh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
@@ -196,7 +195,6 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
     __syncthreads();
   }
   if (any_bad && tid == 0) atomicOr(p.err, kErrTable);
-  if (nc > 1) fused_merge<T>(p, s, h, c, nc, j - c, msh);
 }
 
 // ----------------------------------------------------------- append scatter
@@ -250,6 +248,24 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
 
 // ------------------------------------------------------------- dispatch
 
+template <int T>
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
+  __shared__ MergeShared sh;
+  merge_row<T>(p, sh);
+}
+
+hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.n_seq * kKvHeads * 6 * p.n_qtok), block(kThreads);
+  switch (p.n_qtok) {
+    case 1: hipLaunchKernelGGL((merge_kernel<1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((merge_kernel<2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((merge_kernel<3>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((merge_kernel<4>), grid, block, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int KT>
 hipError_t launch_valu_kt(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.max_items), block(kThreads);
@@ -284,7 +300,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t e
   e = (p.engine == 1) ? launch_split_valu(p, stream) : launch_split_mfma(p, stream);
   if (e != hipSuccess) return e;
   if (ev_end) e = hipEventRecord(ev_end, stream);
-  return e;
+  if (e != hipSuccess) return e;
+  return launch_merge(p, stream);
 }
 
 hipError_t launch_scatter(const uint8_t* staging, int32_t n_rows, uint8_t* k_pool, uint8_t* v_pool,

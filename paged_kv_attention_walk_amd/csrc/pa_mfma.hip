@@ -147,8 +147,37 @@ struct Tile {
 
 // Loads tile registers.  lane = (m, g) for K, (j, seg) for V.  Halves past
 // the chunk end are not read.  Sets bad on an out-of-range table entry.
+// Physical pages of the chunk's logical pages [lp0, lp0 + n): staged in LDS
+// once per workgroup, so the tile loop never waits on a dependent table load.
+typedef __attribute__((address_space(3))) const int lds_int;
+
+struct PageMap {
+  lds_int* tbl;     // LDS copy (typed as LDS, so reading it never waits on global loads)
+  bool in_lds;      // false: read the table in memory
+  int lp0;
+};
+
+// Row index of the first row of the 16-position group starting at pos0
+// (a multiple of 16, so the group lies inside one page).  ok = false for a
+// table entry outside the pool (row 0 is returned, which is in bounds).
+__device__ inline size_t group_row(const DecodeParams& p, const PageMap& pm, int s, int h, int pos0, bool& ok) {
+  if (p.bt == nullptr) {
+    ok = true;
+    const size_t cap = static_cast<size_t>(p.bt_stride) * p.page_size;
+    return (static_cast<size_t>(s) * kKvHeads + h) * cap + pos0;
+  }
+  const int lp = pos0 / p.page_size;
+  int phys;
+  if (pm.in_lds) phys = pm.tbl[lp - pm.lp0];
+  else phys = p.bt[static_cast<size_t>(s) * p.bt_stride + lp];
+  ok = static_cast<unsigned>(phys) < static_cast<unsigned>(p.n_pool_blocks);
+  if (!ok) return 0;
+  return (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + (pos0 - lp * p.page_size);
+}
+
 template <int KT>
-__device__ inline void load_tile(const DecodeParams& p, int s, int h, int tb, int k1, Tile<KT>& t, bool& bad) {
+__device__ inline void load_tile(const DecodeParams& p, const PageMap& pm, int s, int h, int tb, int k1, Tile<KT>& t,
+                                 bool& bad) {
   using F = Fmt<KT>;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
@@ -159,7 +188,7 @@ __device__ inline void load_tile(const DecodeParams& p, int s, int h, int tb, in
     t.half_ok[hf] = false;
     if (pos0 < k1) {
       bool ok;
-      const size_t r0 = kv_row(p.bt, p.bt_stride, p.n_pool_blocks, p.page_size, s, h, pos0, ok);
+      const size_t r0 = group_row(p, pm, s, h, pos0, ok);
       if (!ok) bad = true;
       t.half_ok[hf] = ok;
       if (ok) {
@@ -508,6 +537,8 @@ __device__ inline int out_dim(int mt, int g, int i) {
 // Register double-buffering of the next tile pays for the compact quant rows;
 // the 16-bit rows use a single buffer (their loads are large enough that the
 // other waves cover the latency).
+constexpr int kTblCap = 1024;     // table entries staged in LDS per workgroup
+
 template <int KT, int T>
 constexpr bool kDoubleBuffer = (KT == kQ4_0) || (KT == kQ8_0 && T != 2);
 
@@ -523,13 +554,14 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int kQLds = C::kPack ? 16 : NT * 2 * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
+  __shared__ int tbl_lds[kTblCap];
   __shared__ float ml_lds[4][R][2];
   __shared__ long long sh_sum[4];
   __shared__ int sh_loc[2];
   __shared__ int sh_bad[4];
-  __shared__ MergeShared msh;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int cap = p.bt_stride * p.page_size;
   const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum);
@@ -554,6 +586,17 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   }
   const int k0 = c * chunk;
   const int k1 = min(L, k0 + chunk);
+
+  // ---- the chunk's block-table entries
+  PageMap pm{(lds_int*)(tbl_lds), false, 0};
+  if (p.bt != nullptr && k1 > k0) {
+    pm.lp0 = k0 / p.page_size;
+    const int n_tbl = (k1 - 1) / p.page_size - pm.lp0 + 1;
+    if (n_tbl <= kTblCap) {
+      for (int i = tid; i < n_tbl; i += kThreads) tbl_lds[i] = p.bt[static_cast<size_t>(s) * p.bt_stride + pm.lp0 + i];
+      pm.in_lds = true;
+    }
+  }
 
   // ---- query operands (B of QK^T): q * scale * log2 e split hi + lo.  The
   // element order matches the K operand's dim order of each type.  One token:
@@ -602,7 +645,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       }
     }
   }
-  if constexpr (!C::kPack) __syncthreads();
+  __syncthreads();                       // table entries (and, for more tokens, query operands)
 
   f4 o[NT][16];
   float m_run[NT], l_run[NT];
@@ -621,18 +664,18 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     // the next tile's loads are in flight while the current one is computed
     Tile<KT> ta, tb2;
     int ti = wave;
-    if (ti < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * ti, k1, ta, bad);
+    if (ti < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * ti, k1, ta, bad);
     while (ti < n_tiles) {
       stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k1, tb2, bad);
+      if (ti + 4 < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * (ti + 4), k1, tb2, bad);
       compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
       if (ti >= n_tiles) break;
       stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k1, ta, bad);
+      if (ti + 4 < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * (ti + 4), k1, ta, bad);
       compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
@@ -640,7 +683,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   } else {
     for (int ti = wave; ti < n_tiles; ti += 4) {
       Tile<KT> tt;
-      load_tile<KT>(p, s, h, k0 + 32 * ti, k1, tt, bad);
+      load_tile<KT>(p, pm, s, h, k0 + 32 * ti, k1, tt, bad);
       stage_tile<KT>(wl, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
       compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
@@ -717,7 +760,6 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     }
   }
   if (any_bad && tid == 0) atomicOr(p.err, 1u);
-  if (nc > 1) fused_merge<T>(p, s, h, c, nc, jj - c, msh);
 }
 
 template <int KT>

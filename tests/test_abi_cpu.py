@@ -143,7 +143,7 @@ def test_append_host_checks():
 
 def test_workspace_size_is_accepted_and_needed():
     # pa_decode must accept a workspace of exactly pa_decode_workspace_size()
-    # bytes for every n_seq / n_qtok, and refuse one a work item (24,680 bytes)
+    # bytes for every n_seq / n_qtok, and refuse one a work item (24,672 bytes)
     # smaller.  On a
     # machine without a GPU a call that passes every host check fails at the
     # launch with PA_ERR_HIP, never with PA_ERR_INVALID.
@@ -154,6 +154,6 @@ def test_workspace_size_is_accepted_and_needed():
             ok = pb.make_ext(8, 64, 0.0, None, 1 << 30, n)
             st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q8_0"), 16, a, 0, ok)
             assert st != pb.ERR_INVALID, (n_seq, T, n)
-            small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 24680)
+            small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 24672)
             st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q8_0"), 16, a, 0, small)
             assert st == pb.ERR_INVALID, (n_seq, T, n)
