@@ -339,10 +339,22 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   }
   ws = block_sum_f(ws, sh.red);          // ends with a barrier: sh.w is complete
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = wave; c < nc; c += 4) {
+  const float* base_o = p.part_o + (item0 * kRowsPerItem + r) * kHeadDim + 4 * lane;
+  const size_t cstride = static_cast<size_t>(kKvHeads) * kRowsPerItem * kHeadDim;   // floats between chunks
+  int c = wave;
+  for (; c + 28 < nc; c += 32) {          // 8 independent loads in flight per lane
+    float4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c + 4 * u) * cstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wc = sh.w[c + 4 * u];
+      acc.x += wc * o[u].x; acc.y += wc * o[u].y; acc.z += wc * o[u].z; acc.w += wc * o[u].w;
+    }
+  }
+  for (; c < nc; c += 4) {
     const float wc = sh.w[c];
-    const float4 o = *reinterpret_cast<const float4*>(
-        p.part_o + ((item0 + static_cast<size_t>(c) * kKvHeads) * kRowsPerItem + r) * kHeadDim + 4 * lane);
+    const float4 o = *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c) * cstride);
     acc.x += wc * o.x; acc.y += wc * o.y; acc.z += wc * o.z; acc.w += wc * o.w;
   }
   sh.part[wave][lane] = acc;

@@ -100,24 +100,38 @@ __device__ inline void split8(const float (&x)[8], u4& hi, u4& lo, bool bf) {
   }
 }
 
+// (x & mask) | (0x64006400 & ~mask): one bit-field insert.
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "v"(y));
+  return r;
+}
+
 // (x & mask) | 0x64006400 read as two f16 (1024 + field), minus `sub` each.
 __device__ inline uint32_t nib2h(uint32_t x, uint32_t mask, float sub) {
-  const uint32_t u = (x & mask) | 0x64006400u;
+  const uint32_t u = bfi(mask, x, 0x64006400u);
   h2 v = __builtin_bit_cast(h2, u);
   const h2 s = {static_cast<_Float16>(sub), static_cast<_Float16>(sub)};
   v = v - s;
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// 8 nibbles (bits 4k, k = 0..7) -> f16 operand, element order k = 0,4,1,5,2,6,3,7;
-// elements of odd k carry a factor 16 (the partner operand holds 1/16).
+// 8 nibbles (bits 4k, k = 0..7) -> f16 operand c - 8, element order
+// k = 0,4,1,5,2,6,3,7.  With X16, elements of odd k hold 16 (c - 8) instead
+// (one shift fewer; the partner operand then carries 1/16).
+template <bool X16>
 __device__ inline u4 q4_operand(uint32_t x) {
   const uint32_t y = x >> 8;
   u4 a;
-  a[0] = nib2h(x, 0x000F000Fu, 1032.f);   // k = 0, 4:  c - 8
-  a[1] = nib2h(x, 0x00F000F0u, 1152.f);   // k = 1, 5:  16 (c - 8)
-  a[2] = nib2h(y, 0x000F000Fu, 1032.f);   // k = 2, 6
-  a[3] = nib2h(y, 0x00F000F0u, 1152.f);   // k = 3, 7
+  a[0] = nib2h(x, 0x000F000Fu, 1032.f);                       // k = 0, 4
+  a[2] = nib2h(y, 0x000F000Fu, 1032.f);                       // k = 2, 6
+  if constexpr (X16) {
+    a[1] = nib2h(x, 0x00F000F0u, 1152.f);                     // k = 1, 5: 16 (c - 8)
+    a[3] = nib2h(y, 0x00F000F0u, 1152.f);                     // k = 3, 7
+  } else {
+    a[1] = nib2h(x >> 4, 0x000F000Fu, 1032.f);                // k = 1, 5
+    a[3] = nib2h(y >> 4, 0x000F000Fu, 1032.f);                // k = 3, 7
+  }
   return a;
 }
 
@@ -133,6 +147,29 @@ __device__ inline u4 q8_operand(uint32_t x0, uint32_t x1) {
 }
 
 __device__ inline uint32_t funnel16(uint32_t lo, uint32_t hi) { return (lo >> 16) | (hi << 16); }
+
+// a * d as hi + lo f16 pairs, exactly: a holds small integers (codes) and d
+// fp16 scales, so the product has at most 19 significant bits; hi is its f16
+// rounding and lo = fma(a, d, -hi) the remainder, which f16 holds exactly.
+__device__ inline uint32_t mul_h2(uint32_t a, uint32_t d) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, a) * __builtin_bit_cast(h2, d));
+}
+__device__ inline uint32_t residual_h2(uint32_t a, uint32_t d, uint32_t hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, d),
+                                                                -__builtin_bit_cast(h2, hi)));
+}
+// Written per component: a loop over the vector's elements was compiled into
+// element 0 replicated four times by this toolchain.
+__device__ inline void scale_exact(const u4 a, const u4 d, u4& hi, u4& lo) {
+  hi.x = mul_h2(a.x, d.x);
+  hi.y = mul_h2(a.y, d.y);
+  hi.z = mul_h2(a.z, d.z);
+  hi.w = mul_h2(a.w, d.w);
+  lo.x = residual_h2(a.x, d.x, hi.x);
+  lo.y = residual_h2(a.y, d.y, hi.y);
+  lo.z = residual_h2(a.z, d.z, hi.z);
+  lo.w = residual_h2(a.w, d.w, hi.w);
+}
 
 // Registers of one tile: K operands (per half, per block), K scales, raw V.
 template <int KT>
@@ -271,7 +308,7 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
         *reinterpret_cast<u4*>(w + key * F::kVks + 128 * seg + 16 * i) = x;
       }
     } else {
-      float* vsc = reinterpret_cast<float*>(w + F::kVtile);              // [8 blocks][32 keys]
+      float* vsc = reinterpret_cast<float*>(w + F::kVtile);              // V scales: [8 blocks][4 groups][8] fp16
       float* ksc = reinterpret_cast<float*>(w + F::kVtile + 1024);       // [2 halves][8 blocks][16 keys]
       const uint32_t* v = t.v[hf];
       u4 c0, c1, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
@@ -289,16 +326,9 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
         sa = v[0] & 0xFFFFu;
         sb = v[8] >> 16;
       }
-      float fa = half_bits(sa), fb = half_bits(sb);
-      if constexpr (KT == kQ4_0) {
-        if (key & 1) {      // odd keys: their V operand carries 16 (c - 8)
-          fa *= 0.0625f;
-          fb *= 0.0625f;
-        }
-      }
       if (!valid) {
         c0 = c1 = c2 = c3 = u4{0, 0, 0, 0};
-        fa = fb = 0.f;
+        sa = sb = 0u;
       }
       uint8_t* row = w + key * F::kVks;
       if constexpr (KT == kQ4_0) {
@@ -310,8 +340,17 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
         *reinterpret_cast<u4*>(row + 32 * (2 * seg + 1)) = c2;
         *reinterpret_cast<u4*>(row + 32 * (2 * seg + 1) + 16) = c3;
       }
-      vsc[(2 * seg) * 32 + key] = fa;
-      vsc[(2 * seg + 1) * 32 + key] = fb;
+      // V scales as f16 in the element order of the V operand of lane group
+      // g: key = 16 hf + 4 g + i is k-slot k = i + 4 hf of group g.
+      {
+        const int kk = (key & 3) + 4 * (key >> 4), gg = (key >> 2) & 3;
+        int pos;
+        if constexpr (KT == kQ4_0) pos = (kk & 3) * 2 + (kk >> 2);                 // pairs (0,4)(1,5)(2,6)(3,7)
+        else pos = (kk < 4) ? (kk & 1) * 2 + (kk >> 1) : 4 + ((kk - 4) & 1) * 2 + ((kk - 4) >> 1);  // (0,2)(1,3)(4,6)(5,7)
+        uint16_t* vh = reinterpret_cast<uint16_t*>(vsc);
+        vh[((2 * seg) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sa);        // fp16 bits as stored
+        vh[((2 * seg + 1) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sb);
+      }
       // K scales: lane (m, g) holds blocks 2g, 2g+1 of key m of this half
       float ka = half_bits(t.ks[hf] & 0xFFFFu), kb = half_bits(t.ks[hf] >> 16);
       if (!t.half_ok[hf]) ka = kb = 0.f;
@@ -358,7 +397,7 @@ struct QSrc {
 // the V rows staged in the wave's LDS region `wl`.
 template <int KT, int T>
 __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int k1,
-                                    const int (&lim)[Cols<T>::NT], const QSrc<T>& qs,
+                                    const int (&lim)[Cols<T>::NT], int lim_min, const QSrc<T>& qs,
                                     f4 (&o)[Cols<T>::NT][16], float (&m_run)[Cols<T>::NT],
                                     float (&l_run)[Cols<T>::NT]) {
   using F = Fmt<KT>;
@@ -378,7 +417,7 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       u4 a;
-      if constexpr (KT == kQ4_0) a = q4_operand(t.k[hf][b][0]);
+      if constexpr (KT == kQ4_0) a = q4_operand<true>(t.k[hf][b][0]);
       else if constexpr (KT == kQ8_0) a = q8_operand(t.k[hf][b][0], t.k[hf][b][1]);
       else a = u4{t.k[hf][b][0], t.k[hf][b][1], t.k[hf][b][2], t.k[hf][b][3]};
       if constexpr (F::kQuant) {
@@ -405,7 +444,10 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       for (int i = 0; i < 4; ++i) sacc[0][hf][i] += __shfl_xor(sacc[0][hf][i], 8, 64);
   }
 
-  // ---- online softmax (base 2); p[nt][k] is the weight of key sigma(g, k)
+  // ---- online softmax (base 2); p[nt][k] is the weight of key sigma(g, k).
+  // Masking is needed only where the tile crosses the chunk end or, for
+  // more than one token, the causal limit of some row (uniform test).
+  const bool full = (tb + 32 <= k1) && (tb + 31 <= lim_min);
   float p[NT][8];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -415,27 +457,36 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int pos = tb + 16 * hf + 4 * g + i;
-        const bool ok = t.half_ok[hf] && pos < k1 && pos <= lim[nt];
-        const float x = ok ? sacc[nt][hf][i] : kNegInf;
+        float x = sacc[nt][hf][i];
+        if (!full) {
+          const int pos = tb + 16 * hf + 4 * g + i;
+          const bool ok = t.half_ok[hf] && pos < k1 && pos <= lim[nt];
+          x = ok ? x : kNegInf;
+        }
         sv[4 * hf + i] = x;
         mx = fmaxf(mx, x);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m_run[nt], mx);
-    const float alpha = (mn == kNegInf) ? 1.f : exp2f(m_run[nt] - mn);
+    // The exponent base m_run moves only when the tile max exceeds it by more
+    // than 8 (weights stay below 2^8), so the accumulators are rescaled rarely.
+    float alpha = 1.f;
+    if (mx > m_run[nt] + 8.f) {
+      const float mn = mx;
+      alpha = (m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - mn);
+      m_run[nt] = mn;
+    }
+    const float mb = m_run[nt];
     float rs = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      p[nt][k] = (sv[k] == kNegInf) ? 0.f : exp2f(sv[k] - mn);
+      p[nt][k] = (sv[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[k] - mb);
       rs += p[nt][k];
     }
     rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
     l_run[nt] = l_run[nt] * alpha + rs;
-    m_run[nt] = mn;
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) o[nt][mt] *= alpha;
@@ -451,42 +502,43 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
     }
   };
 
-  // ---- O^T += V^T P'^T
+  // ---- O^T += V^T P^T.  Quant V: the operand is (c - 8) * d_v (or c * d_v)
+  // split exactly into hi + lo f16 parts; P is split hi + lo once per tile.
   if constexpr (F::kQuant) {
-    const float* vsc = reinterpret_cast<const float*>(wl + F::kVtile);
+    const _Float16* vh = reinterpret_cast<const _Float16*>(wl + F::kVtile);
+    u4 bh[NT], bl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x[8];
+      if constexpr (KT == kQ4_0) {
+        constexpr int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]];
+      } else {
+        constexpr int pi[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]];
+      }
+      make_b(x, bh[nt], bl[nt], false);
+    }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const f4 d0 = *reinterpret_cast<const f4*>(vsc + b * 32 + 4 * g);
-      const f4 d1 = *reinterpret_cast<const f4*>(vsc + b * 32 + 16 + 4 * g);
-      const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-      u4 bh[NT], bl[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float x[8];
-        if constexpr (KT == kQ4_0) {
-          constexpr int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]] * dv[pi[e]];
-        } else {
-          constexpr int pi[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]] * dv[pi[e]];
-        }
-        make_b(x, bh[nt], bl[nt], false);
-      }
+      const u4 dv = *reinterpret_cast<const u4*>(vh + (b * 4 + g) * 8);
       if constexpr (KT == kQ4_0) {
         // source lane n supplies key sigma(g, n % 8), code bytes [8 (n / 8), +8) of block b
         const uint8_t* src = wl + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
         const i2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2*)(src));
-        const u4 a0 = q4_operand(static_cast<uint32_t>(r[0]));
-        const u4 a1 = q4_operand(static_cast<uint32_t>(r[1]));
+        u4 ah[2], al[2];
+        scale_exact(q4_operand<false>(static_cast<uint32_t>(r[0])), dv, ah[0], al[0]);
+        scale_exact(q4_operand<false>(static_cast<uint32_t>(r[1])), dv, ah[1], al[1]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          o[nt][2 * b] = mma(a0, bh[nt], o[nt][2 * b], false);
-          o[nt][2 * b + 1] = mma(a1, bh[nt], o[nt][2 * b + 1], false);
-          if constexpr (C::kParts == 2) {
-            o[nt][2 * b] = mma(a0, bl[nt], o[nt][2 * b], false);
-            o[nt][2 * b + 1] = mma(a1, bl[nt], o[nt][2 * b + 1], false);
+        for (int hm = 0; hm < 2; ++hm) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            f4& acc = o[nt][2 * b + hm];
+            acc = mma(ah[hm], bh[nt], acc, false);
+            acc = mma(al[hm], bh[nt], acc, false);
+            if constexpr (C::kParts == 2) acc = mma(ah[hm], bl[nt], acc, false);
           }
         }
       } else {
@@ -495,11 +547,14 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
           // source lane n supplies key sigma(g, n / 2), code bytes [16 hm + 8 (n % 2), +8)
           const uint8_t* src = wl + sigma(g, n >> 1) * F::kVks + 32 * b + 16 * hm + 8 * (n & 1);
           const i2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(src));
-          const u4 a = q8_operand(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1]));
+          u4 ah, al;
+          scale_exact(q8_operand(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])), dv, ah, al);
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            o[nt][2 * b + hm] = mma(a, bh[nt], o[nt][2 * b + hm], false);
-            if constexpr (C::kParts == 2) o[nt][2 * b + hm] = mma(a, bl[nt], o[nt][2 * b + hm], false);
+            f4& acc = o[nt][2 * b + hm];
+            acc = mma(ah, bh[nt], acc, false);
+            acc = mma(al, bh[nt], acc, false);
+            if constexpr (C::kParts == 2) acc = mma(ah, bl[nt], acc, false);
           }
         }
       }
@@ -604,6 +659,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   QSrc<T> qs;
   qs.base = q_lds;
   int lim[NT];
+  const int lim_min = L - T;                           // the first token's limit: every row sees <= lim_min
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = C::kPack ? (n & 7) : 16 * nt + n;    // query row of this lane's column
@@ -669,14 +725,14 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
       if (ti + 4 < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * (ti + 4), k1, tb2, bad);
-      compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
+      compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
       if (ti >= n_tiles) break;
       stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
       wave_lds_sync();
       if (ti + 4 < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * (ti + 4), k1, ta, bad);
-      compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
+      compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
     }
@@ -686,7 +742,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       load_tile<KT>(p, pm, s, h, k0 + 32 * ti, k1, tt, bad);
       stage_tile<KT>(wl, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
-      compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, qs, o, m_run, l_run);
+      compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
     }
   }

@@ -65,6 +65,18 @@ def test_unscaled_data_scale_one(kind, engine):
 
 
 @pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("mag", [1e-3, 30.0])
+def test_value_magnitudes(kind, mag, engine):
+    # small block scales (f16 products near the subnormal range) and large ones
+    w = synth.make_workload(f"mag_{kind}", [700, 90, 2500], 2, kind, kind, 32, seed=23,
+                            value_scale=mag, q_scale=1.0 / mag, scale=1.0 / 16)
+    log(f"[case] magnitude {mag} {kind} {engine}")
+    out, _, err = run(w, engine=engine)
+    parity(out, _oracle(w)[0], what=f"magnitude {mag} {kind}")
+
+
+@pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("P", [16, 48, 128, 256, 512])
 def test_paged_equals_contiguous_bitwise(P, engine):
     lens = [5 * P + 3, 2 * P, 1, 9 * P - 1]
