@@ -63,7 +63,7 @@ def copy_ceiling(steps=20, nbytes=2 << 30):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_internal.h"):
+    for f in ("pa_mfma.hip", "pa_kernels.hip", "pa_device.h", "pa_internal.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_attention_walk_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

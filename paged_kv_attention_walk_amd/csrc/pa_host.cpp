@@ -19,7 +19,7 @@ namespace {
 
 using pa::BlockAllocator;
 
-constexpr int kTargetPerCu = 4;      // work items per compute unit the chunk plan aims at
+constexpr int kTargetPerCu = 4;      // work items per compute unit the workspace is sized for
 constexpr int kDefaultMaxSeqs = 512;
 constexpr int kDefaultAppendRows = 1024;
 constexpr int kStagingSlots = 2;
@@ -434,8 +434,13 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   prm.bt_stride = bt_stride;
   prm.page_size = page_size;
   prm.n_pool_blocks = block_table ? n_pool_blocks : 0;
-  prm.target_items = target;
-  prm.max_items = static_cast<int32_t>(items);
+  // The plan aims at one round of resident workgroups; the workspace check
+  // above used the larger capacity target, so these items always fit.
+  const int cu = cu_count(device);
+  const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, n_qtok, engine);
+  const int64_t plan = pa::plan_target(n_seq, slots, target);
+  prm.target_items = static_cast<int32_t>(plan);
+  prm.max_items = static_cast<int32_t>(pa::max_work_items(n_seq, plan));
   prm.k_type = kt;
   prm.v_type = vt;
   prm.engine = engine;

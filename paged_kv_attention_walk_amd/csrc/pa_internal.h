@@ -41,7 +41,7 @@ struct DecodeParams {
   float* part_lse;         // [item capacity][24]   (log2 units)
   uint32_t* err;           // error word
   int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
-  int32_t target_items;    // occupancy target of the chunk plan
+  int32_t target_items;    // item target of the chunk plan (plan_target)
   int32_t max_items;       // work items the grid covers
   int32_t k_type, v_type;
   int32_t engine;          // 0: matrix-core path, 1: fp32 vector reference path
@@ -52,6 +52,24 @@ struct DecodeParams {
 inline int64_t max_work_items(int64_t n_seq, int64_t target_items) {
   return target_items + kKvHeads * n_seq;
 }
+
+// Item target of the chunk plan for `slots` co-resident workgroups.  The plan
+// yields at most target + 4 n_seq items, so when the sequences leave room the
+// target fills exactly one round of resident workgroups (no second wave of
+// short-lived workgroups, each paying the set-up again); otherwise half a
+// round of chunks goes on top of the one-item-per-(sequence, head) minimum.
+// Never above `cap`, the target the workspace was sized for.
+inline int64_t plan_target(int64_t n_seq, int64_t slots, int64_t cap) {
+  const int64_t per = kKvHeads * n_seq;
+  int64_t t = (2 * per <= slots) ? slots - per : slots / 2;
+  if (t < 1) t = 1;
+  return t < cap ? t : cap;
+}
+
+// Resident workgroups per compute unit of the split kernel a call selects
+// (from the runtime's occupancy query; at least 1).
+int split_wgs_per_cu(int k_type, int n_qtok, int engine);
+int split_mfma_wgs_per_cu(int k_type, int n_qtok);
 
 struct WorkspaceLayout {
   int64_t items;       // work-item capacity

@@ -291,6 +291,11 @@ hipError_t launch_split_valu(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
+int split_wgs_per_cu(int k_type, int n_qtok, int engine) {
+  if (engine == 1) return 2;     // vector reference path: 256 threads, modest registers
+  return split_mfma_wgs_per_cu(k_type, n_qtok);
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.n_seq <= 0) return hipSuccess;
   if (p.k_type != p.v_type) return hipErrorInvalidValue;

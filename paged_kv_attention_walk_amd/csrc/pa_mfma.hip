@@ -171,120 +171,160 @@ __device__ inline void scale_exact(const u4 a, const u4 d, u4& hi, u4& lo) {
   lo.w = residual_h2(a.w, d.w, hi.w);
 }
 
-// Registers of one tile: K operands (per half, per block), K scales, raw V.
-template <int KT>
-struct Tile {
-  static constexpr int kKw = (KT == kQ4_0) ? 1 : (KT == kQ8_0) ? 2 : 4;   // dwords of K per block per lane
-  static constexpr int kVw = (KT == kQ4_0) ? 9 : (KT == kQ8_0) ? 17 : 32; // dwords of V per lane per half
-  uint32_t k[2][8][kKw];
-  uint32_t ks[2];
-  uint32_t v[2][kVw];
-  bool half_ok[2];
+// ------------------------------------------------------------ tile loads
+//
+// A tile is 32 positions of one (sequence, KV head): two 16-position groups
+// ("halves"), each inside one page since page sizes are multiples of 16.
+// Where a half's rows live is wave-uniform: its block-table entry is read
+// with a scalar load and the row address stays in scalar registers, so a
+// lane's load address is that base plus a fixed per-lane offset.  The loads
+// land in raw registers that nothing reads until the tile is staged or
+// computed, so the next tile's loads stay in flight while the current one is
+// computed.  A half past the chunk end, or whose table entry lies outside the
+// pool, re-reads an in-bounds group and is masked.
+
+struct Half {
+  size_t row;   // first row of the group (pool or contiguous storage)
+  bool live;    // inside the chunk, with a valid table entry
 };
 
-// Loads tile registers.  lane = (m, g) for K, (j, seg) for V.  Halves past
-// the chunk end are not read.  Sets bad on an out-of-range table entry.
-// Physical pages of the chunk's logical pages [lp0, lp0 + n): staged in LDS
-// once per workgroup, so the tile loop never waits on a dependent table load.
-typedef __attribute__((address_space(3))) const int lds_int;
-
-struct PageMap {
-  lds_int* tbl;     // LDS copy (typed as LDS, so reading it never waits on global loads)
-  bool in_lds;      // false: read the table in memory
-  int lp0;
-};
-
-// Row index of the first row of the 16-position group starting at pos0
-// (a multiple of 16, so the group lies inside one page).  ok = false for a
-// table entry outside the pool (row 0 is returned, which is in bounds).
-__device__ inline size_t group_row(const DecodeParams& p, const PageMap& pm, int s, int h, int pos0, bool& ok) {
+// Locates the 16-position group at pos0 (all arguments wave-uniform).  `bad`
+// is set for a group inside the chunk whose table entry is outside the pool.
+__device__ inline Half locate(const DecodeParams& p, int s, int h, int pos0, int k0, int k1, bool& bad) {
+  const bool in = pos0 < k1;
+  const int pos = in ? pos0 : k0;
+  Half r;
   if (p.bt == nullptr) {
-    ok = true;
     const size_t cap = static_cast<size_t>(p.bt_stride) * p.page_size;
-    return (static_cast<size_t>(s) * kKvHeads + h) * cap + pos0;
+    r.row = (static_cast<size_t>(s) * kKvHeads + h) * cap + pos;
+    r.live = in;
+    return r;
   }
-  const int lp = pos0 / p.page_size;
-  int phys;
-  if (pm.in_lds) phys = pm.tbl[lp - pm.lp0];
-  else phys = p.bt[static_cast<size_t>(s) * p.bt_stride + lp];
-  ok = static_cast<unsigned>(phys) < static_cast<unsigned>(p.n_pool_blocks);
-  if (!ok) return 0;
-  return (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + (pos0 - lp * p.page_size);
+  const int lp = pos / p.page_size;
+  // read through the constant address space: a scalar load, waited on with
+  // the scalar / LDS counter, never behind the tile loads in flight
+  const int phys = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(p.bt))[static_cast<size_t>(s) * p.bt_stride + lp];
+  const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(p.n_pool_blocks);
+  if (in && !ok) bad = true;
+  r.row = ok ? (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + (pos - lp * p.page_size) : 0;
+  r.live = in && ok;
+  return r;
 }
 
+// Raw registers of one tile.  K: lane (m, g) holds the code bytes of dims
+// 8g..8g+7 of every block of key m, as aligned dwords (blocks that start
+// 2 bytes off a dword boundary take one dword more and are funnel-shifted
+// when used); K scales: the dwords holding the scales of blocks 2g and 2g+1;
+// V: lane (j, seg) holds bytes [seg * 4 kVw, +4 kVw) of row j.
 template <int KT>
-__device__ inline void load_tile(const DecodeParams& p, const PageMap& pm, int s, int h, int tb, int k1, Tile<KT>& t,
-                                 bool& bad) {
+struct Tile {
+  static constexpr int kKr = (KT == kQ4_0) ? 12 : (KT == kQ8_0) ? 20 : 32;   // raw K dwords per half
+  static constexpr int kVw = (KT == kQ4_0) ? 9 : (KT == kQ8_0) ? 17 : 32;    // raw V dwords per half
+  uint32_t k[2][kKr];
+  uint32_t ks[2][2];
+  uint32_t v[2][kVw];
+  bool live[2];
+};
+
+// First raw K dword of block b.
+template <int KT>
+__device__ constexpr int kraw(int b) {
+  if constexpr (KT == kQ4_0) return 3 * (b >> 1) + ((b & 1) ? 2 : 0);
+  else if constexpr (KT == kQ8_0) return 5 * (b >> 1) + ((b & 1) ? 3 : 0);
+  else return 4 * b;
+}
+
+__device__ inline uint32_t ld32(const uint8_t* base, uint32_t off) {
+  return *reinterpret_cast<const uint32_t*>(base + off);
+}
+__device__ inline u2a ld64(const uint8_t* base, uint32_t off) { return *reinterpret_cast<const u2a*>(base + off); }
+__device__ inline u4a ld128(const uint8_t* base, uint32_t off) { return *reinterpret_cast<const u4a*>(base + off); }
+
+// Issues the loads of the tile at tb.  Only loads: no instruction here reads
+// a loaded register.
+template <int KT>
+__device__ inline void load_tile(const DecodeParams& p, int s, int h, int tb, int k0, int k1, Tile<KT>& t, bool& bad) {
   using F = Fmt<KT>;
   const int lane = threadIdx.x & 63;
-  const int m = lane & 15, g = lane >> 4;
-  const int j = lane >> 2, seg = lane & 3;
+  const uint32_t m = lane & 15, g = lane >> 4;
+  const uint32_t j = lane >> 2, seg = lane & 3;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const int pos0 = tb + 16 * hf;
-    t.half_ok[hf] = false;
-    if (pos0 < k1) {
-      bool ok;
-      const size_t r0 = group_row(p, pm, s, h, pos0, ok);
-      if (!ok) bad = true;
-      t.half_ok[hf] = ok;
-      if (ok) {
-        const uint8_t* rk = p.k + (r0 + m) * F::kRow;
-        if constexpr (KT == kF16 || KT == kBF16) {
+    const Half hv = locate(p, s, h, tb + 16 * hf, k0, k1, bad);
+    t.live[hf] = hv.live;
+    const uint8_t* rk = p.k + hv.row * F::kRow;
+    const uint8_t* rv = p.v + hv.row * F::kRow;
+    if constexpr (KT == kF16 || KT == kBF16) {
+      const uint32_t o = m * F::kRow + 16 * g;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const u4 x = *reinterpret_cast<const u4*>(rk + 64 * b + 16 * g);
-            t.k[hf][b][0] = x[0]; t.k[hf][b][1] = x[1]; t.k[hf][b][2] = x[2]; t.k[hf][b][3] = x[3];
-          }
-        } else if constexpr (KT == kQ8_0) {
+      for (int b = 0; b < 8; ++b) {
+        const u4a x = ld128(rk, o + 64 * b);
+        t.k[hf][4 * b] = x[0]; t.k[hf][4 * b + 1] = x[1]; t.k[hf][4 * b + 2] = x[2]; t.k[hf][4 * b + 3] = x[3];
+      }
+    } else if constexpr (KT == kQ8_0) {
+      const uint32_t o = m * F::kRow + 8 * g;
 #pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const int off = 34 * b + 2 + 8 * g;
-            if (b & 1) {
-              const u2a x = *reinterpret_cast<const u2a*>(rk + off);
-              t.k[hf][b][0] = x[0]; t.k[hf][b][1] = x[1];
-            } else {
-              const u2a x = *reinterpret_cast<const u2a*>(rk + off - 2);
-              const uint32_t x2 = *reinterpret_cast<const uint32_t*>(rk + off + 6);
-              t.k[hf][b][0] = funnel16(x[0], x[1]);
-              t.k[hf][b][1] = funnel16(x[1], x2);
-            }
-          }
-          t.ks[hf] = (*reinterpret_cast<const uint32_t*>(rk + 68 * g) & 0xFFFFu) |
-                     (*reinterpret_cast<const uint32_t*>(rk + 68 * g + 32) & 0xFFFF0000u);
-        } else {
-#pragma unroll
-          for (int b = 0; b < 8; ++b) {
-            const int off = 18 * b + 2 + 4 * g;
-            if (b & 1) {
-              t.k[hf][b][0] = *reinterpret_cast<const uint32_t*>(rk + off);
-            } else {
-              const u2a x = *reinterpret_cast<const u2a*>(rk + off - 2);
-              t.k[hf][b][0] = funnel16(x[0], x[1]);
-            }
-          }
-          t.ks[hf] = (*reinterpret_cast<const uint32_t*>(rk + 36 * g) & 0xFFFFu) |
-                     (*reinterpret_cast<const uint32_t*>(rk + 36 * g + 16) & 0xFFFF0000u);
-        }
-        const uint8_t* rv = p.v + (r0 + j) * F::kRow;
-        if constexpr (KT == kF16 || KT == kBF16) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const u4 x = *reinterpret_cast<const u4*>(rv + 128 * seg + 16 * i);
-            t.v[hf][4 * i] = x[0]; t.v[hf][4 * i + 1] = x[1]; t.v[hf][4 * i + 2] = x[2]; t.v[hf][4 * i + 3] = x[3];
-          }
-        } else {
-          constexpr int W = Tile<KT>::kVw;
-          const uint8_t* src = rv + (W * 4) * seg;
-#pragma unroll
-          for (int i = 0; i + 4 <= W; i += 4) {
-            const u4a x = *reinterpret_cast<const u4a*>(src + 4 * i);
-            t.v[hf][i] = x[0]; t.v[hf][i + 1] = x[1]; t.v[hf][i + 2] = x[2]; t.v[hf][i + 3] = x[3];
-          }
-          t.v[hf][W - 1] = *reinterpret_cast<const uint32_t*>(src + 4 * (W - 1));
+      for (int b = 0; b < 8; ++b) {
+        const int i = kraw<KT>(b);
+        if (b & 1) {                        // codes start on a dword boundary
+          const u2a x = ld64(rk, o + 34 * b + 2);
+          t.k[hf][i] = x[0]; t.k[hf][i + 1] = x[1];
+        } else {                            // 2 bytes off: three dwords around them
+          const u2a x = ld64(rk, o + 34 * b);
+          t.k[hf][i] = x[0]; t.k[hf][i + 1] = x[1];
+          t.k[hf][i + 2] = ld32(rk, o + 34 * b + 8);
         }
       }
+      t.ks[hf][0] = ld32(rk, m * F::kRow + 68 * g);
+      t.ks[hf][1] = ld32(rk, m * F::kRow + 68 * g + 32);
+    } else {
+      const uint32_t o = m * F::kRow + 4 * g;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int i = kraw<KT>(b);
+        if (b & 1) {
+          t.k[hf][i] = ld32(rk, o + 18 * b + 2);
+        } else {
+          const u2a x = ld64(rk, o + 18 * b);
+          t.k[hf][i] = x[0]; t.k[hf][i + 1] = x[1];
+        }
+      }
+      t.ks[hf][0] = ld32(rk, m * F::kRow + 36 * g);
+      t.ks[hf][1] = ld32(rk, m * F::kRow + 36 * g + 16);
     }
+    if constexpr (KT == kF16 || KT == kBF16) {
+      const uint32_t o = j * F::kRow + 128 * seg;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u4a x = ld128(rv, o + 16 * i);
+        t.v[hf][4 * i] = x[0]; t.v[hf][4 * i + 1] = x[1]; t.v[hf][4 * i + 2] = x[2]; t.v[hf][4 * i + 3] = x[3];
+      }
+    } else {
+      constexpr int W = Tile<KT>::kVw;
+      const uint32_t o = j * F::kRow + (W * 4) * seg;
+#pragma unroll
+      for (int i = 0; i + 4 <= W; i += 4) {
+        const u4a x = ld128(rv, o + 4 * i);
+        t.v[hf][i] = x[0]; t.v[hf][i + 1] = x[1]; t.v[hf][i + 2] = x[2]; t.v[hf][i + 3] = x[3];
+      }
+      t.v[hf][W - 1] = ld32(rv, o + 4 * (W - 1));
+    }
+  }
+}
+
+// K operand of block b of half hf: 8 dims of one key as f16 (codes exact).
+template <int KT>
+__device__ inline u4 k_operand(const Tile<KT>& t, int hf, int b) {
+  const int i = kraw<KT>(b);
+  if constexpr (KT == kQ4_0) {
+    const uint32_t x = (b & 1) ? t.k[hf][i] : funnel16(t.k[hf][i], t.k[hf][i + 1]);
+    return q4_operand<true>(x);
+  } else if constexpr (KT == kQ8_0) {
+    if (b & 1) return q8_operand(t.k[hf][i], t.k[hf][i + 1]);
+    return q8_operand(funnel16(t.k[hf][i], t.k[hf][i + 1]), funnel16(t.k[hf][i + 1], t.k[hf][i + 2]));
+  } else {
+    return u4{t.k[hf][i], t.k[hf][i + 1], t.k[hf][i + 2], t.k[hf][i + 3]};
   }
 }
 
@@ -299,7 +339,7 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const int key = 16 * hf + j;
-    const bool valid = t.half_ok[hf] && (tb + key < k1);
+    const bool valid = t.live[hf] && (tb + key < k1);
     if constexpr (KT == kF16 || KT == kBF16) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -352,8 +392,8 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
         vh[((2 * seg + 1) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sb);
       }
       // K scales: lane (m, g) holds blocks 2g, 2g+1 of key m of this half
-      float ka = half_bits(t.ks[hf] & 0xFFFFu), kb = half_bits(t.ks[hf] >> 16);
-      if (!t.half_ok[hf]) ka = kb = 0.f;
+      float ka = half_bits(t.ks[hf][0] & 0xFFFFu), kb = half_bits(t.ks[hf][1] >> 16);
+      if (!t.live[hf]) ka = kb = 0.f;
       ksc[(hf * 8 + 2 * g) * 16 + m] = ka;
       ksc[(hf * 8 + 2 * g + 1) * 16 + m] = kb;
     }
@@ -376,20 +416,14 @@ struct Cols {
   static constexpr int kParts = kPack ? 1 : 2;          // hi / lo in separate MFMAs
 };
 
-// Source of the QK^T B operands: registers for one token; for more tokens an
-// LDS copy laid out per (tile, part, block) as 64 lanes x 16 bytes, so each
-// operand is one conflict-free 16-byte read per lane.
+// Source of the QK^T B operands: an LDS copy laid out per (tile, part,
+// block) as 64 lanes x 16 bytes, so each operand is one conflict-free
+// 16-byte read per lane.
 template <int T>
 struct QSrc {
-  static constexpr bool kRegs = Cols<T>::kPack;
-  u4 q[kRegs ? 8 : 1];
   const uint8_t* base;
   __device__ inline u4 get(int nt, int part, int b) const {
-    if constexpr (kRegs) {
-      return q[b];
-    } else {
-      return *reinterpret_cast<const u4*>(base + ((nt * 2 + part) * 8 + b) * 1024 + (threadIdx.x & 63) * 16);
-    }
+    return *reinterpret_cast<const u4*>(base + ((nt * 2 + part) * 8 + b) * 1024 + (threadIdx.x & 63) * 16);
   }
 };
 
@@ -411,28 +445,32 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
   // ---- S^T = K Q^T (lane (n, g) gets rows 4g..4g+3 = keys of each half, column n)
   f4 sacc[NT][2];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sacc[nt][hf] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      u4 a;
-      if constexpr (KT == kQ4_0) a = q4_operand<true>(t.k[hf][b][0]);
-      else if constexpr (KT == kQ8_0) a = q8_operand(t.k[hf][b][0], t.k[hf][b][1]);
-      else a = u4{t.k[hf][b][0], t.k[hf][b][1], t.k[hf][b][2], t.k[hf][b][3]};
+  for (int b = 0; b < 8; ++b) {
+    u4 qb[NT][C::kParts];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const u4 a = k_operand<KT>(t, hf, b);
       if constexpr (F::kQuant) {
         const f4 dk = *reinterpret_cast<const f4*>(wl + F::kVtile + 1024 + ((hf * 8 + b) * 16 + 4 * g) * 4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          f4 cb = mma(a, qs.get(nt, 0, b), f4{0.f, 0.f, 0.f, 0.f}, false);
-          if constexpr (C::kParts == 2) cb = mma(a, qs.get(nt, 1, b), cb, false);
+          f4 cb = mma(a, qb[nt][0], f4{0.f, 0.f, 0.f, 0.f}, false);
+          if constexpr (C::kParts == 2) cb = mma(a, qb[nt][1], cb, false);
           sacc[nt][hf] += dk * cb;       // per-key block scale on the exact-code product
         }
       } else {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          sacc[nt][hf] = mma(a, qs.get(nt, 0, b), sacc[nt][hf], BF);
-          if constexpr (C::kParts == 2) sacc[nt][hf] = mma(a, qs.get(nt, 1, b), sacc[nt][hf], BF);
+          sacc[nt][hf] = mma(a, qb[nt][0], sacc[nt][hf], BF);
+          if constexpr (C::kParts == 2) sacc[nt][hf] = mma(a, qb[nt][1], sacc[nt][hf], BF);
         }
       }
     }
@@ -460,7 +498,7 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
         float x = sacc[nt][hf][i];
         if (!full) {
           const int pos = tb + 16 * hf + 4 * g + i;
-          const bool ok = t.half_ok[hf] && pos < k1 && pos <= lim[nt];
+          const bool ok = t.live[hf] && pos < k1 && pos <= lim[nt];
           x = ok ? x : kNegInf;
         }
         sv[4 * hf + i] = x;
@@ -589,91 +627,25 @@ __device__ inline int out_dim(int mt, int g, int i) {
   return 16 * mt + m;
 }
 
-// Register double-buffering of the next tile pays for the compact quant rows;
-// the 16-bit rows use a single buffer (their loads are large enough that the
-// other waves cover the latency).
-constexpr int kTblCap = 1024;     // table entries staged in LDS per workgroup
-
+// Query operands (B of QK^T): q * scale * log2 e split hi + lo, element
+// order matching the K operand's dim order of each type, written to LDS per
+// (tile, part, block).  One token: lane n < 8 of a column group carries the
+// hi part of row n, lane n + 8 the lo part (one tile, one part).  More
+// tokens: hi and lo in separate parts.  Wave w builds blocks 2w and 2w+1.
 template <int KT, int T>
-constexpr bool kDoubleBuffer = (KT == kQ4_0) || (KT == kQ8_0 && T != 2);
-
-template <int KT, int T>
-__global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(DecodeParams p) {
-  using F = Fmt<KT>;
+__device__ inline void build_q(const DecodeParams& p, int s, int h, int wave, uint8_t* q_lds) {
   using C = Cols<T>;
   constexpr int R = C::R;
-  constexpr int NT = C::NT;
-  constexpr bool BF = F::kBf;
-  constexpr int kRed = 4 * R * kHeadDim * 4;
-  constexpr int kLds = (4 * F::kWave > kRed) ? 4 * F::kWave : kRed;
-  constexpr int kQLds = C::kPack ? 16 : NT * 2 * 8 * 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
-  __shared__ int tbl_lds[kTblCap];
-  __shared__ float ml_lds[4][R][2];
-  __shared__ long long sh_sum[4];
-  __shared__ int sh_loc[2];
-  __shared__ int sh_bad[4];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const int cap = p.bt_stride * p.page_size;
-  const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum);
-  const int jj = blockIdx.x / kKvHeads, h = blockIdx.x % kKvHeads;
-  plan_locate(p.seq_lens, p.n_seq, cap, chunk, jj, sh_loc);
-  const int s = sh_loc[0], c = sh_loc[1];
-  if (s < 0) return;
-  const int L = p.seq_lens[s];
-  const int nc = n_chunks_of(L, cap, chunk);
-  const size_t item = blockIdx.x;
-
-  if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
-    const float nan = __builtin_nanf("");
-    for (int i = tid; i < R * kHeadDim; i += kThreads) {
-      const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, gq = r % 6;
-      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + d] = nan;
-    }
-    if (p.lse_out && tid < R)
-      p.lse_out[(static_cast<size_t>(s) * T + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
-    if (tid == 0) atomicOr(p.err, 2u);
-    return;
-  }
-  const int k0 = c * chunk;
-  const int k1 = min(L, k0 + chunk);
-
-  // ---- the chunk's block-table entries
-  PageMap pm{(lds_int*)(tbl_lds), false, 0};
-  if (p.bt != nullptr && k1 > k0) {
-    pm.lp0 = k0 / p.page_size;
-    const int n_tbl = (k1 - 1) / p.page_size - pm.lp0 + 1;
-    if (n_tbl <= kTblCap) {
-      for (int i = tid; i < n_tbl; i += kThreads) tbl_lds[i] = p.bt[static_cast<size_t>(s) * p.bt_stride + pm.lp0 + i];
-      pm.in_lds = true;
-    }
-  }
-
-  // ---- query operands (B of QK^T): q * scale * log2 e split hi + lo.  The
-  // element order matches the K operand's dim order of each type.  One token:
-  // registers; more: an LDS copy built by the 4 waves (2 blocks each).
-  QSrc<T> qs;
-  qs.base = q_lds;
-  int lim[NT];
-  const int lim_min = L - T;                           // the first token's limit: every row sees <= lim_min
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = C::kPack ? (n & 7) : 16 * nt + n;    // query row of this lane's column
-    lim[nt] = L - T + r / 6;                           // its token sees positions <= lim
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int nt = 0; nt < C::NT; ++nt) {
     const int r = C::kPack ? (n & 7) : 16 * nt + n;
     const bool live = r < R;
     const float* qrow = p.q + ((static_cast<size_t>(s) * T + (live ? r / 6 : 0)) * kQHeads + h * kGroup +
                                (live ? r % 6 : 0)) * kHeadDim;
 #pragma unroll
-    for (int bb = 0; bb < (C::kPack ? 8 : 2); ++bb) {
-      const int b = C::kPack ? bb : 2 * wave + bb;
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * wave + bb;
       float x[8];
       if constexpr (KT == kQ4_0) {
         const float4 lo = *reinterpret_cast<const float4*>(qrow + 32 * b + 4 * g);
@@ -692,16 +664,76 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = live ? x[i] * p.scale_log2 : 0.f;
       u4 hi, lo;
-      split8(x, hi, lo, BF);
+      split8(x, hi, lo, Fmt<KT>::kBf);
       if constexpr (C::kPack) {
-        qs.q[b] = (n & 8) ? lo : hi;
+        *reinterpret_cast<u4*>(q_lds + b * 1024 + lane * 16) = (n & 8) ? lo : hi;
       } else {
         *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 0) * 8 + b) * 1024 + lane * 16) = hi;
         *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 1) * 8 + b) * 1024 + lane * 16) = lo;
       }
     }
   }
-  __syncthreads();                       // table entries (and, for more tokens, query operands)
+}
+
+// Register double-buffering of the next tile pays for the compact quant rows;
+// the 16-bit rows use a single buffer (their loads are large enough that the
+// other waves cover the latency).
+template <int KT, int T>
+constexpr bool kDoubleBuffer = (KT == kQ4_0 && T == 1);
+
+template <int KT, int T>
+__global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(DecodeParams p) {
+  using F = Fmt<KT>;
+  using C = Cols<T>;
+  constexpr int R = C::R;
+  constexpr int NT = C::NT;
+  constexpr int kRed = 4 * R * kHeadDim * 4;
+  constexpr int kLds = (4 * F::kWave > kRed) ? 4 * F::kWave : kRed;
+  constexpr int kQLds = NT * C::kParts * 8 * 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
+  __shared__ float ml_lds[4][R][2];
+  __shared__ long long sh_sum[4];
+  __shared__ int sh_loc[2];
+  __shared__ int sh_bad[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int cap = p.bt_stride * p.page_size;
+  const int chunk = __builtin_amdgcn_readfirstlane(plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum));
+  const int jj = blockIdx.x / kKvHeads, h = blockIdx.x % kKvHeads;
+  plan_locate(p.seq_lens, p.n_seq, cap, chunk, jj, sh_loc);
+  // every value that places loads is wave-uniform (scalar registers)
+  const int s = __builtin_amdgcn_readfirstlane(sh_loc[0]), c = __builtin_amdgcn_readfirstlane(sh_loc[1]);
+  if (s < 0) return;
+  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
+  const int nc = n_chunks_of(L, cap, chunk);
+  const size_t item = blockIdx.x;
+
+  if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
+    const float nan = __builtin_nanf("");
+    for (int i = tid; i < R * kHeadDim; i += kThreads) {
+      const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, gq = r % 6;
+      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + d] = nan;
+    }
+    if (p.lse_out && tid < R)
+      p.lse_out[(static_cast<size_t>(s) * T + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
+    if (tid == 0) atomicOr(p.err, 2u);
+    return;
+  }
+  const int k0 = c * chunk;
+  const int k1 = min(L, k0 + chunk);
+
+  QSrc<T> qs;
+  qs.base = q_lds;
+  int lim[NT];
+  const int lim_min = L - T;                           // the first token's limit: every row sees <= lim_min
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = C::kPack ? (n & 7) : 16 * nt + n;    // query row of this lane's column
+    lim[nt] = L - T + r / 6;                           // its token sees positions <= lim
+  }
 
   f4 o[NT][16];
   float m_run[NT], l_run[NT];
@@ -717,29 +749,34 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   bool bad = false;
   const int n_tiles = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
   if constexpr (kDoubleBuffer<KT, T>) {
-    // the next tile's loads are in flight while the current one is computed
+    // the next tile's loads are in flight while the current one is computed;
+    // the first tile's loads go out before the query operands are built
     Tile<KT> ta, tb2;
     int ti = wave;
-    if (ti < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * ti, k1, ta, bad);
+    if (ti < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * ti, k0, k1, ta, bad);
+    build_q<KT, T>(p, s, h, wave, q_lds);
+    __syncthreads();
     while (ti < n_tiles) {
       stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * (ti + 4), k1, tb2, bad);
+      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
       compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
       if (ti >= n_tiles) break;
       stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, pm, s, h, k0 + 32 * (ti + 4), k1, ta, bad);
+      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
       compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
     }
   } else {
+    build_q<KT, T>(p, s, h, wave, q_lds);
+    __syncthreads();
     for (int ti = wave; ti < n_tiles; ti += 4) {
       Tile<KT> tt;
-      load_tile<KT>(p, pm, s, h, k0 + 32 * ti, k1, tt, bad);
+      load_tile<KT>(p, s, h, k0 + 32 * ti, k0, k1, tt, bad);
       stage_tile<KT>(wl, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
       compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
@@ -831,7 +868,37 @@ hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int KT, int T>
+int wgs_per_cu() {
+  static const int n = [] {
+    int r = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, T>, kThreads, 0) != hipSuccess)
+      r = 1;
+    return r < 1 ? 1 : (r > 4 ? 4 : r);
+  }();
+  return n;
+}
+
+template <int KT>
+int wgs_kt(int T) {
+  switch (T) {
+    case 1: return wgs_per_cu<KT, 1>();
+    case 2: return wgs_per_cu<KT, 2>();
+    case 3: return wgs_per_cu<KT, 3>();
+    default: return wgs_per_cu<KT, 4>();
+  }
+}
+
 }  // namespace
+
+int split_mfma_wgs_per_cu(int k_type, int n_qtok) {
+  switch (k_type) {
+    case kF16: return wgs_kt<kF16>(n_qtok);
+    case kBF16: return wgs_kt<kBF16>(n_qtok);
+    case kQ8_0: return wgs_kt<kQ8_0>(n_qtok);
+    default: return wgs_kt<kQ4_0>(n_qtok);
+  }
+}
 
 hipError_t launch_split_mfma(const DecodeParams& p, hipStream_t stream) {
   switch (p.k_type) {
