@@ -188,9 +188,23 @@ struct Half {
   bool live;    // inside the chunk, with a valid table entry
 };
 
+// Where the chunk's block-table entries are read: an LDS copy of entries
+// [lp0, lp0 + kTblCap) once staged, else the table itself through the
+// constant address space (scalar loads).  Both give wave-uniform values and
+// are waited on with the scalar / LDS counter, never behind tile loads.
+typedef __attribute__((address_space(3))) const int lds_int;
+constexpr int kTblCap = 1024;
+
+struct Pages {
+  lds_int* tbl;
+  int lp0;
+  bool in_lds;
+};
+
 // Locates the 16-position group at pos0 (all arguments wave-uniform).  `bad`
 // is set for a group inside the chunk whose table entry is outside the pool.
-__device__ inline Half locate(const DecodeParams& p, int s, int h, int pos0, int k0, int k1, bool& bad) {
+__device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int h, int pos0, int k0, int k1,
+                              bool& bad) {
   const bool in = pos0 < k1;
   const int pos = in ? pos0 : k0;
   Half r;
@@ -201,10 +215,13 @@ __device__ inline Half locate(const DecodeParams& p, int s, int h, int pos0, int
     return r;
   }
   const int lp = pos / p.page_size;
-  // read through the constant address space: a scalar load, waited on with
-  // the scalar / LDS counter, never behind the tile loads in flight
-  const int phys = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
-      reinterpret_cast<uintptr_t>(p.bt))[static_cast<size_t>(s) * p.bt_stride + lp];
+  int phys;
+  if (pg.in_lds) {
+    phys = __builtin_amdgcn_readfirstlane(pg.tbl[lp - pg.lp0]);
+  } else {
+    phys = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        reinterpret_cast<uintptr_t>(p.bt))[static_cast<size_t>(s) * p.bt_stride + lp];
+  }
   const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(p.n_pool_blocks);
   if (in && !ok) bad = true;
   r.row = ok ? (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + (pos - lp * p.page_size) : 0;
@@ -244,14 +261,15 @@ __device__ inline u4a ld128(const uint8_t* base, uint32_t off) { return *reinter
 // Issues the loads of the tile at tb.  Only loads: no instruction here reads
 // a loaded register.
 template <int KT>
-__device__ inline void load_tile(const DecodeParams& p, int s, int h, int tb, int k0, int k1, Tile<KT>& t, bool& bad) {
+__device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, int h, int tb, int k0, int k1,
+                                 Tile<KT>& t, bool& bad) {
   using F = Fmt<KT>;
   const int lane = threadIdx.x & 63;
   const uint32_t m = lane & 15, g = lane >> 4;
   const uint32_t j = lane >> 2, seg = lane & 3;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const Half hv = locate(p, s, h, tb + 16 * hf, k0, k1, bad);
+    const Half hv = locate(p, pg, s, h, tb + 16 * hf, k0, k1, bad);
     t.live[hf] = hv.live;
     const uint8_t* rk = p.k + hv.row * F::kRow;
     const uint8_t* rv = p.v + hv.row * F::kRow;
@@ -692,6 +710,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
+  __shared__ int tbl_lds[kTblCap];
   __shared__ float ml_lds[4][R][2];
   __shared__ long long sh_sum[4];
   __shared__ int sh_loc[2];
@@ -748,25 +767,38 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   uint8_t* wl = lds + wave * F::kWave;
   bool bad = false;
   const int n_tiles = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
+
+  // The chunk's table entries go to LDS (read there once the barrier below
+  // has passed); the first tile, loaded before it, reads the table itself.
+  Pages pg{(lds_int*)(tbl_lds), 0, false};
+  bool tbl_fits = false;
+  if (p.bt != nullptr && k1 > k0) {
+    pg.lp0 = k0 / p.page_size;
+    const int n_tbl = (k1 - 1) / p.page_size - pg.lp0 + 1;
+    tbl_fits = n_tbl <= kTblCap;
+    if (tbl_fits)
+      for (int i = tid; i < n_tbl; i += kThreads) tbl_lds[i] = p.bt[static_cast<size_t>(s) * p.bt_stride + pg.lp0 + i];
+  }
   if constexpr (kDoubleBuffer<KT, T>) {
     // the next tile's loads are in flight while the current one is computed;
     // the first tile's loads go out before the query operands are built
     Tile<KT> ta, tb2;
     int ti = wave;
-    if (ti < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * ti, k0, k1, ta, bad);
+    if (ti < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
+    pg.in_lds = tbl_fits;
     while (ti < n_tiles) {
       stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+      if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
       compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
       if (ti >= n_tiles) break;
       stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
+      if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
       compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
@@ -774,9 +806,10 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   } else {
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
+    pg.in_lds = tbl_fits;
     for (int ti = wave; ti < n_tiles; ti += 4) {
       Tile<KT> tt;
-      load_tile<KT>(p, s, h, k0 + 32 * ti, k0, k1, tt, bad);
+      load_tile<KT>(p, pg, s, h, k0 + 32 * ti, k0, k1, tt, bad);
       stage_tile<KT>(wl, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
       compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
