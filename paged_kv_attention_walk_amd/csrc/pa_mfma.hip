@@ -116,9 +116,20 @@ __device__ inline uint32_t nib2h(uint32_t x, uint32_t mask, float sub) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// (x & 0x00F000F0) | 0x64006400 read as two f16 (1024 + 16 field), times
+// 1/16 minus 72: the field minus 8, exactly (one fused multiply-add).
+__device__ inline uint32_t nib2h_hi(uint32_t x) {
+  const uint32_t u = bfi(0x00F000F0u, x, 0x64006400u);
+  const h2 v = __builtin_bit_cast(h2, u);
+  const h2 k = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const h2 c = {static_cast<_Float16>(-72.f), static_cast<_Float16>(-72.f)};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v, k, c));
+}
+
 // 8 nibbles (bits 4k, k = 0..7) -> f16 operand c - 8, element order
 // k = 0,4,1,5,2,6,3,7.  With X16, elements of odd k hold 16 (c - 8) instead
-// (one shift fewer; the partner operand then carries 1/16).
+// (the partner operand then carries 1/16); without, they are brought down
+// by a fused multiply-add.  No shift for odd k either way.
 template <bool X16>
 __device__ inline u4 q4_operand(uint32_t x) {
   const uint32_t y = x >> 8;
@@ -129,8 +140,8 @@ __device__ inline u4 q4_operand(uint32_t x) {
     a[1] = nib2h(x, 0x00F000F0u, 1152.f);                     // k = 1, 5: 16 (c - 8)
     a[3] = nib2h(y, 0x00F000F0u, 1152.f);                     // k = 3, 7
   } else {
-    a[1] = nib2h(x >> 4, 0x000F000Fu, 1032.f);                // k = 1, 5
-    a[3] = nib2h(y >> 4, 0x000F000Fu, 1032.f);                // k = 3, 7
+    a[1] = nib2h_hi(x);                                       // k = 1, 5
+    a[3] = nib2h_hi(y);                                       // k = 3, 7
   }
   return a;
 }
@@ -147,6 +158,35 @@ __device__ inline u4 q8_operand(uint32_t x0, uint32_t x1) {
 }
 
 __device__ inline uint32_t funnel16(uint32_t lo, uint32_t hi) { return (lo >> 16) | (hi << 16); }
+
+// Cross-lane butterflies without LDS.  The value of lane l ^ 8 (inside each
+// 16-lane row: a rotation by 8), and x op x' for the partner l ^ 16 or
+// l ^ 32 from the gfx950 row / half swaps: the two swapped copies hold own
+// and partner values in some order, and op is commutative, so every lane of
+// a pair gets the same result.
+__device__ inline float lane_xor8(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+__device__ inline float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, static_cast<unsigned>(r[0])) + __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, static_cast<unsigned>(r[0])) + __builtin_bit_cast(float, static_cast<unsigned>(r[1]));
+}
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(r[0])), __builtin_bit_cast(float, static_cast<unsigned>(r[1])));
+}
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, static_cast<unsigned>(r[0])), __builtin_bit_cast(float, static_cast<unsigned>(r[1])));
+}
 
 // a * d as hi + lo f16 pairs, exactly: a holds small integers (codes) and d
 // fp16 scales, so the product has at most 19 significant bits; hi is its f16
@@ -497,7 +537,7 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[0][hf][i] += __shfl_xor(sacc[0][hf][i], 8, 64);
+      for (int i = 0; i < 4; ++i) sacc[0][hf][i] += lane_xor8(sacc[0][hf][i]);
   }
 
   // ---- online softmax (base 2); p[nt][k] is the weight of key sigma(g, k).
@@ -509,22 +549,20 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
   for (int nt = 0; nt < NT; ++nt) {
     float sv[8];
     float mx = kNegInf;
+    // key 16 hf + 4 g + i is visible iff 16 hf + i <= rel
+    const int rel = min(k1 - 1, lim[nt]) - (tb + 4 * g);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = sacc[nt][hf][i];
-        if (!full) {
-          const int pos = tb + 16 * hf + 4 * g + i;
-          const bool ok = t.live[hf] && pos < k1 && pos <= lim[nt];
-          x = ok ? x : kNegInf;
-        }
+        if (!full) x = (t.live[hf] && 16 * hf + i <= rel) ? x : kNegInf;
         sv[4 * hf + i] = x;
         mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
     // The exponent base m_run moves only when the tile max exceeds it by more
     // than 8 (weights stay below 2^8), so the accumulators are rescaled rarely.
     float alpha = 1.f;
@@ -540,8 +578,8 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       p[nt][k] = (sv[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[k] - mb);
       rs += p[nt][k];
     }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
+    rs = sum_xor16(rs);
+    rs = sum_xor32(rs);
     l_run[nt] = l_run[nt] * alpha + rs;
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
