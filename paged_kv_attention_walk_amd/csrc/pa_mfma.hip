@@ -64,7 +64,15 @@ struct Fmt {
   // so that keys 4 apart fall in different banks.
   static constexpr int kVks = kQuant ? 8 * kCodes + 16 : 512 + 16;
   static constexpr int kVtile = 32 * kVks;                                     // 32 keys
-  static constexpr int kWave = kVtile + (kQuant ? 2048 : 0);                   // + V and K scales (f32)
+  // Q4_0 K rows are fetched as contiguous 16-byte pieces and kept raw in LDS
+  // (the operands are read there); other types load K in operand layout.
+  static constexpr bool kKStage = (KT == kQ4_0);
+  static constexpr int kKraw = kKStage ? 32 * kRow : 0;
+  // Per wave: V codes; then (quant) V scales (f16, 512 B), the key bias
+  // (f32 [2][16]: 0 for a visible key, -inf past the chunk end or for a dead
+  // half), K scales (f32 [2][8][16] at +1024); then raw K rows.
+  static constexpr int kBias = kVtile + 512;
+  static constexpr int kWave = kVtile + (kQuant ? 2048 : 0) + kKraw;
 };
 
 __device__ inline f4 mma(u4 a, u4 b, f4 c, bool bf) {
@@ -276,13 +284,22 @@ __device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int
 // V: lane (j, seg) holds bytes [seg * 4 kVw, +4 kVw) of row j.
 template <int KT>
 struct Tile {
-  static constexpr int kKr = (KT == kQ4_0) ? 12 : (KT == kQ8_0) ? 20 : 32;   // raw K dwords per half
+  // raw K dwords per half (Q4_0: both halves as 5 16-byte pieces in kp)
+  static constexpr int kKr = (KT == kQ4_0) ? 1 : (KT == kQ8_0) ? 20 : 32;
+  static constexpr int kKp = (KT == kQ4_0) ? 20 : 1;
   static constexpr int kVw = (KT == kQ4_0) ? 9 : (KT == kQ8_0) ? 17 : 32;    // raw V dwords per half
   uint32_t k[2][kKr];
+  uint32_t kp[kKp];
   uint32_t ks[2][2];
   uint32_t v[2][kVw];
   bool live[2];
 };
+
+// Q4_0 K: the two 16-row groups (2 x 2304 bytes) as 288 16-byte pieces;
+// piece e = 64 i + lane of load i is byte 16 e' of group e >= 144 (e' the
+// index inside its group).  Lanes past piece 287 re-read a piece of group 1.
+__device__ inline int kpiece_group(int e) { return e >= 144 ? 1 : 0; }
+__device__ inline uint32_t kpiece_off(int e) { return 16u * static_cast<uint32_t>(e >= 288 ? e - 288 : e >= 144 ? e - 144 : e); }
 
 // First raw K dword of block b.
 template <int KT>
@@ -307,13 +324,17 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
   const int lane = threadIdx.x & 63;
   const uint32_t m = lane & 15, g = lane >> 4;
   const uint32_t j = lane >> 2, seg = lane & 3;
+  const uint8_t* rk_half[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const Half hv = locate(p, pg, s, h, tb + 16 * hf, k0, k1, bad);
     t.live[hf] = hv.live;
     const uint8_t* rk = p.k + hv.row * F::kRow;
     const uint8_t* rv = p.v + hv.row * F::kRow;
-    if constexpr (KT == kF16 || KT == kBF16) {
+    rk_half[hf] = rk;
+    if constexpr (F::kKStage) {
+      // K of both halves is loaded below as contiguous pieces
+    } else if constexpr (KT == kF16 || KT == kBF16) {
       const uint32_t o = m * F::kRow + 16 * g;
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
@@ -336,20 +357,6 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
       }
       t.ks[hf][0] = ld32(rk, m * F::kRow + 68 * g);
       t.ks[hf][1] = ld32(rk, m * F::kRow + 68 * g + 32);
-    } else {
-      const uint32_t o = m * F::kRow + 4 * g;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int i = kraw<KT>(b);
-        if (b & 1) {
-          t.k[hf][i] = ld32(rk, o + 18 * b + 2);
-        } else {
-          const u2a x = ld64(rk, o + 18 * b);
-          t.k[hf][i] = x[0]; t.k[hf][i + 1] = x[1];
-        }
-      }
-      t.ks[hf][0] = ld32(rk, m * F::kRow + 36 * g);
-      t.ks[hf][1] = ld32(rk, m * F::kRow + 36 * g + 16);
     }
     if constexpr (KT == kF16 || KT == kBF16) {
       const uint32_t o = j * F::kRow + 128 * seg;
@@ -369,14 +376,34 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
       t.v[hf][W - 1] = ld32(rv, o + 4 * (W - 1));
     }
   }
+  if constexpr (F::kKStage) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int e = 64 * i + lane;
+      const u4a x = ld128(kpiece_group(e) ? rk_half[1] : rk_half[0], kpiece_off(e));
+      t.kp[4 * i] = x[0]; t.kp[4 * i + 1] = x[1]; t.kp[4 * i + 2] = x[2]; t.kp[4 * i + 3] = x[3];
+    }
+  }
 }
 
 // K operand of block b of half hf: 8 dims of one key as f16 (codes exact).
 template <int KT>
-__device__ inline u4 k_operand(const Tile<KT>& t, int hf, int b) {
+__device__ inline u4 k_operand(const Tile<KT>& t, const uint8_t* wl, int hf, int b) {
   const int i = kraw<KT>(b);
   if constexpr (KT == kQ4_0) {
-    const uint32_t x = (b & 1) ? t.k[hf][i] : funnel16(t.k[hf][i], t.k[hf][i + 1]);
+    // raw row 16 hf + m in LDS: the 4 code bytes of dims 8g..8g+7 of block b
+    // (2 bytes off a dword boundary for even b: two aligned dwords, shifted)
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    const uint8_t* r = wl + Fmt<KT>::kVtile + 2048 + (16 * hf + m) * Fmt<KT>::kRow + 18 * b + 4 * g;
+    uint32_t x;
+    if (b & 1) {
+      x = *reinterpret_cast<const uint32_t*>(r + 2);
+    } else {
+      const uint32_t lo = *reinterpret_cast<const uint32_t*>(r), hi = *reinterpret_cast<const uint32_t*>(r + 4);
+      x = funnel16(lo, hi);
+    }
+    (void)i;
+    (void)t;
     return q4_operand<true>(x);
   } else if constexpr (KT == kQ8_0) {
     if (b & 1) return q8_operand(t.k[hf][i], t.k[hf][i + 1]);
@@ -449,12 +476,42 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
         vh[((2 * seg) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sa);        // fp16 bits as stored
         vh[((2 * seg + 1) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sb);
       }
-      // K scales: lane (m, g) holds blocks 2g, 2g+1 of key m of this half
-      float ka = half_bits(t.ks[hf][0] & 0xFFFFu), kb = half_bits(t.ks[hf][1] >> 16);
-      if (!t.live[hf]) ka = kb = 0.f;
-      ksc[(hf * 8 + 2 * g) * 16 + m] = ka;
-      ksc[(hf * 8 + 2 * g + 1) * 16 + m] = kb;
+      if constexpr (!F::kKStage) {
+        // K scales: lane (m, g) holds blocks 2g, 2g+1 of key m of this half;
+        // zero for keys that are not visible, so their codes give 0, not NaN
+        float ka = half_bits(t.ks[hf][0] & 0xFFFFu), kb = half_bits(t.ks[hf][1] >> 16);
+        if (!t.live[hf] || tb + 16 * hf + m >= k1) ka = kb = 0.f;
+        ksc[(hf * 8 + 2 * g) * 16 + m] = ka;
+        ksc[(hf * 8 + 2 * g + 1) * 16 + m] = kb;
+      }
+      if (seg == 0) {
+        float* bias = reinterpret_cast<float*>(w + F::kBias);
+        bias[hf * 16 + j] = valid ? 0.f : kNegInf;
+      }
     }
+  }
+  if constexpr (F::kKStage) {
+    // raw K rows of both halves: piece e at byte 16 e
+    uint8_t* kr = w + F::kVtile + 2048;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int e = 64 * i + lane;
+      if (e < 288) *reinterpret_cast<u4*>(kr + 16 * e) = u4{t.kp[4 * i], t.kp[4 * i + 1], t.kp[4 * i + 2], t.kp[4 * i + 3]};
+    }
+    wave_lds_sync();
+    // K scales as f32 [half][block][16 keys]: lane l writes keys 4 (l % 4) ..
+    // +3 of block (l / 4) % 8 of half l / 32
+    const int hf = lane >> 5, b = (lane >> 2) & 7, m0 = 4 * (lane & 3);
+    f4 d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d[i] = half_bits(*reinterpret_cast<const uint16_t*>(kr + (16 * hf + m0 + i) * F::kRow + 18 * b));
+    // zero for keys that are not visible (a select on live: t stays in registers)
+    const bool lv = hf ? t.live[1] : t.live[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!lv || tb + 16 * hf + m0 + i >= k1) d[i] = 0.f;
+    *reinterpret_cast<f4*>(w + F::kVtile + 1024 + ((hf * 8 + b) * 16 + m0) * 4) = d;
   }
 }
 
@@ -501,11 +558,17 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
   const bool lo_lane = (n & 8) != 0;      // packed case: this lane carries lo parts
 
   // ---- S^T = K Q^T (lane (n, g) gets rows 4g..4g+3 = keys of each half, column n)
+  // Quant K: the accumulators start at the key bias (-inf for keys that are
+  // not visible; their zeroed scales keep the products finite), so no
+  // per-value mask is needed for the chunk end.
   f4 sacc[NT][2];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+  for (int hf = 0; hf < 2; ++hf) {
+    f4 init = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (F::kQuant) init = *reinterpret_cast<const f4*>(wl + F::kBias + (hf * 16 + 4 * g) * 4);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sacc[nt][hf] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) sacc[nt][hf] = init;
+  }
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     u4 qb[NT][C::kParts];
@@ -515,7 +578,7 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const u4 a = k_operand<KT>(t, hf, b);
+      const u4 a = k_operand<KT>(t, wl, hf, b);
       if constexpr (F::kQuant) {
         const f4 dk = *reinterpret_cast<const f4*>(wl + F::kVtile + 1024 + ((hf * 8 + b) * 16 + 4 * g) * 4);
 #pragma unroll
@@ -543,7 +606,9 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
   // ---- online softmax (base 2); p[nt][k] is the weight of key sigma(g, k).
   // Masking is needed only where the tile crosses the chunk end or, for
   // more than one token, the causal limit of some row (uniform test).
-  const bool full = (tb + 32 <= k1) && (tb + 31 <= lim_min);
+  // Quant K needs a mask only where the causal limit of some row (more than
+  // one token) falls inside the tile; other types also at the chunk end.
+  const bool full = (F::kQuant || tb + 32 <= k1) && (T == 1 || tb + 31 <= lim_min);
   float p[NT][8];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -571,11 +636,13 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       alpha = (m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - mn);
       m_run[nt] = mn;
     }
-    const float mb = m_run[nt];
+    // exp2(-inf) is 0; only an all-masked history (base still -inf) needs a
+    // finite stand-in base
+    const float mb = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
     float rs = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      p[nt][k] = (sv[k] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(sv[k] - mb);
+      p[nt][k] = __builtin_amdgcn_exp2f(sv[k] - mb);
       rs += p[nt][k];
     }
     rs = sum_xor16(rs);
