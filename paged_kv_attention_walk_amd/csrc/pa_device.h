@@ -308,6 +308,7 @@ __device__ inline float block_sum_f(float v, float* sh) {
 template <int T>
 __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   constexpr int R = 6 * T;
+  constexpr int kEarly = 8;                              // chunk outputs per lane fetched before the weights
   const int row_id = blockIdx.x;
   const int r = row_id % R;
   const int sh_id = row_id / R;
@@ -319,6 +320,16 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   if (nc <= 1) return;                                   // written by the split kernel
   const int base = plan_prefix(p.seq_lens, s, cap, chunk, sh.sum);
   const size_t item0 = static_cast<size_t>(base) * kKvHeads + h;   // chunk c at item0 + c * 4
+  const float* base_o = p.part_o + (item0 * kRowsPerItem + r) * kHeadDim + 4 * lane;
+  const size_t cstride = static_cast<size_t>(kKvHeads) * kRowsPerItem * kHeadDim;   // floats between chunks
+  // the first chunk outputs of this wave go out now, before the weights
+  float4 early[kEarly];
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) {
+    const int c = wave + 4 * u;
+    early[u] = c < nc ? *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c) * cstride)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   // weights
   float mx = kNegInf;
   bool nan = false;
@@ -339,9 +350,15 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   }
   ws = block_sum_f(ws, sh.red);          // ends with a barrier: sh.w is complete
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* base_o = p.part_o + (item0 * kRowsPerItem + r) * kHeadDim + 4 * lane;
-  const size_t cstride = static_cast<size_t>(kKvHeads) * kRowsPerItem * kHeadDim;   // floats between chunks
-  int c = wave;
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) {
+    const int c = wave + 4 * u;
+    if (c < nc) {
+      const float wc = sh.w[c];
+      acc.x += wc * early[u].x; acc.y += wc * early[u].y; acc.z += wc * early[u].z; acc.w += wc * early[u].w;
+    }
+  }
+  int c = wave + 4 * kEarly;
   for (; c + 28 < nc; c += 32) {          // 8 independent loads in flight per lane
     float4 o[8];
 #pragma unroll

@@ -798,6 +798,19 @@ __device__ inline void build_q(const DecodeParams& p, int s, int h, int wave, ui
   }
 }
 
+// Issue priority from the share of this wave's tiles still to do.  Two
+// workgroups share each compute unit and the hardware favours the older
+// wave of a SIMD; a wave that falls behind its SIMD partner (which has the
+// same share of work) gets ahead in issue instead of finishing alone at the
+// end.  Results do not depend on it.
+__device__ inline void set_prio_remaining(int rem, int total) {
+  const int q = total > 0 ? (4 * rem - 1) / total : 0;
+  if (q >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (q == 2) __builtin_amdgcn_s_setprio(2);
+  else if (q == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Register double-buffering of the next tile pays for the compact quant rows;
 // the 16-bit rows use a single buffer (their loads are large enough that the
 // other waves cover the latency).
@@ -889,6 +902,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     // the first tile's loads go out before the query operands are built
     Tile<KT> ta, tb2;
     int ti = wave;
+    const int my_total = (n_tiles - wave + 3) / 4;
     if (ti < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
@@ -897,6 +911,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
       if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+      set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
       compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
@@ -904,6 +919,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
       wave_lds_sync();
       if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
+      set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
       compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
       ti += 4;
@@ -928,6 +944,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       for (int i = 0; i < 4; ++i) o[0][mt][i] += __shfl_xor(o[0][mt][i], 8, 64);
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- combine the 4 waves, write this chunk's rows, then merge
   __syncthreads();                       // every wave is done with its LDS tile region
   if (g == 0) {
