@@ -68,11 +68,14 @@ struct Fmt {
   // (the operands are read there); other types load K in operand layout.
   static constexpr bool kKStage = (KT == kQ4_0);
   static constexpr int kKraw = kKStage ? 32 * kRow : 0;
-  // Per wave: V codes; then (quant) V scales (f16, 512 B), the key bias
-  // (f32 [2][16]: 0 for a visible key, -inf past the chunk end or for a dead
-  // half), K scales (f32 [2][8][16] at +1024); then raw K rows.
-  static constexpr int kBias = kVtile + 512;
-  static constexpr int kWave = kVtile + (kQuant ? 2048 : 0) + kKraw;
+  // A V buffer: V codes, then (quant) V scales as f16 (512 B).  The K area
+  // (quant): the key bias (f32 [2][16]: 0 for a visible key, -inf past the
+  // chunk end or for a dead half), K scales (f32 [2][8][16]), raw K rows.
+  static constexpr int kVbuf = kVtile + (kQuant ? 512 : 0);
+  static constexpr int kKBias = 0;
+  static constexpr int kKScale = 512;
+  static constexpr int kKRaw = 1536;
+  static constexpr int kKarea = kQuant ? kKRaw + kKraw : 0;
 };
 
 __device__ inline f4 mma(u4 a, u4 b, f4 c, bool bf) {
@@ -388,13 +391,13 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
 
 // K operand of block b of half hf: 8 dims of one key as f16 (codes exact).
 template <int KT>
-__device__ inline u4 k_operand(const Tile<KT>& t, const uint8_t* wl, int hf, int b) {
+__device__ inline u4 k_operand(const Tile<KT>& t, const uint8_t* wk, int hf, int b) {
   const int i = kraw<KT>(b);
   if constexpr (KT == kQ4_0) {
     // raw row 16 hf + m in LDS: the 4 code bytes of dims 8g..8g+7 of block b
     // (2 bytes off a dword boundary for even b: two aligned dwords, shifted)
     const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
-    const uint8_t* r = wl + Fmt<KT>::kVtile + 2048 + (16 * hf + m) * Fmt<KT>::kRow + 18 * b + 4 * g;
+    const uint8_t* r = wk + Fmt<KT>::kKRaw + (16 * hf + m) * Fmt<KT>::kRow + 18 * b + 4 * g;
     uint32_t x;
     if (b & 1) {
       x = *reinterpret_cast<const uint32_t*>(r + 2);
@@ -416,7 +419,7 @@ __device__ inline u4 k_operand(const Tile<KT>& t, const uint8_t* wl, int hf, int
 // Writes the tile's V rows (and, for quant, V and K scales as f32) into the
 // wave's LDS region.  Keys at or past k1 are written as zeros.
 template <int KT>
-__device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1) {
+__device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT>& t, int tb, int k1) {
   using F = Fmt<KT>;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
@@ -434,7 +437,7 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
       }
     } else {
       float* vsc = reinterpret_cast<float*>(w + F::kVtile);              // V scales: [8 blocks][4 groups][8] fp16
-      float* ksc = reinterpret_cast<float*>(w + F::kVtile + 1024);       // [2 halves][8 blocks][16 keys]
+      float* ksc = reinterpret_cast<float*>(wk + F::kKScale);            // [2 halves][8 blocks][16 keys]
       const uint32_t* v = t.v[hf];
       u4 c0, c1, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
       uint32_t sa, sb;
@@ -485,14 +488,14 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
         ksc[(hf * 8 + 2 * g + 1) * 16 + m] = kb;
       }
       if (seg == 0) {
-        float* bias = reinterpret_cast<float*>(w + F::kBias);
+        float* bias = reinterpret_cast<float*>(wk + F::kKBias);
         bias[hf * 16 + j] = valid ? 0.f : kNegInf;
       }
     }
   }
   if constexpr (F::kKStage) {
     // raw K rows of both halves: piece e at byte 16 e
-    uint8_t* kr = w + F::kVtile + 2048;
+    uint8_t* kr = wk + F::kKRaw;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int e = 64 * i + lane;
@@ -511,7 +514,7 @@ __device__ inline void stage_tile(uint8_t* w, const Tile<KT>& t, int tb, int k1)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (!lv || tb + 16 * hf + m0 + i >= k1) d[i] = 0.f;
-    *reinterpret_cast<f4*>(w + F::kVtile + 1024 + ((hf * 8 + b) * 16 + m0) * 4) = d;
+    *reinterpret_cast<f4*>(wk + F::kKScale + ((hf * 8 + b) * 16 + m0) * 4) = d;
   }
 }
 
@@ -542,30 +545,24 @@ struct QSrc {
   }
 };
 
-// One tile's QK^T, online-softmax update and PV on the registers of `t` and
-// the V rows staged in the wave's LDS region `wl`.
+// QK^T of one tile: sacc[nt][hf] = S^T of half hf (lane (n, g): keys
+// 4g..4g+3 of the half, column n), from the tile's K and the K area `wk`.
+// Quant K: the accumulators start at the key bias (-inf for keys that are
+// not visible; their zeroed scales keep the products finite), so no
+// per-value mask is needed for the chunk end.
 template <int KT, int T>
-__device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int k1,
-                                    const int (&lim)[Cols<T>::NT], int lim_min, const QSrc<T>& qs,
-                                    f4 (&o)[Cols<T>::NT][16], float (&m_run)[Cols<T>::NT],
-                                    float (&l_run)[Cols<T>::NT]) {
+__device__ inline void qk_tile(const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs,
+                               f4 (&sacc)[Cols<T>::NT][2]) {
   using F = Fmt<KT>;
   using C = Cols<T>;
   constexpr int NT = C::NT;
   constexpr bool BF = F::kBf;
   const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-  const bool lo_lane = (n & 8) != 0;      // packed case: this lane carries lo parts
-
-  // ---- S^T = K Q^T (lane (n, g) gets rows 4g..4g+3 = keys of each half, column n)
-  // Quant K: the accumulators start at the key bias (-inf for keys that are
-  // not visible; their zeroed scales keep the products finite), so no
-  // per-value mask is needed for the chunk end.
-  f4 sacc[NT][2];
+  const int g = lane >> 4;
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     f4 init = f4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (F::kQuant) init = *reinterpret_cast<const f4*>(wl + F::kBias + (hf * 16 + 4 * g) * 4);
+    if constexpr (F::kQuant) init = *reinterpret_cast<const f4*>(wk + F::kKBias + (hf * 16 + 4 * g) * 4);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sacc[nt][hf] = init;
   }
@@ -578,9 +575,9 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const u4 a = k_operand<KT>(t, wl, hf, b);
+      const u4 a = k_operand<KT>(t, wk, hf, b);
       if constexpr (F::kQuant) {
-        const f4 dk = *reinterpret_cast<const f4*>(wl + F::kVtile + 1024 + ((hf * 8 + b) * 16 + 4 * g) * 4);
+        const f4 dk = *reinterpret_cast<const f4*>(wk + F::kKScale + ((hf * 8 + b) * 16 + 4 * g) * 4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           f4 cb = mma(a, qb[nt][0], f4{0.f, 0.f, 0.f, 0.f}, false);
@@ -602,14 +599,29 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[0][hf][i] += lane_xor8(sacc[0][hf][i]);
   }
+}
 
-  // ---- online softmax (base 2); p[nt][k] is the weight of key sigma(g, k).
-  // Masking is needed only where the tile crosses the chunk end or, for
-  // more than one token, the causal limit of some row (uniform test).
+// Online softmax (base 2) of one tile.  Updates the running base and sum,
+// returns the factor alpha[nt] by which the output accumulators must be
+// scaled (the caller applies it, after any PV still in flight for the base
+// before), and the PV B operands: the weights of keys sigma(g, k) split hi
+// + lo (one token: this lane's part), in the V operand's key order.
+// Returns true if some alpha is not 1.
+template <int KT, int T>
+__device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile<KT>& t, int tb, int k1,
+                                    const int (&lim)[Cols<T>::NT], int lim_min, float (&m_run)[Cols<T>::NT],
+                                    float (&l_run)[Cols<T>::NT], float (&alpha)[Cols<T>::NT],
+                                    u4 (&bh)[Cols<T>::NT], u4 (&bl)[Cols<T>::NT]) {
+  using F = Fmt<KT>;
+  using C = Cols<T>;
+  constexpr int NT = C::NT;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const bool lo_lane = (n & 8) != 0;      // packed case: this lane carries lo parts
   // Quant K needs a mask only where the causal limit of some row (more than
   // one token) falls inside the tile; other types also at the chunk end.
   const bool full = (F::kQuant || tb + 32 <= k1) && (T == 1 || tb + 31 <= lim_min);
-  float p[NT][8];
+  bool any = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float sv[8];
@@ -630,64 +642,69 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
     mx = max_xor32(mx);
     // The exponent base m_run moves only when the tile max exceeds it by more
     // than 8 (weights stay below 2^8), so the accumulators are rescaled rarely.
-    float alpha = 1.f;
+    float al = 1.f;
     if (mx > m_run[nt] + 8.f) {
       const float mn = mx;
-      alpha = (m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - mn);
+      al = (m_run[nt] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run[nt] - mn);
       m_run[nt] = mn;
     }
+    alpha[nt] = al;
+    any |= (al != 1.f);
     // exp2(-inf) is 0; only an all-masked history (base still -inf) needs a
     // finite stand-in base
     const float mb = (m_run[nt] == kNegInf) ? 0.f : m_run[nt];
+    float p[8];
     float rs = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      p[nt][k] = __builtin_amdgcn_exp2f(sv[k] - mb);
-      rs += p[nt][k];
+      p[k] = __builtin_amdgcn_exp2f(sv[k] - mb);
+      rs += p[k];
     }
     rs = sum_xor16(rs);
     rs = sum_xor32(rs);
-    l_run[nt] = l_run[nt] * alpha + rs;
-    if (__ballot(alpha != 1.f)) {
+    l_run[nt] = l_run[nt] * al + rs;
+    // PV B operand from the 8 weights, in the V operand's key order
+    float x[8];
+    if constexpr (KT == kQ4_0) {
+      constexpr int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
-      for (int mt = 0; mt < 16; ++mt) o[nt][mt] *= alpha;
+      for (int e = 0; e < 8; ++e) x[e] = p[pi[e]];
+    } else if constexpr (KT == kQ8_0) {
+      constexpr int pi[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = p[pi[e]];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = p[e];
     }
-  }
-
-  // B operands of PV from 8 weights: hi and lo parts (packed: this lane's part)
-  auto make_b = [&](const float (&x)[8], u4& bh, u4& bl, bool bf) {
-    split8(x, bh, bl, bf);
+    split8(x, bh[nt], bl[nt], F::kQuant ? false : F::kBf);
     if constexpr (C::kPack) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bh[k] = lo_lane ? bl[k] : bh[k];
+      for (int k = 0; k < 4; ++k) bh[nt][k] = lo_lane ? bl[nt][k] : bh[nt][k];
     }
-  };
+  }
+  return __ballot(any) != 0;
+}
 
-  // ---- O^T += V^T P^T.  Quant V: the operand is (c - 8) * d_v (or c * d_v)
-  // split exactly into hi + lo f16 parts; P is split hi + lo once per tile.
+// O^T += V^T P^T for one tile from the V buffer `wv`.  Quant V: the operand
+// is (c - 8) * d_v split exactly into hi + lo f16 parts.
+template <int KT, int T>
+__device__ inline void pv_tile(const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
+                               f4 (&o)[Cols<T>::NT][16]) {
+  using F = Fmt<KT>;
+  using C = Cols<T>;
+  constexpr int NT = C::NT;
+  constexpr bool BF = F::kBf;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
   if constexpr (F::kQuant) {
-    const _Float16* vh = reinterpret_cast<const _Float16*>(wl + F::kVtile);
-    u4 bh[NT], bl[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x[8];
-      if constexpr (KT == kQ4_0) {
-        constexpr int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]];
-      } else {
-        constexpr int pi[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = p[nt][pi[e]];
-      }
-      make_b(x, bh[nt], bl[nt], false);
-    }
+    const _Float16* vh = reinterpret_cast<const _Float16*>(wv + F::kVtile);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const u4 dv = *reinterpret_cast<const u4*>(vh + (b * 4 + g) * 8);
       if constexpr (KT == kQ4_0) {
         // source lane n supplies key sigma(g, n % 8), code bytes [8 (n / 8), +8) of block b
-        const uint8_t* src = wl + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
+        const uint8_t* src = wv + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
         const i2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2*)(src));
         u4 ah[2], al[2];
         scale_exact(q4_operand<false>(static_cast<uint32_t>(r[0])), dv, ah[0], al[0]);
@@ -706,7 +723,7 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
 #pragma unroll
         for (int hm = 0; hm < 2; ++hm) {
           // source lane n supplies key sigma(g, n / 2), code bytes [16 hm + 8 (n % 2), +8)
-          const uint8_t* src = wl + sigma(g, n >> 1) * F::kVks + 32 * b + 16 * hm + 8 * (n & 1);
+          const uint8_t* src = wv + sigma(g, n >> 1) * F::kVks + 32 * b + 16 * hm + 8 * (n & 1);
           const i2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(src));
           u4 ah, al;
           scale_exact(q8_operand(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])), dv, ah, al);
@@ -721,14 +738,11 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       }
     }
   } else {
-    u4 bh[NT], bl[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) make_b(p[nt], bh[nt], bl[nt], BF);
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt) {
       // source lane n supplies key sigma(g, n / 4) (then sigma(g, 4 + n / 4)), halves [16 mt + 4 (n % 4), +4)
-      const uint8_t* s0 = wl + sigma(g, n >> 2) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
-      const uint8_t* s1 = wl + sigma(g, 4 + (n >> 2)) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
+      const uint8_t* s0 = wv + sigma(g, n >> 2) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
+      const uint8_t* s1 = wv + sigma(g, 4 + (n >> 2)) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
       const s4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s0));
       const s4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(s1));
       const u2 ua = __builtin_bit_cast(u2, ra), ub = __builtin_bit_cast(u2, rb);
@@ -740,6 +754,29 @@ __device__ inline void compute_tile(const Tile<KT>& t, uint8_t* wl, int tb, int 
       }
     }
   }
+}
+
+template <int T>
+__device__ inline void rescale(f4 (&o)[Cols<T>::NT][16], const float (&alpha)[Cols<T>::NT]) {
+#pragma unroll
+  for (int nt = 0; nt < Cols<T>::NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 16; ++mt) o[nt][mt] *= alpha[nt];
+}
+
+// One tile in sequence: QK^T, softmax, PV.
+template <int KT, int T>
+__device__ inline void compute_tile(const Tile<KT>& t, const uint8_t* wv, const uint8_t* wk, int tb, int k1,
+                                    const int (&lim)[Cols<T>::NT], int lim_min, const QSrc<T>& qs,
+                                    f4 (&o)[Cols<T>::NT][16], float (&m_run)[Cols<T>::NT],
+                                    float (&l_run)[Cols<T>::NT]) {
+  constexpr int NT = Cols<T>::NT;
+  f4 sacc[NT][2];
+  qk_tile<KT, T>(t, wk, qs, sacc);
+  float alpha[NT];
+  u4 bh[NT], bl[NT];
+  if (softmax_tile<KT, T>(sacc, t, tb, k1, lim, lim_min, m_run, l_run, alpha, bh, bl)) rescale<T>(o, alpha);
+  pv_tile<KT, T>(wv, bh, bl, o);
 }
 
 // Output dim of accumulator element (M-tile mt, lane group g, element i).
@@ -823,8 +860,10 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   using C = Cols<T>;
   constexpr int R = C::R;
   constexpr int NT = C::NT;
+  // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
+  constexpr int kWaveBytes = (kDoubleBuffer<KT, T> ? 2 : 1) * F::kVbuf + F::kKarea;
   constexpr int kRed = 4 * R * kHeadDim * 4;
-  constexpr int kLds = (4 * F::kWave > kRed) ? 4 * F::kWave : kRed;
+  constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
@@ -882,7 +921,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     for (int mt = 0; mt < 16; ++mt) o[nt][mt] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint8_t* wl = lds + wave * F::kWave;
+  uint8_t* wl = lds + wave * kWaveBytes;
   bool bad = false;
   const int n_tiles = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
 
@@ -898,8 +937,12 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       for (int i = tid; i < n_tbl; i += kThreads) tbl_lds[i] = p.bt[static_cast<size_t>(s) * p.bt_stride + pg.lp0 + i];
   }
   if constexpr (kDoubleBuffer<KT, T>) {
-    // the next tile's loads are in flight while the current one is computed;
-    // the first tile's loads go out before the query operands are built
+    // Registers hold the next tile's loads while the current one is worked
+    // on, and PV runs one tile behind: while tile i is staged, its QK^T and
+    // softmax computed, the PV of tile i-4 (this wave's previous) runs from
+    // the other V buffer, giving the scheduler two independent streams.
+    // The output is rescaled for tile i's base only after that PV.
+    uint8_t* wk = wl + 2 * F::kVbuf;
     Tile<KT> ta, tb2;
     int ti = wave;
     const int my_total = (n_tiles - wave + 3) / 4;
@@ -907,33 +950,58 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
-    while (ti < n_tiles) {
-      stage_tile<KT>(wl, ta, k0 + 32 * ti, k1);
+    if (ti < n_tiles) {
+      u4 bh[NT], bl[NT];                  // PV operands of the previous tile
+      float alpha[NT];
+      f4 sacc[NT][2];
+      int vb = 0;                         // V buffer of the current tile
+      // first tile: no PV behind it yet
+      stage_tile<KT>(wl, wk, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
       if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
-      set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
-      compute_tile<KT, T>(ta, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
+      qk_tile<KT, T>(ta, wk, qs, sacc);
+      softmax_tile<KT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl);
       wave_lds_sync();
       ti += 4;
-      if (ti >= n_tiles) break;
-      stage_tile<KT>(wl, tb2, k0 + 32 * ti, k1);
-      wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
-      set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
-      compute_tile<KT, T>(tb2, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
-      wave_lds_sync();
-      ti += 4;
+      vb = 1;
+      while (ti < n_tiles) {
+        set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
+        stage_tile<KT>(wl + vb * F::kVbuf, wk, tb2, k0 + 32 * ti, k1);
+        wave_lds_sync();
+        if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
+        qk_tile<KT, T>(tb2, wk, qs, sacc);
+        pv_tile<KT, T>(wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
+        if (softmax_tile<KT, T>(sacc, tb2, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
+          rescale<T>(o, alpha);
+        wave_lds_sync();
+        ti += 4;
+        vb ^= 1;
+        if (ti >= n_tiles) break;
+        set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
+        stage_tile<KT>(wl + vb * F::kVbuf, wk, ta, k0 + 32 * ti, k1);
+        wave_lds_sync();
+        if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+        qk_tile<KT, T>(ta, wk, qs, sacc);
+        pv_tile<KT, T>(wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
+        if (softmax_tile<KT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
+          rescale<T>(o, alpha);
+        wave_lds_sync();
+        ti += 4;
+        vb ^= 1;
+      }
+      pv_tile<KT, T>(wl + (vb ^ 1) * F::kVbuf, bh, bl, o);   // the last tile's PV
     }
   } else {
+    uint8_t* wk = wl + F::kVbuf;
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
     for (int ti = wave; ti < n_tiles; ti += 4) {
       Tile<KT> tt;
       load_tile<KT>(p, pg, s, h, k0 + 32 * ti, k0, k1, tt, bad);
-      stage_tile<KT>(wl, tt, k0 + 32 * ti, k1);
+      stage_tile<KT>(wl, wk, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
-      compute_tile<KT, T>(tt, wl, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
+      compute_tile<KT, T>(tt, wl, wk, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
     }
   }
