@@ -551,54 +551,74 @@ struct QSrc {
 // not visible; their zeroed scales keep the products finite), so no
 // per-value mask is needed for the chunk end.
 template <int KT, int T>
-__device__ inline void qk_tile(const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs,
-                               f4 (&sacc)[Cols<T>::NT][2]) {
+__device__ inline void qk_init(const uint8_t* wk, f4 (&sacc)[Cols<T>::NT][2]) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f4 init = f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (Fmt<KT>::kQuant) init = *reinterpret_cast<const f4*>(wk + Fmt<KT>::kKBias + (hf * 16 + 4 * g) * 4);
+#pragma unroll
+    for (int nt = 0; nt < Cols<T>::NT; ++nt) sacc[nt][hf] = init;
+  }
+}
+
+// Block b (32 dims) of QK^T, both halves.
+template <int KT, int T>
+__device__ inline void qk_block(int b, const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs,
+                                f4 (&sacc)[Cols<T>::NT][2]) {
   using F = Fmt<KT>;
   using C = Cols<T>;
   constexpr int NT = C::NT;
   constexpr bool BF = F::kBf;
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
+  const int g = (threadIdx.x & 63) >> 4;
+  u4 qb[NT][C::kParts];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    f4 init = f4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (F::kQuant) init = *reinterpret_cast<const f4*>(wk + F::kKBias + (hf * 16 + 4 * g) * 4);
+    const u4 a = k_operand<KT>(t, wk, hf, b);
+    if constexpr (F::kQuant) {
+      const f4 dk = *reinterpret_cast<const f4*>(wk + F::kKScale + ((hf * 8 + b) * 16 + 4 * g) * 4);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sacc[nt][hf] = init;
-  }
+      for (int nt = 0; nt < NT; ++nt) {
+        f4 cb = mma(a, qb[nt][0], f4{0.f, 0.f, 0.f, 0.f}, false);
+        if constexpr (C::kParts == 2) cb = mma(a, qb[nt][1], cb, false);
+        sacc[nt][hf] += dk * cb;       // per-key block scale on the exact-code product
+      }
+    } else {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    u4 qb[NT][C::kParts];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const u4 a = k_operand<KT>(t, wk, hf, b);
-      if constexpr (F::kQuant) {
-        const f4 dk = *reinterpret_cast<const f4*>(wk + F::kKScale + ((hf * 8 + b) * 16 + 4 * g) * 4);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f4 cb = mma(a, qb[nt][0], f4{0.f, 0.f, 0.f, 0.f}, false);
-          if constexpr (C::kParts == 2) cb = mma(a, qb[nt][1], cb, false);
-          sacc[nt][hf] += dk * cb;       // per-key block scale on the exact-code product
-        }
-      } else {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          sacc[nt][hf] = mma(a, qb[nt][0], sacc[nt][hf], BF);
-          if constexpr (C::kParts == 2) sacc[nt][hf] = mma(a, qb[nt][1], sacc[nt][hf], BF);
-        }
+      for (int nt = 0; nt < NT; ++nt) {
+        sacc[nt][hf] = mma(a, qb[nt][0], sacc[nt][hf], BF);
+        if constexpr (C::kParts == 2) sacc[nt][hf] = mma(a, qb[nt][1], sacc[nt][hf], BF);
       }
     }
   }
-  if constexpr (C::kPack) {
+}
+
+template <int T>
+__device__ inline void qk_finish(f4 (&sacc)[Cols<T>::NT][2]) {
+  if constexpr (Cols<T>::kPack) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 4; ++i) sacc[0][hf][i] += lane_xor8(sacc[0][hf][i]);
   }
+}
+
+// QK^T of one tile: sacc[nt][hf] = S^T of half hf (lane (n, g): keys
+// 4g..4g+3 of the half, column n), from the tile's K and the K area `wk`.
+// Quant K: the accumulators start at the key bias (-inf for keys that are
+// not visible; their zeroed scales keep the products finite), so no
+// per-value mask is needed for the chunk end.
+template <int KT, int T>
+__device__ inline void qk_tile(const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs,
+                               f4 (&sacc)[Cols<T>::NT][2]) {
+  qk_init<KT, T>(wk, sacc);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) qk_block<KT, T>(b, t, wk, qs, sacc);
+  qk_finish<T>(sacc);
 }
 
 // Online softmax (base 2) of one tile.  Updates the running base and sum,
@@ -686,11 +706,12 @@ __device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile
   return __ballot(any) != 0;
 }
 
-// O^T += V^T P^T for one tile from the V buffer `wv`.  Quant V: the operand
-// is (c - 8) * d_v split exactly into hi + lo f16 parts.
+// Block b of O^T += V^T P^T from the V buffer `wv` (quant V; for 16-bit V
+// the two M-tiles of dims [32 b, 32 b + 32)).  Quant V: the operand is
+// (c - 8) * d_v split exactly into hi + lo f16 parts.
 template <int KT, int T>
-__device__ inline void pv_tile(const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
-                               f4 (&o)[Cols<T>::NT][16]) {
+__device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
+                                f4 (&o)[Cols<T>::NT][16]) {
   using F = Fmt<KT>;
   using C = Cols<T>;
   constexpr int NT = C::NT;
@@ -699,47 +720,44 @@ __device__ inline void pv_tile(const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], c
   const int n = lane & 15, g = lane >> 4;
   if constexpr (F::kQuant) {
     const _Float16* vh = reinterpret_cast<const _Float16*>(wv + F::kVtile);
+    const u4 dv = *reinterpret_cast<const u4*>(vh + (b * 4 + g) * 8);
+    if constexpr (KT == kQ4_0) {
+      // source lane n supplies key sigma(g, n % 8), code bytes [8 (n / 8), +8) of block b
+      const uint8_t* src = wv + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
+      const i2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2*)(src));
+      u4 ah[2], al[2];
+      scale_exact(q4_operand<false>(static_cast<uint32_t>(r[0])), dv, ah[0], al[0]);
+      scale_exact(q4_operand<false>(static_cast<uint32_t>(r[1])), dv, ah[1], al[1]);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const u4 dv = *reinterpret_cast<const u4*>(vh + (b * 4 + g) * 8);
-      if constexpr (KT == kQ4_0) {
-        // source lane n supplies key sigma(g, n % 8), code bytes [8 (n / 8), +8) of block b
-        const uint8_t* src = wv + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
-        const i2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2*)(src));
-        u4 ah[2], al[2];
-        scale_exact(q4_operand<false>(static_cast<uint32_t>(r[0])), dv, ah[0], al[0]);
-        scale_exact(q4_operand<false>(static_cast<uint32_t>(r[1])), dv, ah[1], al[1]);
+      for (int hm = 0; hm < 2; ++hm) {
 #pragma unroll
-        for (int hm = 0; hm < 2; ++hm) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f4& acc = o[nt][2 * b + hm];
-            acc = mma(ah[hm], bh[nt], acc, false);
-            acc = mma(al[hm], bh[nt], acc, false);
-            if constexpr (C::kParts == 2) acc = mma(ah[hm], bl[nt], acc, false);
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          f4& acc = o[nt][2 * b + hm];
+          acc = mma(ah[hm], bh[nt], acc, false);
+          acc = mma(al[hm], bh[nt], acc, false);
+          if constexpr (C::kParts == 2) acc = mma(ah[hm], bl[nt], acc, false);
         }
-      } else {
+      }
+    } else {
 #pragma unroll
-        for (int hm = 0; hm < 2; ++hm) {
-          // source lane n supplies key sigma(g, n / 2), code bytes [16 hm + 8 (n % 2), +8)
-          const uint8_t* src = wv + sigma(g, n >> 1) * F::kVks + 32 * b + 16 * hm + 8 * (n & 1);
-          const i2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(src));
-          u4 ah, al;
-          scale_exact(q8_operand(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])), dv, ah, al);
+      for (int hm = 0; hm < 2; ++hm) {
+        // source lane n supplies key sigma(g, n / 2), code bytes [16 hm + 8 (n % 2), +8)
+        const uint8_t* src = wv + sigma(g, n >> 1) * F::kVks + 32 * b + 16 * hm + 8 * (n & 1);
+        const i2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i2*)(src));
+        u4 ah, al;
+        scale_exact(q8_operand(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])), dv, ah, al);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f4& acc = o[nt][2 * b + hm];
-            acc = mma(ah, bh[nt], acc, false);
-            acc = mma(al, bh[nt], acc, false);
-            if constexpr (C::kParts == 2) acc = mma(ah, bl[nt], acc, false);
-          }
+        for (int nt = 0; nt < NT; ++nt) {
+          f4& acc = o[nt][2 * b + hm];
+          acc = mma(ah, bh[nt], acc, false);
+          acc = mma(al, bh[nt], acc, false);
+          if constexpr (C::kParts == 2) acc = mma(ah, bl[nt], acc, false);
         }
       }
     }
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt) {
+    for (int mt = 2 * b; mt < 2 * b + 2; ++mt) {
       // source lane n supplies key sigma(g, n / 4) (then sigma(g, 4 + n / 4)), halves [16 mt + 4 (n % 4), +4)
       const uint8_t* s0 = wv + sigma(g, n >> 2) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
       const uint8_t* s1 = wv + sigma(g, 4 + (n >> 2)) * F::kVks + 2 * (16 * mt + 4 * (n & 3));
@@ -754,6 +772,29 @@ __device__ inline void pv_tile(const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], c
       }
     }
   }
+}
+
+template <int KT, int T>
+__device__ inline void pv_tile(const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
+                               f4 (&o)[Cols<T>::NT][16]) {
+#pragma unroll
+  for (int b = 0; b < 8; ++b) pv_block<KT, T>(b, wv, bh, bl, o);
+}
+
+// QK^T of tile i interleaved block by block with the PV of the previous tile
+// (independent work: in-order issue then finds one stream's instructions
+// while the other waits on LDS or matrix-core results).
+template <int KT, int T>
+__device__ inline void qk_with_pv(const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs, f4 (&sacc)[Cols<T>::NT][2],
+                                  const uint8_t* wv_prev, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
+                                  f4 (&o)[Cols<T>::NT][16]) {
+  qk_init<KT, T>(wk, sacc);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    qk_block<KT, T>(b, t, wk, qs, sacc);
+    pv_block<KT, T>(b, wv_prev, bh, bl, o);
+  }
+  qk_finish<T>(sacc);
 }
 
 template <int T>
@@ -969,8 +1010,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
         stage_tile<KT>(wl + vb * F::kVbuf, wk, tb2, k0 + 32 * ti, k1);
         wave_lds_sync();
         if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
-        qk_tile<KT, T>(tb2, wk, qs, sacc);
-        pv_tile<KT, T>(wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
+        qk_with_pv<KT, T>(tb2, wk, qs, sacc, wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
         if (softmax_tile<KT, T>(sacc, tb2, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
           rescale<T>(o, alpha);
         wave_lds_sync();
@@ -981,8 +1021,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
         stage_tile<KT>(wl + vb * F::kVbuf, wk, ta, k0 + 32 * ti, k1);
         wave_lds_sync();
         if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
-        qk_tile<KT, T>(ta, wk, qs, sacc);
-        pv_tile<KT, T>(wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
+        qk_with_pv<KT, T>(ta, wk, qs, sacc, wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
         if (softmax_tile<KT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
           rescale<T>(o, alpha);
         wave_lds_sync();
