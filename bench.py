@@ -31,7 +31,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ragged", choices=["ragged", "uniform", "f16"])
+    ap.add_argument("--workload", default="ragged", choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16"],
+                    help="ragged: 131072 + 7 x 8192 Q4_0 (the headline); ragged_q8k_q4v: same with Q8_0 K and Q4_0 V; "
+                         "uniform: 8 x 4096 Q4_0; mtp: one 131072-position Q8_0 sequence, --qtok query tokens; "
+                         "f16: one 1024-position F16 sequence")
+    ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -125,8 +129,12 @@ def main():
     t_gen = time.perf_counter()
     if args.workload == "ragged":
         w = synth.config3()
+    elif args.workload == "ragged_q8k_q4v":
+        w = synth.ragged_mixed()
     elif args.workload == "uniform":
         w = synth.config2()
+    elif args.workload == "mtp":
+        w = synth.config4(ctx=131072, n_qtok=args.qtok)
     else:
         w = synth.config1()
     print(f"[bench] workload {w['name']} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -227,7 +235,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w["name"], "n_seq": n_seq, "seq_lens": "131072+7x8192" if args.workload == "ragged"
+        "config": {"workload": w["name"], "n_seq": n_seq, "seq_lens": "131072+7x8192" if args.workload.startswith("ragged")
                    else ",".join(str(int(x)) for x in w["seq_lens"]), "n_qtok": T, "kv": w["k_kind"],
                    "page_size": P, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "kv_bytes": int(kv_bytes)},
         "attention_step_ms": round(cold_ms, 4),

@@ -69,8 +69,10 @@ const char *pa_version(void);
  *    value = (c-8)*d (size: lucebox pull 555, K/V capacity table; scale
  *    position: llama.cpp pull 2, same commit).  144 bytes.
  * A kv_type argument packs the K encoding in bits 0-7 and the V encoding in
- * bits 8-15; a V field of 0 means "same as K".  This build decodes pairs with
- * K == V; other pairs return PA_ERR_UNSUPPORTED. */
+ * bits 8-15; a V field of 0 means "same as K".  Every pair is decoded: K and
+ * V pools may hold different encodings (lucebox pull 555, Validation: all
+ * nine F16/Q8_0/Q4_0 K x V combinations; llama.cpp pull 2 defaults to Q8_0
+ * K with Q4_0 V). */
 enum { PA_F16 = 1, PA_BF16 = 2, PA_Q8_0 = 3, PA_Q4_0 = 4 };
 #define PA_KV_TYPE(k, v) ((int32_t)((k) | ((v) << 8)))
 

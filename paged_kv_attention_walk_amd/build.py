@@ -5,6 +5,7 @@
 Every call compiles from source; nothing is cached between calls.
 """
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -53,10 +54,16 @@ def build(verbose: bool = True) -> str:
     o = os.path.join(BUILD_DIR, "pa_host.o")
     _run([cxx, *HOST_FLAGS, *inc, *hip_inc, "-c", os.path.join(CSRC, "pa_host.cpp"), "-o", o], verbose)
     objs.append(o)
+    # the two device sources compile in parallel (each instantiates every
+    # K type x V type x token count)
+    cmds = []
     for name in ("pa_kernels", "pa_mfma"):
         o = os.path.join(BUILD_DIR, name + ".o")
-        _run([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o], verbose)
+        cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

@@ -81,7 +81,6 @@ pa_status parse_kv_type(int32_t kv_type, int* k, int* v) {
   int vt = (kv_type >> 8) & 0xFF;
   if (vt == 0) vt = kt;
   if (!type_ok(kt) || !type_ok(vt)) return PA_ERR_INVALID;
-  if (kt != vt) return PA_ERR_UNSUPPORTED;
   *k = kt;
   *v = vt;
   return PA_OK;
@@ -437,7 +436,7 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   // The plan aims at one round of resident workgroups; the workspace check
   // above used the larger capacity target, so these items always fit.
   const int cu = cu_count(device);
-  const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, n_qtok, engine);
+  const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, n_qtok, engine);
   const int64_t plan = pa::plan_target(n_seq, slots, target);
   prm.target_items = static_cast<int32_t>(plan);
   prm.max_items = static_cast<int32_t>(pa::max_work_items(n_seq, plan));

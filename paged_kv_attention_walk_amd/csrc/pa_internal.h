@@ -68,8 +68,8 @@ inline int64_t plan_target(int64_t n_seq, int64_t slots, int64_t cap) {
 
 // Resident workgroups per compute unit of the split kernel a call selects
 // (from the runtime's occupancy query; at least 1).
-int split_wgs_per_cu(int k_type, int n_qtok, int engine);
-int split_mfma_wgs_per_cu(int k_type, int n_qtok);
+int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine);
+int split_mfma_wgs_per_cu(int k_type, int v_type, int n_qtok);
 
 struct WorkspaceLayout {
   int64_t items;       // work-item capacity

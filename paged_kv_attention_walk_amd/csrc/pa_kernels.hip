@@ -266,17 +266,28 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int KT>
-hipError_t launch_valu_kt(const DecodeParams& p, hipStream_t stream) {
+template <int KT, int VT>
+hipError_t launch_valu_kvt(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.max_items), block(kThreads);
   switch (p.n_qtok) {
-    case 1: hipLaunchKernelGGL((split_valu_kernel<KT, KT, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((split_valu_kernel<KT, KT, 2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((split_valu_kernel<KT, KT, 3>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((split_valu_kernel<KT, KT, 4>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((split_valu_kernel<KT, VT, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((split_valu_kernel<KT, VT, 2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((split_valu_kernel<KT, VT, 3>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((split_valu_kernel<KT, VT, 4>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int KT>
+hipError_t launch_valu_kt(const DecodeParams& p, hipStream_t stream) {
+  switch (p.v_type) {
+    case kF16: return launch_valu_kvt<KT, kF16>(p, stream);
+    case kBF16: return launch_valu_kvt<KT, kBF16>(p, stream);
+    case kQ8_0: return launch_valu_kvt<KT, kQ8_0>(p, stream);
+    case kQ4_0: return launch_valu_kvt<KT, kQ4_0>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_split_valu(const DecodeParams& p, hipStream_t stream) {
@@ -291,14 +302,13 @@ hipError_t launch_split_valu(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-int split_wgs_per_cu(int k_type, int n_qtok, int engine) {
+int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine) {
   if (engine == 1) return 2;     // vector reference path: 256 threads, modest registers
-  return split_mfma_wgs_per_cu(k_type, n_qtok);
+  return split_mfma_wgs_per_cu(k_type, v_type, n_qtok);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.n_seq <= 0) return hipSuccess;
-  if (p.k_type != p.v_type) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   if (ev_begin) e = hipEventRecord(ev_begin, stream);
   if (e != hipSuccess) return e;

@@ -284,13 +284,14 @@ __device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int
 // 8g..8g+7 of every block of key m, as aligned dwords (blocks that start
 // 2 bytes off a dword boundary take one dword more and are funnel-shifted
 // when used); K scales: the dwords holding the scales of blocks 2g and 2g+1;
-// V: lane (j, seg) holds bytes [seg * 4 kVw, +4 kVw) of row j.
-template <int KT>
+// V: lane (j, seg) holds bytes [seg * 4 kVw, +4 kVw) of row j.  K and V
+// may be of different types.
+template <int KT, int VT>
 struct Tile {
   // raw K dwords per half (Q4_0: both halves as 5 16-byte pieces in kp)
   static constexpr int kKr = (KT == kQ4_0) ? 1 : (KT == kQ8_0) ? 20 : 32;
   static constexpr int kKp = (KT == kQ4_0) ? 20 : 1;
-  static constexpr int kVw = (KT == kQ4_0) ? 9 : (KT == kQ8_0) ? 17 : 32;    // raw V dwords per half
+  static constexpr int kVw = (VT == kQ4_0) ? 9 : (VT == kQ8_0) ? 17 : 32;    // raw V dwords per half
   uint32_t k[2][kKr];
   uint32_t kp[kKp];
   uint32_t ks[2][2];
@@ -320,10 +321,11 @@ __device__ inline u4a ld128(const uint8_t* base, uint32_t off) { return *reinter
 
 // Issues the loads of the tile at tb.  Only loads: no instruction here reads
 // a loaded register.
-template <int KT>
+template <int KT, int VT>
 __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, int h, int tb, int k0, int k1,
-                                 Tile<KT>& t, bool& bad) {
+                                 Tile<KT, VT>& t, bool& bad) {
   using F = Fmt<KT>;
+  using FV = Fmt<VT>;
   const int lane = threadIdx.x & 63;
   const uint32_t m = lane & 15, g = lane >> 4;
   const uint32_t j = lane >> 2, seg = lane & 3;
@@ -333,7 +335,7 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
     const Half hv = locate(p, pg, s, h, tb + 16 * hf, k0, k1, bad);
     t.live[hf] = hv.live;
     const uint8_t* rk = p.k + hv.row * F::kRow;
-    const uint8_t* rv = p.v + hv.row * F::kRow;
+    const uint8_t* rv = p.v + hv.row * FV::kRow;
     rk_half[hf] = rk;
     if constexpr (F::kKStage) {
       // K of both halves is loaded below as contiguous pieces
@@ -361,16 +363,16 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
       t.ks[hf][0] = ld32(rk, m * F::kRow + 68 * g);
       t.ks[hf][1] = ld32(rk, m * F::kRow + 68 * g + 32);
     }
-    if constexpr (KT == kF16 || KT == kBF16) {
-      const uint32_t o = j * F::kRow + 128 * seg;
+    if constexpr (VT == kF16 || VT == kBF16) {
+      const uint32_t o = j * FV::kRow + 128 * seg;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const u4a x = ld128(rv, o + 16 * i);
         t.v[hf][4 * i] = x[0]; t.v[hf][4 * i + 1] = x[1]; t.v[hf][4 * i + 2] = x[2]; t.v[hf][4 * i + 3] = x[3];
       }
     } else {
-      constexpr int W = Tile<KT>::kVw;
-      const uint32_t o = j * F::kRow + (W * 4) * seg;
+      constexpr int W = Tile<KT, VT>::kVw;
+      const uint32_t o = j * FV::kRow + (W * 4) * seg;
 #pragma unroll
       for (int i = 0; i + 4 <= W; i += 4) {
         const u4a x = ld128(rv, o + 4 * i);
@@ -390,8 +392,8 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
 }
 
 // K operand of block b of half hf: 8 dims of one key as f16 (codes exact).
-template <int KT>
-__device__ inline u4 k_operand(const Tile<KT>& t, const uint8_t* wk, int hf, int b) {
+template <int KT, int VT>
+__device__ inline u4 k_operand(const Tile<KT, VT>& t, const uint8_t* wk, int hf, int b) {
   const int i = kraw<KT>(b);
   if constexpr (KT == kQ4_0) {
     // raw row 16 hf + m in LDS: the 4 code bytes of dims 8g..8g+7 of block b
@@ -416,11 +418,13 @@ __device__ inline u4 k_operand(const Tile<KT>& t, const uint8_t* wk, int hf, int
   }
 }
 
-// Writes the tile's V rows (and, for quant, V and K scales as f32) into the
-// wave's LDS region.  Keys at or past k1 are written as zeros.
-template <int KT>
-__device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT>& t, int tb, int k1) {
+// Writes the tile's V rows into the V buffer `w` (quant V: codes and f16
+// scales) and, for quant K, the K scales (f32) and key bias into the K area
+// `wk`.  Keys at or past k1 are written as zeros.
+template <int KT, int VT>
+__device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT, VT>& t, int tb, int k1) {
   using F = Fmt<KT>;
+  using FV = Fmt<VT>;
   const int lane = threadIdx.x & 63;
   const int m = lane & 15, g = lane >> 4;
   const int j = lane >> 2, seg = lane & 3;
@@ -428,20 +432,19 @@ __device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT>& t, in
   for (int hf = 0; hf < 2; ++hf) {
     const int key = 16 * hf + j;
     const bool valid = t.live[hf] && (tb + key < k1);
-    if constexpr (KT == kF16 || KT == kBF16) {
+    if constexpr (VT == kF16 || VT == kBF16) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         u4 x = {t.v[hf][4 * i], t.v[hf][4 * i + 1], t.v[hf][4 * i + 2], t.v[hf][4 * i + 3]};
         if (!valid) x = u4{0, 0, 0, 0};
-        *reinterpret_cast<u4*>(w + key * F::kVks + 128 * seg + 16 * i) = x;
+        *reinterpret_cast<u4*>(w + key * FV::kVks + 128 * seg + 16 * i) = x;
       }
     } else {
-      float* vsc = reinterpret_cast<float*>(w + F::kVtile);              // V scales: [8 blocks][4 groups][8] fp16
-      float* ksc = reinterpret_cast<float*>(wk + F::kKScale);            // [2 halves][8 blocks][16 keys]
+      float* vsc = reinterpret_cast<float*>(w + FV::kVtile);             // V scales: [8 blocks][4 groups][8] fp16
       const uint32_t* v = t.v[hf];
       u4 c0, c1, c2 = {0, 0, 0, 0}, c3 = {0, 0, 0, 0};
       uint32_t sa, sb;
-      if constexpr (KT == kQ4_0) {
+      if constexpr (VT == kQ4_0) {
         c0 = u4{funnel16(v[0], v[1]), funnel16(v[1], v[2]), funnel16(v[2], v[3]), funnel16(v[3], v[4])};
         c1 = u4{v[5], v[6], v[7], v[8]};
         sa = v[0] & 0xFFFFu;
@@ -458,8 +461,8 @@ __device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT>& t, in
         c0 = c1 = c2 = c3 = u4{0, 0, 0, 0};
         sa = sb = 0u;
       }
-      uint8_t* row = w + key * F::kVks;
-      if constexpr (KT == kQ4_0) {
+      uint8_t* row = w + key * FV::kVks;
+      if constexpr (VT == kQ4_0) {
         *reinterpret_cast<u4*>(row + 16 * (2 * seg)) = c0;
         *reinterpret_cast<u4*>(row + 16 * (2 * seg + 1)) = c1;
       } else {
@@ -473,15 +476,18 @@ __device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT>& t, in
       {
         const int kk = (key & 3) + 4 * (key >> 4), gg = (key >> 2) & 3;
         int pos;
-        if constexpr (KT == kQ4_0) pos = (kk & 3) * 2 + (kk >> 2);                 // pairs (0,4)(1,5)(2,6)(3,7)
+        if constexpr (VT == kQ4_0) pos = (kk & 3) * 2 + (kk >> 2);                 // pairs (0,4)(1,5)(2,6)(3,7)
         else pos = (kk < 4) ? (kk & 1) * 2 + (kk >> 1) : 4 + ((kk - 4) & 1) * 2 + ((kk - 4) >> 1);  // (0,2)(1,3)(4,6)(5,7)
         uint16_t* vh = reinterpret_cast<uint16_t*>(vsc);
         vh[((2 * seg) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sa);        // fp16 bits as stored
         vh[((2 * seg + 1) * 4 + gg) * 8 + pos] = static_cast<uint16_t>(sb);
       }
+    }
+    if constexpr (F::kQuant) {
       if constexpr (!F::kKStage) {
         // K scales: lane (m, g) holds blocks 2g, 2g+1 of key m of this half;
         // zero for keys that are not visible, so their codes give 0, not NaN
+        float* ksc = reinterpret_cast<float*>(wk + F::kKScale);          // [2 halves][8 blocks][16 keys]
         float ka = half_bits(t.ks[hf][0] & 0xFFFFu), kb = half_bits(t.ks[hf][1] >> 16);
         if (!t.live[hf] || tb + 16 * hf + m >= k1) ka = kb = 0.f;
         ksc[(hf * 8 + 2 * g) * 16 + m] = ka;
@@ -563,8 +569,8 @@ __device__ inline void qk_init(const uint8_t* wk, f4 (&sacc)[Cols<T>::NT][2]) {
 }
 
 // Block b (32 dims) of QK^T, both halves.
-template <int KT, int T>
-__device__ inline void qk_block(int b, const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs,
+template <int KT, int VT, int T>
+__device__ inline void qk_block(int b, const Tile<KT, VT>& t, const uint8_t* wk, const QSrc<T>& qs,
                                 f4 (&sacc)[Cols<T>::NT][2]) {
   using F = Fmt<KT>;
   using C = Cols<T>;
@@ -578,7 +584,7 @@ __device__ inline void qk_block(int b, const Tile<KT>& t, const uint8_t* wk, con
     for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const u4 a = k_operand<KT>(t, wk, hf, b);
+    const u4 a = k_operand<KT, VT>(t, wk, hf, b);
     if constexpr (F::kQuant) {
       const f4 dk = *reinterpret_cast<const f4*>(wk + F::kKScale + ((hf * 8 + b) * 16 + 4 * g) * 4);
 #pragma unroll
@@ -612,12 +618,12 @@ __device__ inline void qk_finish(f4 (&sacc)[Cols<T>::NT][2]) {
 // Quant K: the accumulators start at the key bias (-inf for keys that are
 // not visible; their zeroed scales keep the products finite), so no
 // per-value mask is needed for the chunk end.
-template <int KT, int T>
-__device__ inline void qk_tile(const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs,
+template <int KT, int VT, int T>
+__device__ inline void qk_tile(const Tile<KT, VT>& t, const uint8_t* wk, const QSrc<T>& qs,
                                f4 (&sacc)[Cols<T>::NT][2]) {
   qk_init<KT, T>(wk, sacc);
 #pragma unroll
-  for (int b = 0; b < 8; ++b) qk_block<KT, T>(b, t, wk, qs, sacc);
+  for (int b = 0; b < 8; ++b) qk_block<KT, VT, T>(b, t, wk, qs, sacc);
   qk_finish<T>(sacc);
 }
 
@@ -627,8 +633,8 @@ __device__ inline void qk_tile(const Tile<KT>& t, const uint8_t* wk, const QSrc<
 // before), and the PV B operands: the weights of keys sigma(g, k) split hi
 // + lo (one token: this lane's part), in the V operand's key order.
 // Returns true if some alpha is not 1.
-template <int KT, int T>
-__device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile<KT>& t, int tb, int k1,
+template <int KT, int VT, int T>
+__device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile<KT, VT>& t, int tb, int k1,
                                     const int (&lim)[Cols<T>::NT], int lim_min, float (&m_run)[Cols<T>::NT],
                                     float (&l_run)[Cols<T>::NT], float (&alpha)[Cols<T>::NT],
                                     u4 (&bh)[Cols<T>::NT], u4 (&bl)[Cols<T>::NT]) {
@@ -685,11 +691,11 @@ __device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile
     l_run[nt] = l_run[nt] * al + rs;
     // PV B operand from the 8 weights, in the V operand's key order
     float x[8];
-    if constexpr (KT == kQ4_0) {
+    if constexpr (VT == kQ4_0) {
       constexpr int pi[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = p[pi[e]];
-    } else if constexpr (KT == kQ8_0) {
+    } else if constexpr (VT == kQ8_0) {
       constexpr int pi[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = p[pi[e]];
@@ -697,7 +703,7 @@ __device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = p[e];
     }
-    split8(x, bh[nt], bl[nt], F::kQuant ? false : F::kBf);
+    split8(x, bh[nt], bl[nt], Fmt<VT>::kQuant ? false : Fmt<VT>::kBf);
     if constexpr (C::kPack) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) bh[nt][k] = lo_lane ? bl[nt][k] : bh[nt][k];
@@ -709,10 +715,10 @@ __device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile
 // Block b of O^T += V^T P^T from the V buffer `wv` (quant V; for 16-bit V
 // the two M-tiles of dims [32 b, 32 b + 32)).  Quant V: the operand is
 // (c - 8) * d_v split exactly into hi + lo f16 parts.
-template <int KT, int T>
+template <int VT, int T>
 __device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
                                 f4 (&o)[Cols<T>::NT][16]) {
-  using F = Fmt<KT>;
+  using F = Fmt<VT>;
   using C = Cols<T>;
   constexpr int NT = C::NT;
   constexpr bool BF = F::kBf;
@@ -721,7 +727,7 @@ __device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>
   if constexpr (F::kQuant) {
     const _Float16* vh = reinterpret_cast<const _Float16*>(wv + F::kVtile);
     const u4 dv = *reinterpret_cast<const u4*>(vh + (b * 4 + g) * 8);
-    if constexpr (KT == kQ4_0) {
+    if constexpr (VT == kQ4_0) {
       // source lane n supplies key sigma(g, n % 8), code bytes [8 (n / 8), +8) of block b
       const uint8_t* src = wv + sigma(g, n & 7) * F::kVks + 16 * b + 8 * (n >> 3);
       const i2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i2*)(src));
@@ -774,25 +780,25 @@ __device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>
   }
 }
 
-template <int KT, int T>
+template <int VT, int T>
 __device__ inline void pv_tile(const uint8_t* wv, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
                                f4 (&o)[Cols<T>::NT][16]) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) pv_block<KT, T>(b, wv, bh, bl, o);
+  for (int b = 0; b < 8; ++b) pv_block<VT, T>(b, wv, bh, bl, o);
 }
 
 // QK^T of tile i interleaved block by block with the PV of the previous tile
 // (independent work: in-order issue then finds one stream's instructions
 // while the other waits on LDS or matrix-core results).
-template <int KT, int T>
-__device__ inline void qk_with_pv(const Tile<KT>& t, const uint8_t* wk, const QSrc<T>& qs, f4 (&sacc)[Cols<T>::NT][2],
+template <int KT, int VT, int T>
+__device__ inline void qk_with_pv(const Tile<KT, VT>& t, const uint8_t* wk, const QSrc<T>& qs, f4 (&sacc)[Cols<T>::NT][2],
                                   const uint8_t* wv_prev, const u4 (&bh)[Cols<T>::NT], const u4 (&bl)[Cols<T>::NT],
                                   f4 (&o)[Cols<T>::NT][16]) {
   qk_init<KT, T>(wk, sacc);
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
-    qk_block<KT, T>(b, t, wk, qs, sacc);
-    pv_block<KT, T>(b, wv_prev, bh, bl, o);
+    qk_block<KT, VT, T>(b, t, wk, qs, sacc);
+    pv_block<VT, T>(b, wv_prev, bh, bl, o);
   }
   qk_finish<T>(sacc);
 }
@@ -806,18 +812,18 @@ __device__ inline void rescale(f4 (&o)[Cols<T>::NT][16], const float (&alpha)[Co
 }
 
 // One tile in sequence: QK^T, softmax, PV.
-template <int KT, int T>
-__device__ inline void compute_tile(const Tile<KT>& t, const uint8_t* wv, const uint8_t* wk, int tb, int k1,
+template <int KT, int VT, int T>
+__device__ inline void compute_tile(const Tile<KT, VT>& t, const uint8_t* wv, const uint8_t* wk, int tb, int k1,
                                     const int (&lim)[Cols<T>::NT], int lim_min, const QSrc<T>& qs,
                                     f4 (&o)[Cols<T>::NT][16], float (&m_run)[Cols<T>::NT],
                                     float (&l_run)[Cols<T>::NT]) {
   constexpr int NT = Cols<T>::NT;
   f4 sacc[NT][2];
-  qk_tile<KT, T>(t, wk, qs, sacc);
+  qk_tile<KT, VT, T>(t, wk, qs, sacc);
   float alpha[NT];
   u4 bh[NT], bl[NT];
-  if (softmax_tile<KT, T>(sacc, t, tb, k1, lim, lim_min, m_run, l_run, alpha, bh, bl)) rescale<T>(o, alpha);
-  pv_tile<KT, T>(wv, bh, bl, o);
+  if (softmax_tile<KT, VT, T>(sacc, t, tb, k1, lim, lim_min, m_run, l_run, alpha, bh, bl)) rescale<T>(o, alpha);
+  pv_tile<VT, T>(wv, bh, bl, o);
 }
 
 // Output dim of accumulator element (M-tile mt, lane group g, element i).
@@ -892,17 +898,18 @@ __device__ inline void set_prio_remaining(int rem, int total) {
 // Register double-buffering of the next tile pays for the compact quant rows;
 // the 16-bit rows use a single buffer (their loads are large enough that the
 // other waves cover the latency).
-template <int KT, int T>
-constexpr bool kDoubleBuffer = (KT == kQ4_0 && T == 1);
+template <int KT, int VT, int T>
+constexpr bool kDoubleBuffer = (KT == kQ4_0 && VT == kQ4_0 && T == 1);
 
-template <int KT, int T>
+template <int KT, int VT, int T>
 __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(DecodeParams p) {
   using F = Fmt<KT>;
+  using FV = Fmt<VT>;
   using C = Cols<T>;
   constexpr int R = C::R;
   constexpr int NT = C::NT;
   // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
-  constexpr int kWaveBytes = (kDoubleBuffer<KT, T> ? 2 : 1) * F::kVbuf + F::kKarea;
+  constexpr int kWaveBytes = (kDoubleBuffer<KT, VT, T> ? 2 : 1) * FV::kVbuf + F::kKarea;
   constexpr int kRed = 4 * R * kHeadDim * 4;
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
@@ -977,17 +984,17 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     if (tbl_fits)
       for (int i = tid; i < n_tbl; i += kThreads) tbl_lds[i] = p.bt[static_cast<size_t>(s) * p.bt_stride + pg.lp0 + i];
   }
-  if constexpr (kDoubleBuffer<KT, T>) {
+  if constexpr (kDoubleBuffer<KT, VT, T>) {
     // Registers hold the next tile's loads while the current one is worked
     // on, and PV runs one tile behind: while tile i is staged, its QK^T and
     // softmax computed, the PV of tile i-4 (this wave's previous) runs from
     // the other V buffer, giving the scheduler two independent streams.
     // The output is rescaled for tile i's base only after that PV.
-    uint8_t* wk = wl + 2 * F::kVbuf;
-    Tile<KT> ta, tb2;
+    uint8_t* wk = wl + 2 * FV::kVbuf;
+    Tile<KT, VT> ta, tb2;
     int ti = wave;
     const int my_total = (n_tiles - wave + 3) / 4;
-    if (ti < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
+    if (ti < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
@@ -997,50 +1004,50 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       f4 sacc[NT][2];
       int vb = 0;                         // V buffer of the current tile
       // first tile: no PV behind it yet
-      stage_tile<KT>(wl, wk, ta, k0 + 32 * ti, k1);
+      stage_tile<KT, VT>(wl, wk, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
-      qk_tile<KT, T>(ta, wk, qs, sacc);
-      softmax_tile<KT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl);
+      if (ti + 4 < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+      qk_tile<KT, VT, T>(ta, wk, qs, sacc);
+      softmax_tile<KT, VT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl);
       wave_lds_sync();
       ti += 4;
       vb = 1;
       while (ti < n_tiles) {
         set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
-        stage_tile<KT>(wl + vb * F::kVbuf, wk, tb2, k0 + 32 * ti, k1);
+        stage_tile<KT, VT>(wl + vb * FV::kVbuf, wk, tb2, k0 + 32 * ti, k1);
         wave_lds_sync();
-        if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
-        qk_with_pv<KT, T>(tb2, wk, qs, sacc, wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
-        if (softmax_tile<KT, T>(sacc, tb2, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
+        if (ti + 4 < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
+        qk_with_pv<KT, VT, T>(tb2, wk, qs, sacc, wl + (vb ^ 1) * FV::kVbuf, bh, bl, o);
+        if (softmax_tile<KT, VT, T>(sacc, tb2, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
           rescale<T>(o, alpha);
         wave_lds_sync();
         ti += 4;
         vb ^= 1;
         if (ti >= n_tiles) break;
         set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
-        stage_tile<KT>(wl + vb * F::kVbuf, wk, ta, k0 + 32 * ti, k1);
+        stage_tile<KT, VT>(wl + vb * FV::kVbuf, wk, ta, k0 + 32 * ti, k1);
         wave_lds_sync();
-        if (ti + 4 < n_tiles) load_tile<KT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
-        qk_with_pv<KT, T>(ta, wk, qs, sacc, wl + (vb ^ 1) * F::kVbuf, bh, bl, o);
-        if (softmax_tile<KT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
+        if (ti + 4 < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+        qk_with_pv<KT, VT, T>(ta, wk, qs, sacc, wl + (vb ^ 1) * FV::kVbuf, bh, bl, o);
+        if (softmax_tile<KT, VT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
           rescale<T>(o, alpha);
         wave_lds_sync();
         ti += 4;
         vb ^= 1;
       }
-      pv_tile<KT, T>(wl + (vb ^ 1) * F::kVbuf, bh, bl, o);   // the last tile's PV
+      pv_tile<VT, T>(wl + (vb ^ 1) * FV::kVbuf, bh, bl, o);   // the last tile's PV
     }
   } else {
-    uint8_t* wk = wl + F::kVbuf;
+    uint8_t* wk = wl + FV::kVbuf;
     build_q<KT, T>(p, s, h, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
     for (int ti = wave; ti < n_tiles; ti += 4) {
-      Tile<KT> tt;
-      load_tile<KT>(p, pg, s, h, k0 + 32 * ti, k0, k1, tt, bad);
-      stage_tile<KT>(wl, wk, tt, k0 + 32 * ti, k1);
+      Tile<KT, VT> tt;
+      load_tile<KT, VT>(p, pg, s, h, k0 + 32 * ti, k0, k1, tt, bad);
+      stage_tile<KT, VT>(wl, wk, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
-      compute_tile<KT, T>(tt, wl, wk, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
+      compute_tile<KT, VT, T>(tt, wl, wk, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
       wave_lds_sync();
     }
   }
@@ -1079,7 +1086,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[out_dim<KT>(mt, g, i)] = o[nt][mt][i] * a;
+        for (int i = 0; i < 4; ++i) dst[out_dim<VT>(mt, g, i)] = o[nt][mt][i] * a;
       }
     }
   }
@@ -1117,48 +1124,69 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   if (any_bad && tid == 0) atomicOr(p.err, 1u);
 }
 
-template <int KT>
-hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
+template <int KT, int VT>
+hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid(p.max_items), block(kThreads);
   switch (p.n_qtok) {
-    case 1: hipLaunchKernelGGL((split_mfma_kernel<KT, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((split_mfma_kernel<KT, 2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((split_mfma_kernel<KT, 3>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((split_mfma_kernel<KT, 4>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 3>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 4>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int KT, int T>
+template <int KT>
+hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
+  switch (p.v_type) {
+    case kF16: return launch_kvt<KT, kF16>(p, stream);
+    case kBF16: return launch_kvt<KT, kBF16>(p, stream);
+    case kQ8_0: return launch_kvt<KT, kQ8_0>(p, stream);
+    case kQ4_0: return launch_kvt<KT, kQ4_0>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int KT, int VT, int T>
 int wgs_per_cu() {
   static const int n = [] {
     int r = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, T>, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, VT, T>, kThreads, 0) != hipSuccess)
       r = 1;
     return r < 1 ? 1 : (r > 4 ? 4 : r);
   }();
   return n;
 }
 
-template <int KT>
-int wgs_kt(int T) {
+template <int KT, int VT>
+int wgs_kvt(int T) {
   switch (T) {
-    case 1: return wgs_per_cu<KT, 1>();
-    case 2: return wgs_per_cu<KT, 2>();
-    case 3: return wgs_per_cu<KT, 3>();
-    default: return wgs_per_cu<KT, 4>();
+    case 1: return wgs_per_cu<KT, VT, 1>();
+    case 2: return wgs_per_cu<KT, VT, 2>();
+    case 3: return wgs_per_cu<KT, VT, 3>();
+    default: return wgs_per_cu<KT, VT, 4>();
+  }
+}
+
+template <int KT>
+int wgs_kt(int v_type, int T) {
+  switch (v_type) {
+    case kF16: return wgs_kvt<KT, kF16>(T);
+    case kBF16: return wgs_kvt<KT, kBF16>(T);
+    case kQ8_0: return wgs_kvt<KT, kQ8_0>(T);
+    default: return wgs_kvt<KT, kQ4_0>(T);
   }
 }
 
 }  // namespace
 
-int split_mfma_wgs_per_cu(int k_type, int n_qtok) {
+int split_mfma_wgs_per_cu(int k_type, int v_type, int n_qtok) {
   switch (k_type) {
-    case kF16: return wgs_kt<kF16>(n_qtok);
-    case kBF16: return wgs_kt<kBF16>(n_qtok);
-    case kQ8_0: return wgs_kt<kQ8_0>(n_qtok);
-    default: return wgs_kt<kQ4_0>(n_qtok);
+    case kF16: return wgs_kt<kF16>(v_type, n_qtok);
+    case kBF16: return wgs_kt<kBF16>(v_type, n_qtok);
+    case kQ8_0: return wgs_kt<kQ8_0>(v_type, n_qtok);
+    default: return wgs_kt<kQ4_0>(v_type, n_qtok);
   }
 }
 

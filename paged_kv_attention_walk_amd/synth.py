@@ -238,6 +238,13 @@ def config3(seed=3, table="round_robin"):
                          RAGGED_LENS, 1, "q4_0", "q4_0", 16, table=table, seed=seed)
 
 
+def ragged_mixed(seed=3, k_kind="q8_0", v_kind="q4_0"):
+    """The ragged 131072 + 7 x 8192 step with K and V pools of different
+    encodings (Q8_0 K with Q4_0 V by default), same table and pages."""
+    return make_workload(f"{k_kind}k_{v_kind}v_ragged_128k_7x8k_p16_interleaved", RAGGED_LENS, 1, k_kind, v_kind, 16,
+                         table="round_robin", seed=seed)
+
+
 def config4(ctx=32768, n_qtok=1, seed=4):
     """One sequence, 1-4 query tokens with a causal mask among them, Q8_0 K/V,
     256-token shuffled pages."""

@@ -100,13 +100,17 @@ def test_pool_create_rejects_bad_descriptors():
     for kwargs, status in [(dict(n_blocks=0, page_size=16, kv="f16"), pb.ERR_INVALID),
                            (dict(n_blocks=4, page_size=24, kv="f16"), pb.ERR_UNSUPPORTED),
                            (dict(n_blocks=4, page_size=1024, kv="f16"), pb.ERR_UNSUPPORTED),
-                           (dict(n_blocks=4, page_size=16, kv=9), pb.ERR_INVALID),
-                           (dict(n_blocks=4, page_size=16, kv=pb.kv_type("q8_0", "q4_0")), pb.ERR_UNSUPPORTED)]:
+                           (dict(n_blocks=4, page_size=16, kv=9), pb.ERR_INVALID)]:
         with pytest.raises(pb.PaError) as e:
             pb.Pool(kwargs["n_blocks"], kwargs["page_size"], kwargs["kv"], host_only=True)
         assert e.value.status == status
     p = pb.Pool(4, 48, "bf16", host_only=True)                         # 48: non-power-of-two page
     assert p.info().page_size == 48
+    p.destroy()
+    p = pb.Pool(4, 16, pb.kv_type("q8_0", "q4_0"), host_only=True)     # K and V of different types
+    info = p.info()
+    assert (info.k_row_bytes, info.v_row_bytes) == (272, 144)
+    assert (info.k_page_bytes, info.v_page_bytes) == (4 * 16 * 272, 4 * 16 * 144)
     p.destroy()
 
 
@@ -120,7 +124,7 @@ def test_decode_host_checks_fail_before_device_work():
     assert st(n_qtok=5) == pb.ERR_INVALID
     assert st(n_seq=-1) == pb.ERR_INVALID
     assert st(kv=0x10000 | 4) == pb.ERR_INVALID
-    assert st(kv=pb.kv_type("q4_0", "f16")) == pb.ERR_UNSUPPORTED
+    assert st(kv=pb.kv_type("q4_0", "f16")) == pb.ERR_NOT_FOUND     # a mixed pair passes the type checks
     assert st(page_size=40) == pb.ERR_UNSUPPORTED
     assert st(q=a + 4) == pb.ERR_INVALID                  # misaligned
     assert st(k_pool=a + 8) == pb.ERR_INVALID

@@ -154,3 +154,41 @@ def test_lse_matches_oracle_and_merge_of_halves():
     parity(out, ref, what="lse case out")
     fin = np.isfinite(rlse)
     assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-4 * max(1.0, np.abs(rlse[fin]).max())
+
+
+MIXED = [(k, v) for k in KINDS for v in KINDS if k != v]
+
+
+@pytest.mark.parametrize("engine", ENGINES)
+@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("kv", MIXED, ids=lambda p: f"K{p[0]}-V{p[1]}")
+def test_mixed_types_parity(kv, T, engine):
+    # K and V pools of different encodings (every off-diagonal pair)
+    k, v = kv
+    lens = [0, 3, 64, 129, 1000, 2047]
+    w = synth.make_workload(f"mixed_{k}_{v}_{T}", lens, T, k, v, 48, table="shuffled", seed=61 + T)
+    log(f"[case] mixed K={k} V={v} T={T} P=48 lens={lens} {engine}")
+    out, lse, err = run(w, lse=True, engine=engine)
+    ref, rlse = _oracle(w)
+    assert err == 0
+    parity(out, ref, what=f"mixed K={k} V={v} T={T}")
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-3
+
+
+@pytest.mark.parametrize("kv", [("q8_0", "q4_0"), ("f16", "q4_0"), ("q4_0", "bf16")], ids=lambda p: f"K{p[0]}-V{p[1]}")
+@pytest.mark.parametrize("P", [16, 256])
+def test_mixed_paged_equals_contiguous_bitwise(kv, P):
+    k, v = kv
+    lens = [3 * P + 5, P, 7 * P - 2]
+    w = synth.make_workload(f"mpc_{k}_{v}_{P}", lens, 1, k, v, P, table="shuffled", seed=70 + P)
+    log(f"[case] mixed paged==contiguous K={k} V={v} P={P}")
+    cap = w["block_table"].shape[1] * P
+    kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], lens, cap)
+    vc = synth.contiguous_from_table(w["v_pool"], w["block_table"], lens, cap)
+    a, al, _ = run(w, lse=True)
+    b, bl, _ = run(w, contiguous=True, kc=kc, vc=vc, lse=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(al.view(np.uint32), bl.view(np.uint32))
+    parity(a, _oracle(w)[0], what=f"mixed pc K={k} V={v} P={P}")

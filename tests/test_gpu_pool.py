@@ -144,3 +144,26 @@ def test_rotate_every_page_between_steps():
         w2.update(k_pool=k, v_pool=v, block_table=bt)
         got, _, _ = run(synth.Workload(w2))
         assert np.array_equal(got.view(np.uint32), base.view(np.uint32)), rep
+
+
+def test_append_scatter_mixed_types_bitexact():
+    # K and V pools of different encodings: each row lands with its own size
+    P, nb = 16, 6
+    kv = pb.kv_type("q8_0", "q4_0")
+    rbk, rbv = synth.ROW_BYTES["q8_0"], synth.ROW_BYTES["q4_0"]
+    log("[case] append scatter K=q8_0 V=q4_0")
+    kp = torch.zeros((nb, 4, P, rbk), dtype=torch.uint8, device="cuda")
+    vp = torch.zeros((nb, 4, P, rbv), dtype=torch.uint8, device="cuda")
+    pool = pb.Pool(nb, P, kv, k_pool=kp, v_pool=vp, max_append_rows=5)
+    _, idx = pool.alloc(4)
+    rng = np.random.default_rng(9)
+    n = 23
+    blocks = rng.choice(idx, size=n).astype(np.int32)
+    slots = rng.integers(0, P, size=n).astype(np.int32)
+    krows = rng.integers(0, 256, size=(n, 4, rbk), dtype=np.uint8)
+    vrows = rng.integers(0, 256, size=(n, 4, rbv), dtype=np.uint8)
+    assert pool.append_kv(blocks, slots, krows, vrows) == pb.OK
+    torch.cuda.synchronize()
+    assert np.array_equal(kp.cpu().numpy(), pool_model.scatter_rows(np.zeros((nb, 4, P, rbk), np.uint8), blocks, slots, krows))
+    assert np.array_equal(vp.cpu().numpy(), pool_model.scatter_rows(np.zeros((nb, 4, P, rbv), np.uint8), blocks, slots, vrows))
+    pool.destroy()
