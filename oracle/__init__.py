@@ -31,6 +31,8 @@ Source pages cited throughout (title, then the section used):
 Modules:
 
 * ``quant``       -- decoding of F16 / BF16 / Q8_0 / Q4_0 rows to float64.
+* ``encode``      -- encoding of float32 rows into those four formats (the
+                     quantiser of a device-side append).
 * ``attention``   -- block-table gather, plain causal GQA softmax attention,
                      the log-sum-exp merge of chunk partials.
 * ``pool_model``  -- byte-level model of the paged pool (row addresses,
@@ -42,7 +44,7 @@ itself (values printed on the pages, closed forms, a library routine, brute
 force on tiny inputs, invariants).  the design doc lists each pin.
 """
 
-from . import quant, attention, pool_model, alloc_model  # noqa: F401
+from . import quant, encode, attention, pool_model, alloc_model  # noqa: F401
 
 # Names of the four K/V encodings the pages list (lucebox#555, Summary, for
 # F16 / Q4_0 / Q8_0; TensorFold#1156, Summary, for bf16 K/V).

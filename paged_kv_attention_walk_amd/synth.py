@@ -46,6 +46,9 @@ def normal(shape, seed, scale=1.0, dtype=np.float32) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def _round_half_away(x: np.ndarray) -> np.ndarray:
+    # in float64, where |x| + 0.5 is exact for float32 x (in float32 it can
+    # round up to the next integer just below a half)
+    x = np.asarray(x, dtype=np.float64)
     return np.sign(x) * np.floor(np.abs(x) + 0.5)
 
 

@@ -188,3 +188,150 @@ def check_paged_equals_contiguous(paged_decode, contiguous_decode, pages=(16, 48
             a, al = paged_decode(w["q"], w["k_pool"], w["v_pool"], kind, kind, w["block_table"], lens, 1 / 16)
             b, bl = contiguous_decode(w["q"], kc, vc, kind, kind, lens, 1 / 16)
             assert np.array_equal(a, b) and np.array_equal(al, bl), f"paged != contiguous (P={P}, {kind})"
+
+
+# ---------------------------------------------------------------- encoding
+#
+# Each check takes ``enc(x, kind)``: float32 [..., 256] -> encoded rows.
+
+def _row_of_blocks(blocks):
+    """A 256-value float32 row from up to 8 blocks of 32 (the rest zero)."""
+    row = np.zeros(256, np.float32)
+    for b, v in enumerate(blocks):
+        row[32 * b:32 * b + 32] = v
+    return row
+
+
+def q4_fields(row_bytes):
+    """(scale, 32 codes) of each block of a Q4_0 row, read byte by byte: the
+    fp16 scale first, then byte j = code j | code j+16 << 4."""
+    out = []
+    for b in range(8):
+        blk = row_bytes[18 * b:18 * b + 18]
+        d = float(np.frombuffer(bytes(blk[0:2]), "<f2")[0])
+        out.append((d, [int(blk[2 + j]) & 15 for j in range(16)] + [int(blk[2 + j]) >> 4 for j in range(16)]))
+    return out
+
+
+def q8_fields(row_bytes):
+    """(scale, 32 codes) of each block of a Q8_0 row."""
+    out = []
+    for b in range(8):
+        blk = row_bytes[34 * b:34 * b + 34]
+        d = float(np.frombuffer(bytes(blk[0:2]), "<f2")[0])
+        out.append((d, [int(c) for c in np.frombuffer(bytes(blk[2:]), np.int8)]))
+    return out
+
+
+def _one_block(enc, kind, blk):
+    fields = q4_fields if kind == "q4_0" else q8_fields
+    return fields(enc(_row_of_blocks([blk])[None], kind)[0])[0]
+
+
+def check_encode_closed_forms(enc):
+    """Blocks built from codes: Q4_0 values (c-8) 2^e with a code 0 present
+    (max|x| = 8 2^e, so d = 2^e exactly), Q8_0 values c 2^e with |c| = 127
+    present; the encoder must return exactly those scales and codes."""
+    for e in (-14, -5, 0, 3, 12):
+        rng = np.random.default_rng(e + 100)
+        blocks = []
+        for _ in range(8):
+            c = rng.integers(0, 16, size=32)
+            c[rng.integers(0, 32)] = 0
+            blocks.append(c)
+        row = _row_of_blocks([(c - 8).astype(np.float32) * np.float32(2.0 ** e) for c in blocks])
+        for (d, codes), c in zip(q4_fields(enc(row[None], "q4_0")[0]), blocks):
+            assert d == 2.0 ** e and codes == [int(v) for v in c]
+    for e in (-17, -7, 0, 4, 8):
+        rng = np.random.default_rng(e + 200)
+        blocks = []
+        for _ in range(8):
+            c = rng.integers(-127, 128, size=32)
+            c[rng.integers(0, 32)] = rng.choice([-127, 127])
+            blocks.append(c)
+        row = _row_of_blocks([c.astype(np.float32) * np.float32(2.0 ** e) for c in blocks])
+        for (d, codes), c in zip(q8_fields(enc(row[None], "q8_0")[0]), blocks):
+            assert d == 2.0 ** e and codes == [int(v) for v in c]
+
+
+def check_encode_clip_and_zero(enc):
+    """Q4_0: a block whose max|x| is a positive value maps it to 16 steps,
+    stored as 15; blocks of zeros store scale 0 and codes 8 (Q4_0) / 0."""
+    blk = np.linspace(-3, 8, 32).astype(np.float32)
+    d, codes = _one_block(enc, "q4_0", blk)
+    assert d == 1.0 and codes[31] == 15 and codes[0] == 5
+    z = np.zeros((1, 256), np.float32)
+    q4, q8 = enc(z, "q4_0")[0], enc(z, "q8_0")[0]
+    for b in range(8):
+        assert q4[18 * b] == 0 and q4[18 * b + 1] == 0 and np.all(q4[18 * b + 2:18 * b + 18] == 0x88)
+        assert np.all(q8[34 * b:34 * b + 34] == 0)
+
+
+def check_encode_rounding(enc):
+    """Codes: halves away from zero; a float32 just below a half rounds down
+    (0.5 - 2^-25, whose float32 sum with 0.5 is 1); the step is the stored
+    fp16 scale; the product x r is a float32 operation."""
+    vals = np.array([2.5, -2.5, 0.5, -0.5, 1.4999999, -1.4999999, 126.5], np.float32)
+    blk = np.zeros(32, np.float32)
+    blk[:len(vals)], blk[31] = vals, 127.0
+    d, codes = _one_block(enc, "q8_0", blk)
+    assert d == 1.0 and codes[:len(vals)] == [3, -3, 1, -1, 1, -1, 127]
+    blk = np.zeros(32, np.float32)
+    blk[:4], blk[31] = [0.5, -0.5, 3.5, -7.5], -8.0
+    d, codes = _one_block(enc, "q4_0", blk)
+    assert d == 1.0 and codes[:4] == [9, 7, 12, 0] and codes[31] == 0
+    v = np.float32(0.5) - np.float32(2.0 ** -25)
+    assert v < 0.5 and np.float32(v + np.float32(0.5)) == 1.0
+    blk = np.zeros(32, np.float32)
+    blk[0], blk[1], blk[2], blk[31] = v, -v, 0.5, 127.0
+    d, codes = _one_block(enc, "q8_0", blk)
+    assert d == 1.0 and codes[:3] == [0, 0, 1]
+    # max 127.0127: d = 1.0001, stored as fp16 1.0; 2.50015 is 2.50015 stored
+    # steps (code 3) but 2.4999 unrounded ones
+    blk = np.zeros(32, np.float32)
+    blk[0], blk[31] = 2.50015, 127.0127
+    d, codes = _one_block(enc, "q8_0", blk)
+    assert d == 1.0 and codes[0] == 3 and codes[31] == 127
+    # d = 3 (max 381), r = float32(1/3): x = 7.5 - 2^-21 has x / 3 < 2.5 but
+    # float32(x r) == 2.5, so the code is 3
+    x = np.float32(7.5) - np.float32(2.0 ** -21)
+    assert float(x) / 3.0 < 2.5 and np.float32(x * (np.float32(1) / np.float32(3))) == np.float32(2.5)
+    blk = np.zeros(32, np.float32)
+    blk[0], blk[31] = x, 381.0
+    d, codes = _one_block(enc, "q8_0", blk)
+    assert d == 3.0 and codes[0] == 3
+
+
+def check_encode_scale_rounding(enc):
+    """max|x| / 127 is stored as the nearest fp16 (ties to even), subnormal
+    scales included; below half the smallest subnormal the scale is 0."""
+    for amax, d_want in [(127.0 * (1 + 2.0 ** -11), 1.0),
+                         (127.0 * (1 + 3 * 2.0 ** -11), 1 + 2.0 ** -9),
+                         (127.0 * 2.0 ** -24, 2.0 ** -24),
+                         (127.0 * 2.0 ** -26, 0.0)]:
+        blk = np.zeros(32, np.float32)
+        blk[5] = -amax
+        d, codes = _one_block(enc, "q8_0", blk)
+        assert d == d_want, (amax, d)
+        assert codes[5] == (max(-127, -round(amax / d_want)) if d_want else 0)
+
+
+def check_encode_two_byte_rounding(enc):
+    """F16 and BF16: nearest value, ties to even, overflow to infinity,
+    subnormals kept."""
+    vals = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65519.0, 65520.0, -2.0 ** -25, 2.0 ** -24], np.float32)
+    with np.errstate(over="ignore"):
+        f16 = enc(np.resize(vals, 256)[None], "f16")[0].view("<u2")[:len(vals)]
+    assert list(f16) == [0x3C00, 0x3C02, 0x7BFF, 0x7C00, 0x8000, 0x0001]
+    vals = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -7), 3.0e38, 1.0e-40], np.float32)
+    bf = enc(np.resize(vals, 256)[None], "bf16")[0].view("<u2")[:len(vals)]
+    assert list(bf) == [0x3F80, 0x3F82, 0xBF81, 0x7F62, 0x0001]
+    x = (np.random.default_rng(1).standard_normal(256).astype(np.float32).view(np.uint32)
+         & np.uint32(0xFFFF0000)).view(np.float32)
+    assert np.array_equal(enc(x[None], "bf16")[0].view("<u2"), (x.view(np.uint32) >> 16).astype(np.uint16))
+    assert np.all(enc(-np.zeros((1, 256), np.float32), "f16")[0][1::2] == 0x80)
+    assert np.all(enc(-np.zeros((1, 256), np.float32), "bf16")[0][1::2] == 0x80)
+
+
+ENCODE_CHECKS = (check_encode_closed_forms, check_encode_clip_and_zero, check_encode_rounding,
+                 check_encode_scale_rounding, check_encode_two_byte_rounding)

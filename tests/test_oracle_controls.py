@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention, pool_model, quant
+from oracle import attention, encode, pool_model, quant
 from oracle_checks import (check_against_brute_force, check_against_sdpa, check_closed_forms,
                            check_paged_equals_contiguous, check_scale_position, random_sequence_case)
 
@@ -162,3 +162,66 @@ def test_gather_mistake_is_caught():
                                           pages=(16,), kinds=("f16",))
     finally:
         pool_model.gather_rows = orig
+
+
+# ------------------------------------------------------------ row encoding
+
+def _planted_encoder(mistake):
+    """A copy of the block encoders with one planted mistake."""
+    def enc(x, kind):
+        if kind in ("f16", "bf16"):
+            x = np.asarray(x, np.float32)
+            if mistake == "bf16_truncate" and kind == "bf16":
+                b = (x.view(np.uint32) >> 16).astype("<u2")
+                return b.view(np.uint8).reshape(x.shape[:-1] + (512,))
+            return encode.encode(x, kind)
+        qmax = 127.0 if kind == "q8_0" else (7.0 if mistake == "q4_over_7" else 8.0)
+        x = np.asarray(x, np.float32)
+        blk = x.reshape(x.shape[:-1] + (8, 32))
+        amax = np.abs(blk).max(-1)
+        d16 = (amax / np.float32(qmax)).astype(np.float16)
+        dd = amax / np.float32(qmax) if mistake == "unrounded_scale" else d16.astype(np.float32)
+        r = np.where(dd != 0, np.float32(1) / np.where(dd != 0, dd, 1), 0).astype(np.float32)
+        if mistake == "f64_division":
+            v = blk.astype(np.float64) / np.where(dd != 0, dd, np.inf)[..., None].astype(np.float64)
+        else:
+            v = (blk * r[..., None]).astype(np.float32)
+        if mistake == "half_even":
+            c = np.rint(v)
+        elif mistake == "f32_floor":
+            c = np.sign(v) * np.floor(np.abs(v).astype(np.float32) + np.float32(0.5))
+        else:
+            c = encode.round_half_away(v)
+        out = np.empty(blk.shape[:-1] + ((34,) if kind == "q8_0" else (18,)), np.uint8)
+        out[..., 0:2] = d16.astype("<f2")[..., None].view(np.uint8)
+        if kind == "q8_0":
+            out[..., 2:] = np.clip(c, -127, 127).astype(np.int8).view(np.uint8)
+        else:
+            c = c + 8
+            c = (c.astype(np.int64) & 15) if mistake == "q4_no_clip" else np.clip(c, 0, 15).astype(np.int64)
+            c = c.astype(np.uint8)
+            lo, hi = (c[..., 16:], c[..., :16]) if mistake == "q4_nibbles_swapped" else (c[..., :16], c[..., 16:])
+            out[..., 2:] = lo | (hi << 4)
+        return out.reshape(x.shape[:-1] + (out.shape[-2] * out.shape[-1],))
+    return enc
+
+
+@pytest.mark.parametrize("mistake", ["bf16_truncate", "q4_over_7", "unrounded_scale", "f64_division",
+                                     "half_even", "f32_floor", "q4_no_clip", "q4_nibbles_swapped"])
+def test_encode_mistakes_fail_pins(mistake):
+    from oracle_checks import ENCODE_CHECKS
+    bad = _planted_encoder(mistake)
+    failed = []
+    for check in ENCODE_CHECKS:
+        try:
+            check(bad)
+        except AssertionError:
+            failed.append(check.__name__)
+    assert failed, f"planted mistake {mistake!r} passed every encoder pin"
+
+
+def test_planted_encoder_without_mistake_passes():
+    # the harness of the controls is sound: with no mistake every pin passes
+    from oracle_checks import ENCODE_CHECKS
+    for check in ENCODE_CHECKS:
+        check(_planted_encoder(None))
