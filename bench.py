@@ -1,6 +1,6 @@
 """Benchmark of one paged decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ragged|uniform|f16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ragged|uniform|mtp|f16|serving|...]
 
 A step is one pa_decode call -- plan, block-table walk, K/V stream, dequant,
 QK^T, online softmax, PV, chunk epilogue, LSE merge -- over the ragged
@@ -31,10 +31,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ragged", choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16"],
+    ap.add_argument("--workload", default="ragged",
+                    choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16", "serving"],
                     help="ragged: 131072 + 7 x 8192 Q4_0 (the headline); ragged_q8k_q4v: same with Q8_0 K and Q4_0 V; "
                          "uniform: 8 x 4096 Q4_0; mtp: one 131072-position Q8_0 sequence, --qtok query tokens; "
-                         "f16: one 1024-position F16 sequence")
+                         "f16: one 1024-position F16 sequence; serving: 128 BF16 streams of 512..8192 positions in "
+                         "64-position pages, each step a device append of one float32 K/V row per stream "
+                         "(encoded to BF16 into its page) followed by the decode")
     ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
     ap.add_argument("--no-contiguous", action="store_true")
@@ -84,6 +87,10 @@ def load_traffic(workload_name):
     return d.get("traffic_bytes_per_launch")
 
 
+def synth_row_bytes(kind):
+    return {"f16": 512, "bf16": 512, "q8_0": 272, "q4_0": 144}[kind]
+
+
 def cpu_baseline(w, seconds):
     """The float64 oracle, as it stands, on a bounded sample of the workload:
     one 8192-position sequence of it (all 24 query heads), repeated for about
@@ -96,7 +103,7 @@ def cpu_baseline(w, seconds):
     bt = w["block_table"][s:s + 1]
     lens = w["seq_lens"][s:s + 1]
     q = w["q"][s:s + 1]
-    per = L * 4 * (144 if w["k_kind"] == "q4_0" else 512) * 2
+    per = L * 4 * (synth_row_bytes(w["k_kind"]) + synth_row_bytes(w["v_kind"]))
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -135,6 +142,8 @@ def main():
         w = synth.config2()
     elif args.workload == "mtp":
         w = synth.config4(ctx=131072, n_qtok=args.qtok)
+    elif args.workload == "serving":
+        w = synth.config5()
     else:
         w = synth.config1()
     print(f"[bench] workload {w['name']} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -175,27 +184,56 @@ def main():
     lib = pb.lib()
     stream = torch.cuda.current_stream().cuda_stream
 
-    def make_call(kp, vp, bt, nb):
+    # serving: every step first appends one new float32 K/V row per stream at
+    # its last position (the row the decode then attends to), encoded on the
+    # device into the pool's encoding
+    serving = args.workload == "serving"
+    append = None
+    if serving:
+        last = w["seq_lens"].astype(np.int64) - 1
+        dst_block = torch.from_numpy(w["block_table"][np.arange(n_seq), last // P].astype(np.int32)).cuda()
+        dst_slot = torch.from_numpy((last % P).astype(np.int32)).cuda()
+        xk = torch.from_numpy(synth.normal((n_seq, 4, 256), seed=505)).cuda()
+        xv = torch.from_numpy(synth.normal((n_seq, 4, 256), seed=506)).cuda()
+        append_pools = [pb.Pool(nblocks, P, kv, k_pool=kp, v_pool=vp, max_seqs=1, max_blocks_per_seq=bt_stride)
+                        for kp, vp in pools]
+        append = {"rows": n_seq, "src": "f32", "keep": (dst_block, dst_slot, xk, xv)}
+
+    def make_call(kp, vp, bt, nb, pool=None):
         """A step with every pointer and the ext struct prepared up front, so
-        that the timed loop is one ctypes call per step."""
+        that the timed loop is one ctypes call per step (two with an append)."""
         ext = pb.make_ext(bt_stride, nb, w["scale"], None, ws, ws.numel() * 4)
         ext_ref = ctypes.byref(ext)
         a = (dq.data_ptr(), kp.data_ptr(), vp.data_ptr(), bt.data_ptr() if bt is not None else None,
              dlens.data_ptr(), n_seq, T, kv, P, out.data_ptr(), stream)
+        ap = None
+        if pool is not None:
+            ap = (pool._h, n_seq, dst_block.data_ptr(), dst_slot.data_ptr(), xk.data_ptr(), xv.data_ptr(), pb.F32,
+                  ws.data_ptr(), stream)
 
         def f(events):
+            if ap is not None:
+                st = lib.pa_append_kv_device(*ap)
+                if st != pb.OK:
+                    raise pb.PaError(st, "pa_append_kv_device")
             ext.split_events[0], ext.split_events[1] = (events if events else (None, None))
             st = lib.pa_decode(*a, ext_ref)
             if st != pb.OK:
                 raise pb.PaError(st, "pa_decode")
-        f.keep = (ext, kp, vp, bt)
+        f.keep = (ext, kp, vp, bt, pool)
         return f
 
-    def paged_call(r):
-        return make_call(pools[r][0], pools[r][1], bts[r], nblocks)
+    def paged_call(r, with_append=True):
+        return make_call(pools[r][0], pools[r][1], bts[r], nblocks,
+                         append_pools[r] if (serving and with_append) else None)
 
     cold_ms, cold_k, cold_k_med = timed([paged_call(r) for r in range(reps)], args.steps, args.warmup)
     hot_ms, hot_k, _ = timed([paged_call(0)], args.steps, args.warmup)
+    decode_only_ms = None
+    if serving:
+        decode_only_ms, _, _ = timed([paged_call(r, False) for r in range(reps)], args.steps, args.warmup)
+        append["ms_per_step_decode_only"] = round(decode_only_ms, 4)
+        append["append_ms_est"] = round(cold_ms - decode_only_ms, 4)
     err = pb.device_error(ws)
     if err:
         raise RuntimeError(f"device error word {err}")
@@ -204,8 +242,12 @@ def main():
     contig = None
     if not args.no_contiguous:
         max_len = bt_stride * P
-        kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], w["seq_lens"], max_len)
-        vc = synth.contiguous_from_table(w["v_pool"], w["block_table"], w["seq_lens"], max_len)
+        # with appends, the pools now hold the appended rows: copy those
+        hk = k0.cpu().numpy() if serving else w["k_pool"]
+        hv = v0.cpu().numpy() if serving else w["v_pool"]
+        kc = synth.contiguous_from_table(hk, w["block_table"], w["seq_lens"], max_len)
+        vc = synth.contiguous_from_table(hv, w["block_table"], w["seq_lens"], max_len)
+        del hk, hv
         creps = max(1, min(reps, int(np.ceil(2 * 2 * 256e6 / (kc.nbytes + vc.nbytes)))))
         kc0 = torch.from_numpy(kc).cuda()
         vc0 = torch.from_numpy(vc).cuda()
@@ -235,13 +277,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w["name"], "n_seq": n_seq, "seq_lens": "131072+7x8192" if args.workload.startswith("ragged")
-                   else ",".join(str(int(x)) for x in w["seq_lens"]), "n_qtok": T, "kv": w["k_kind"],
+        "config": {"workload": w["name"], "n_seq": n_seq,
+                   "seq_lens": ("131072+7x8192" if args.workload.startswith("ragged") else
+                                "U{512..8192}+1" if serving else ",".join(str(int(x)) for x in w["seq_lens"])),
+                   "n_qtok": T, "kv": w["k_kind"] if w["k_kind"] == w["v_kind"] else f"K {w['k_kind']} V {w['v_kind']}",
                    "page_size": P, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "kv_bytes": int(kv_bytes)},
         "attention_step_ms": round(cold_ms, 4),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "paged_over_contiguous": (round(contig["ms_per_step"] / cold_ms, 4) if contig else None),
+        # the contiguous step has no append: compare it with the decode alone
+        "paged_over_contiguous": (round(contig["ms_per_step"] / (decode_only_ms or cold_ms), 4) if contig else None),
         "contiguous": contig,
+        "append": append and {k: v for k, v in append.items() if k != "keep"},
         "hot": {"ms_per_step": round(hot_ms, 4), "split_kernel_ms": round(hot_k, 4),
                 "gbps": round(kv_bytes / (hot_ms * 1e-3) / 1e9, 2)},
         "replicas": reps,

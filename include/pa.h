@@ -74,6 +74,9 @@ const char *pa_version(void);
  * nine F16/Q8_0/Q4_0 K x V combinations; llama.cpp pull 2 defaults to Q8_0
  * K with Q4_0 V). */
 enum { PA_F16 = 1, PA_BF16 = 2, PA_Q8_0 = 3, PA_Q4_0 = 4 };
+
+/* float32 values: a source type of pa_append_kv_device, not a pool encoding. */
+#define PA_F32 5
 #define PA_KV_TYPE(k, v) ((int32_t)((k) | ((v) << 8)))
 
 #define PA_HEAD_DIM   256
@@ -189,6 +192,41 @@ pa_status pa_append_kv(pa_pool *pool, int32_t n_rows, const int32_t *dst_block,
                        const int32_t *dst_slot, const void *k_rows, const void *v_rows,
                        hipStream_t stream);
 
+/* Device-side append with fused encoding (colibri pull 372, Summary: only
+ * the new rows move and a scatter kernel places them; here they are already
+ * on the device, as a K/V projection leaves them, and the kernel encodes
+ * them on the way, with no host staging and no separate pass over HBM).
+ *
+ * k_src, v_src  device [n_rows][4][256] values of src_type: PA_F32, PA_BF16
+ *               or PA_F16 (16-byte aligned).  They are encoded into the
+ *               pool's K and V encodings:
+ *                 F16 / BF16: the nearest value, ties to even;
+ *                 Q8_0 / Q4_0, per block of 32 (the Q8_0 and Q4_0 workload
+ *                 definitions: scale max|x|/127 resp. max|x|/8): the scale is
+ *                 max|x|/127 (/8) computed in float32 and stored as the
+ *                 nearest fp16; codes are round(x * r), r = 1/scale as
+ *                 stored, in float32, halves away from zero, Q8_0 clipped to
+ *                 [-127, 127], Q4_0 stored as code + 8 clipped to [0, 15] (a
+ *                 block's positive extreme, 8 steps, is stored as 7); a block
+ *                 of zeros stores scale 0.  Values must be finite.
+ * dst_block,
+ * dst_slot      device int32 [n_rows]: row i goes to page dst_block[i], slot
+ *               dst_slot[i], for all 4 KV heads (the page holding position L
+ *               and slot L % page_size for a sequence of committed length L).
+ *               A destination outside [0, n_blocks) x [0, page_size) is
+ *               skipped and PA_DEVERR_APPEND is ORed into the error word;
+ *               whether a page is allocated is not known on the device and
+ *               is the caller's to ensure.  Two rows with the same
+ *               destination leave unspecified bytes there.
+ * err_word      device int32, or NULL for the error word of the pool's own
+ *               workspace (read with pa_get_device_error(pool, NULL, ...)).
+ * stream        one kernel is enqueued; nothing is staged on the host.
+ * Errors: PA_ERR_INVALID (null pool or arrays with n_rows > 0, n_rows < 0,
+ * another src_type, misalignment, a host-only pool), PA_ERR_HIP. */
+pa_status pa_append_kv_device(pa_pool *pool, int32_t n_rows, const int32_t *dst_block,
+                              const int32_t *dst_slot, const void *k_src, const void *v_src,
+                              int32_t src_type, int32_t *err_word, hipStream_t stream);
+
 /* ------------------------------------------------------------------ decode */
 
 /* pa_decode_ext.flags: run the fp32 vector-ALU path instead of the matrix-core
@@ -198,6 +236,7 @@ pa_status pa_append_kv(pa_pool *pool, int32_t n_rows, const int32_t *dst_block,
 /* Device-side error bits, ORed into the workspace's error word. */
 #define PA_DEVERR_TABLE  1 /* a block-table entry outside [0, n_pool_blocks)         */
 #define PA_DEVERR_LENGTH 2 /* a seq_len < 0, or beyond the table row / contiguous rows */
+#define PA_DEVERR_APPEND 4 /* pa_append_kv_device: a destination outside the pool     */
 
 typedef struct pa_decode_ext {
     int32_t  bt_stride;      /* int32 entries per block-table row; in contiguous mode the

@@ -19,17 +19,20 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa_walk.so")
 
 F16, BF16, Q8_0, Q4_0 = 1, 2, 3, 4
+F32 = 5                                   # a source type of pa_append_kv_device only
+SRC_CODES = {"f32": F32, "bf16": BF16, "f16": F16}
 TYPE_CODES = {"f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0}
 ROW_BYTES = {F16: 512, BF16: 512, Q8_0: 272, Q4_0: 144}
 HEAD_DIM, N_Q_HEADS, N_KV_HEADS, MAX_QTOK = 256, 24, 4, 4
 
 OK, ERR_INVALID, ERR_NOMEM, ERR_STALE, ERR_UNSUPPORTED, ERR_HIP, ERR_NOT_FOUND = 0, -1, -2, -3, -4, -5, -6
-DEVERR_TABLE, DEVERR_LENGTH = 1, 2
+DEVERR_TABLE, DEVERR_LENGTH, DEVERR_APPEND = 1, 2, 4
 DECODE_VECTOR_REFERENCE = 1
 POOL_HOST_ONLY = 1
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "pa_pool_destroy",
-           "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_decode",
+           "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_append_kv_device",
+           "pa_decode",
            "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather")
 
 
@@ -89,6 +92,7 @@ def _lib():
             "pa_alloc_blocks": (I32, [P, I32, VP, VP]),
             "pa_free_blocks": (I32, [P, I32, VP]),
             "pa_append_kv": (I32, [P, I32, VP, VP, VP, VP, VP]),
+            "pa_append_kv_device": (I32, [P, I32, VP, VP, VP, VP, I32, VP, VP]),
             "pa_decode": (I32, [VP, VP, VP, VP, VP, I32, I32, I32, I32, VP, VP, ctypes.POINTER(DecodeExt)]),
             "pa_decode_workspace_size": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
             "pa_get_device_error": (I32, [P, VP, VP, I32, ctypes.POINTER(I32)]),
@@ -201,6 +205,19 @@ class Pool:
         k = np.ascontiguousarray(k_rows, dtype=np.uint8)
         v = np.ascontiguousarray(v_rows, dtype=np.uint8)
         return _lib().pa_append_kv(self._h, len(b), _ptr(b), _ptr(s), _ptr(k), _ptr(v), _stream(stream))
+
+    def append_kv_device_status(self, n_rows, blocks, slots, k_src, v_src, src_type, err_word=None,
+                                stream=None) -> int:
+        """pa_append_kv_device: device int32 ``blocks`` / ``slots`` and device
+        rows [n_rows][4][256] of ``src_type`` ("f32", "bf16", "f16" or a code)."""
+        st = SRC_CODES.get(src_type, src_type)
+        return _lib().pa_append_kv_device(self._h, int(n_rows), _ptr(blocks), _ptr(slots), _ptr(k_src),
+                                          _ptr(v_src), int(st), _ptr(err_word), _stream(stream))
+
+    def append_kv_device(self, blocks, slots, k_src, v_src, src_type="f32", err_word=None, stream=None):
+        n = int(blocks.shape[0])
+        _check(self.append_kv_device_status(n, blocks, slots, k_src, v_src, src_type, err_word, stream),
+               "pa_append_kv_device")
 
     def device_error(self, stream=None, clear=True) -> int:
         e = ctypes.c_int32()

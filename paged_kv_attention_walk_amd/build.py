@@ -54,10 +54,10 @@ def build(verbose: bool = True) -> str:
     o = os.path.join(BUILD_DIR, "pa_host.o")
     _run([cxx, *HOST_FLAGS, *inc, *hip_inc, "-c", os.path.join(CSRC, "pa_host.cpp"), "-o", o], verbose)
     objs.append(o)
-    # the two device sources compile in parallel (each instantiates every
+    # the device sources compile in parallel (two of them instantiate every
     # K type x V type x token count)
     cmds = []
-    for name in ("pa_kernels", "pa_mfma"):
+    for name in ("pa_kernels", "pa_mfma", "pa_append"):
         o = os.path.join(BUILD_DIR, name + ".o")
         cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)

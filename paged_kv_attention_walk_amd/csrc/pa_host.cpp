@@ -343,6 +343,38 @@ pa_status pa_append_kv(pa_pool* p, int32_t n_rows, const int32_t* dst_block, con
   return PA_OK;
 }
 
+pa_status pa_append_kv_device(pa_pool* p, int32_t n_rows, const int32_t* dst_block, const int32_t* dst_slot,
+                              const void* k_src, const void* v_src, int32_t src_type, int32_t* err_word,
+                              hipStream_t stream) {
+  if (!p || n_rows < 0) return PA_ERR_INVALID;
+  if (src_type != PA_F32 && src_type != PA_BF16 && src_type != PA_F16) return PA_ERR_INVALID;
+  if (n_rows == 0) return PA_OK;
+  if (!dst_block || !dst_slot || !k_src || !v_src) return PA_ERR_INVALID;
+  if (p->desc.flags & PA_POOL_HOST_ONLY) return PA_ERR_INVALID;
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(dst_block, 4) || !aligned(dst_slot, 4) ||
+      (err_word && !aligned(err_word, 4)))
+    return PA_ERR_INVALID;
+  uint32_t* err = err_word ? reinterpret_cast<uint32_t*>(err_word) : static_cast<uint32_t*>(p->workspace);
+  if (!err) return PA_ERR_INVALID;
+  DeviceGuard dg(p->desc.device);
+  if (!dg.ok) return PA_ERR_HIP;
+  pa::AppendLaunch l;
+  l.k_src = k_src;
+  l.v_src = v_src;
+  l.src_type = src_type;
+  l.k_pool = static_cast<uint8_t*>(p->desc.k_pool);
+  l.v_pool = static_cast<uint8_t*>(p->desc.v_pool);
+  l.k_type = p->k_type;
+  l.v_type = p->v_type;
+  l.dst_block = dst_block;
+  l.dst_slot = dst_slot;
+  l.err = err;
+  l.n_rows = n_rows;
+  l.n_blocks = p->desc.n_blocks;
+  l.page_size = p->desc.page_size;
+  return hip_status(pa::launch_append_encode(l, stream));
+}
+
 pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                     const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
                     float* out, hipStream_t stream, const pa_decode_ext* ext) {

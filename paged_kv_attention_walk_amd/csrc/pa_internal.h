@@ -19,6 +19,10 @@ constexpr int kChunkGranule = 64;           // chunk lengths are multiples of th
 
 enum KvType { kF16 = 1, kBF16 = 2, kQ8_0 = 3, kQ4_0 = 4 };
 
+// Value types of the source rows of a device-side append (PA_F32, PA_BF16,
+// PA_F16).
+enum SrcType { kSrcF16 = 1, kSrcBF16 = 2, kSrcF32 = 5 };
+
 inline int row_bytes_of(int t) {
   switch (t) {
     case kF16: case kBF16: return 512;
@@ -119,6 +123,24 @@ PA_HD inline size_t staging_bytes(int64_t n, int rb_k, int rb_v) {
 
 hipError_t launch_scatter(const uint8_t* staging, int32_t n_rows, uint8_t* k_pool, uint8_t* v_pool,
                           int32_t rb_k, int32_t rb_v, int32_t page_size, hipStream_t stream);
+
+// Device-side append with fused encoding: rows [n_rows][4][256] of src_type
+// values, encoded into the K and V pools' encodings and written at
+// (dst_block[i], dst_slot[i]).  All pointers are device pointers.
+struct AppendLaunch {
+  const void* k_src;
+  const void* v_src;
+  int32_t src_type;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int32_t k_type, v_type;
+  const int32_t* dst_block;
+  const int32_t* dst_slot;
+  uint32_t* err;            // PA_DEVERR_APPEND is ORed in for a skipped row
+  int32_t n_rows, n_blocks, page_size;
+};
+
+hipError_t launch_append_encode(const AppendLaunch& l, hipStream_t stream);
 
 hipError_t launch_gather(const uint8_t* pool, int32_t row_bytes, const int32_t* bt, int32_t bt_stride,
                          int32_t n_pool_blocks, int32_t seq, int32_t seq_len, int32_t page_size,

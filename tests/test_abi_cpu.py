@@ -22,7 +22,8 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "pa_decode" in names and "pa_append_kv" in names and len(names) >= 13
+    assert "pa_decode" in names and "pa_append_kv" in names and "pa_append_kv_device" in names
+    assert len(names) >= 14
     lib = pb.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -143,6 +144,23 @@ def test_append_host_checks():
     z = np.zeros((1, 4, 144), np.uint8)
     assert pool.append_kv([0], [0], z, z, stream=0) == pb.ERR_INVALID       # host-only pool
     pool.destroy()
+
+
+def test_append_device_host_checks():
+    pool = _host_pool(8)
+    a = 1 << 20
+    st = lambda **kw: pool.append_kv_device_status(**{**dict(n_rows=3, blocks=a, slots=a, k_src=a, v_src=a,
+                                                              src_type="f32", stream=0), **kw})
+    assert st(src_type=9) == pb.ERR_INVALID
+    assert st(src_type=pb.Q4_0) == pb.ERR_INVALID            # an encoding, not a source type
+    assert st(n_rows=-1) == pb.ERR_INVALID
+    assert st(n_rows=0) == pb.OK                             # nothing to do
+    assert st(blocks=None) == pb.ERR_INVALID
+    assert st() == pb.ERR_INVALID                            # host-only pool: no device memory
+    for src in ("f32", "bf16", "f16"):
+        assert st(src_type=src) == pb.ERR_INVALID
+    pool.destroy()
+    assert pb.lib().pa_append_kv_device(None, 1, a, a, a, a, pb.F32, None, None) == pb.ERR_INVALID
 
 
 def test_workspace_size_is_accepted_and_needed():
