@@ -5,8 +5,9 @@
  * The method (Luce-Org/lucebox pull 555, "feat(qwen35): add paged-attention
  * monolithic decode-only AR foundation", Summary): decode attention with head
  * size 256 and grouped queries -- 24 query heads over 4 KV heads, so one KV
- * head serves 6 query heads -- for 1 to 4 new query tokens per sequence, with
- * K and V stored as F16, BF16, Q8_0 or Q4_0 rows in fixed-size pages that a
+ * head serves 6 query heads -- for 1 to 4 new query tokens per sequence
+ * (and, as achyudh/llama.cpp pull 2 extends its decode kernel to verify
+ * batches of up to 8 query tokens, for 5 to 8 as well), with K and V stored as F16, BF16, Q8_0 or Q4_0 rows in fixed-size pages that a
  * per-sequence block table scatters through one pool.  Each sequence's
  * context is split into chunks; every chunk produces a normalised partial
  * output and its log-sum-exp, and a stable merge combines them.
@@ -82,7 +83,7 @@ enum { PA_F16 = 1, PA_BF16 = 2, PA_Q8_0 = 3, PA_Q4_0 = 4 };
 #define PA_HEAD_DIM   256
 #define PA_N_Q_HEADS  24
 #define PA_N_KV_HEADS 4
-#define PA_MAX_QTOK   4
+#define PA_MAX_QTOK   8
 
 /* Bytes of one row of encoding t (0 for an unknown t). */
 size_t pa_row_bytes(int32_t t);
@@ -133,7 +134,7 @@ typedef struct pa_pool_info {
 /* Creates a pool and its block allocator; all blocks start free.  With NULL
  * k_pool / v_pool the library allocates them (hipMalloc, not zeroed).  Unless
  * the pool is host-only it also allocates a decode workspace sized for
- * max_seqs sequences of up to 4 query tokens, pinned and device staging for
+ * max_seqs sequences of up to 8 query tokens, pinned and device staging for
  * pa_append_kv, and registers k_pool so that pa_decode can find the pool from
  * the pointer.  Errors: PA_ERR_INVALID (null out/desc, n_blocks < 1, bad
  * head count / head_dim, a K/V pointer already registered), PA_ERR_UNSUPPORTED
@@ -271,7 +272,7 @@ typedef struct pa_decode_ext {
  * seq_lens device int32 [n_seq]: stored rows of each sequence, including the
  *          n_qtok new tokens.  New token t sits at position
  *          seq_len - n_qtok + t and attends to positions 0..seq_len-n_qtok+t.
- * n_seq    >= 0 (0 is a no-op).   n_qtok  1..4.
+ * n_seq    >= 0 (0 is a no-op).   n_qtok  1..8 (PA_MAX_QTOK).
  * kv_type  PA_KV_TYPE(k, v), matching the pool.   page_size: as the pool.
  * out      device float [n_seq][n_qtok][24][256]; query head h reads KV head
  *          h / 6.  A row with no visible key is 0.  All rows of a sequence
@@ -290,7 +291,7 @@ typedef struct pa_decode_ext {
  * work items, whose count and chunk sizes depend only on seq_lens, n_qtok and
  * the device's compute-unit count (so paged and contiguous storage give
  * bitwise-equal outputs), and a merge kernel for sequences split in several
- * chunks.  Errors: PA_ERR_INVALID (null pointers, n_qtok outside 1..4,
+ * chunks.  Errors: PA_ERR_INVALID (null pointers, n_qtok outside 1..8,
  * misaligned K/V (16 bytes) or q/out (16 bytes), workspace too small,
  * page_size or kv_type different from the pool's), PA_ERR_UNSUPPORTED,
  * PA_ERR_NOT_FOUND (ext NULL and k_pool not a pool), PA_ERR_HIP. */
@@ -299,11 +300,11 @@ pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
                     int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
                     float *out, hipStream_t stream, const pa_decode_ext *ext);
 
-/* Bytes of decode workspace for n_seq sequences of up to 4 tokens on `device`
- * (reserved up front, as llama.cpp pull 2 does for its split partials in the
- * commit that moved them out of run-time pool allocations).  n_qtok is
- * checked (1..4) but the size covers 4 tokens, so one workspace serves every
- * n_qtok. */
+/* Bytes of decode workspace for n_seq sequences of n_qtok (1..8) tokens on
+ * `device` (reserved up front, as llama.cpp pull 2 does for its split
+ * partials in the commit that moved them out of run-time pool allocations).
+ * A workspace of this size also serves every call of n_seq or fewer
+ * sequences with n_qtok or fewer tokens. */
 pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t *bytes);
 
 /* Reads the error word of a workspace after the work on `stream` finishes

@@ -23,7 +23,7 @@ F32 = 5                                   # a source type of pa_append_kv_device
 SRC_CODES = {"f32": F32, "bf16": BF16, "f16": F16}
 TYPE_CODES = {"f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0}
 ROW_BYTES = {F16: 512, BF16: 512, Q8_0: 272, Q4_0: 144}
-HEAD_DIM, N_Q_HEADS, N_KV_HEADS, MAX_QTOK = 256, 24, 4, 4
+HEAD_DIM, N_Q_HEADS, N_KV_HEADS, MAX_QTOK = 256, 24, 4, 8
 
 OK, ERR_INVALID, ERR_NOMEM, ERR_STALE, ERR_UNSUPPORTED, ERR_HIP, ERR_NOT_FOUND = 0, -1, -2, -3, -4, -5, -6
 DEVERR_TABLE, DEVERR_LENGTH, DEVERR_APPEND = 1, 2, 4

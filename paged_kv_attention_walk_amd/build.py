@@ -26,6 +26,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+MAX_QTOK = 8   # query tokens per sequence (one split-kernel object per count)
 
 
 def _run(cmd, verbose):
@@ -54,14 +55,21 @@ def build(verbose: bool = True) -> str:
     o = os.path.join(BUILD_DIR, "pa_host.o")
     _run([cxx, *HOST_FLAGS, *inc, *hip_inc, "-c", os.path.join(CSRC, "pa_host.cpp"), "-o", o], verbose)
     objs.append(o)
-    # the device sources compile in parallel (two of them instantiate every
-    # K type x V type x token count)
+    # the device sources compile in parallel; the two split-kernel sources
+    # are built once per query-token count (each instantiates every K x V
+    # encoding pair for its count)
     cmds = []
-    for name in ("pa_kernels", "pa_mfma", "pa_append"):
+    for name in ("pa_kernels", "pa_append"):
         o = os.path.join(BUILD_DIR, name + ".o")
         cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    for name in ("pa_mfma", "pa_valu"):
+        for t in range(1, MAX_QTOK + 1):
+            o = os.path.join(BUILD_DIR, f"{name}_t{t}.o")
+            cmds.append([hipcc, *HIP_FLAGS, *inc, f"-DPA_T={t}", "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
+            objs.append(o)
+    workers = max(1, min(len(cmds), os.cpu_count() or 8))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB + ".tmp"

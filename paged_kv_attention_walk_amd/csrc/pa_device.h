@@ -320,8 +320,8 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   if (nc <= 1) return;                                   // written by the split kernel
   const int base = plan_prefix(p.seq_lens, s, cap, chunk, sh.sum);
   const size_t item0 = static_cast<size_t>(base) * kKvHeads + h;   // chunk c at item0 + c * 4
-  const float* base_o = p.part_o + (item0 * kRowsPerItem + r) * kHeadDim + 4 * lane;
-  const size_t cstride = static_cast<size_t>(kKvHeads) * kRowsPerItem * kHeadDim;   // floats between chunks
+  const float* base_o = p.part_o + (item0 * R + r) * kHeadDim + 4 * lane;
+  const size_t cstride = static_cast<size_t>(kKvHeads) * R * kHeadDim;   // floats between chunks
   // the first chunk outputs of this wave go out now, before the weights
   float4 early[kEarly];
 #pragma unroll
@@ -334,7 +334,7 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   float mx = kNegInf;
   bool nan = false;
   for (int c = tid; c < nc; c += kThreads) {
-    const float x = p.part_lse[(item0 + static_cast<size_t>(c) * kKvHeads) * kRowsPerItem + r];
+    const float x = p.part_lse[(item0 + static_cast<size_t>(c) * kKvHeads) * R + r];
     sh.w[c] = x;
     nan |= (x != x);
     mx = fmaxf(mx, x);

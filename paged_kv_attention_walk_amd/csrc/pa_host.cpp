@@ -148,7 +148,7 @@ size_t pa_row_bytes(int32_t t) { return static_cast<size_t>(pa::row_bytes_of(t))
 
 pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
   if (!bytes || n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_QTOK) return PA_ERR_INVALID;
-  *bytes = pa::workspace_layout(n_seq, target_items(device)).total;
+  *bytes = pa::workspace_layout(n_seq, target_items(device), n_qtok).total;
   return PA_OK;
 }
 
@@ -198,7 +198,7 @@ pa_status pa_pool_create(const pa_pool_desc* d, pa_pool** out) {
     p->own_v = st == PA_OK;
   }
   if (st == PA_OK) {
-    const pa::WorkspaceLayout wl = pa::workspace_layout(p->desc.max_seqs, target_items(d->device));
+    const pa::WorkspaceLayout wl = pa::workspace_layout(p->desc.max_seqs, target_items(d->device), PA_MAX_QTOK);
     p->workspace_bytes = wl.total;
     st = hip_status(hipMalloc(&p->workspace, p->workspace_bytes));
     if (st == PA_OK) st = hip_status(hipMemset(p->workspace, 0, wl.lse_off));   // error word
@@ -443,7 +443,7 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   if (static_cast<int64_t>(bt_stride) * page_size > (1ll << 30)) return PA_ERR_INVALID;
   const int target = target_items(device);
   if (!ws || !aligned(ws, 256)) return PA_ERR_INVALID;
-  const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes);
+  const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes, n_qtok);
   const int64_t items = pa::max_work_items(n_seq, target);
   if (wl.items < items) return PA_ERR_INVALID;
   if (items > (1ll << 31) - 1) return PA_ERR_UNSUPPORTED;

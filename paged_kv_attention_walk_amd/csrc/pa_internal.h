@@ -14,7 +14,7 @@ constexpr int kHeadDim = 256;
 constexpr int kQHeads = 24;
 constexpr int kKvHeads = 4;
 constexpr int kGroup = kQHeads / kKvHeads;  // query heads per KV head
-constexpr int kMaxQtok = 4;
+constexpr int kMaxQtok = 8;
 constexpr int kChunkGranule = 64;           // chunk lengths are multiples of this
 
 enum KvType { kF16 = 1, kBF16 = 2, kQ8_0 = 3, kQ4_0 = 4 };
@@ -73,7 +73,6 @@ inline int64_t plan_target(int64_t n_seq, int64_t slots, int64_t cap) {
 // Resident workgroups per compute unit of the split kernel a call selects
 // (from the runtime's occupancy query; at least 1).
 int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine);
-int split_mfma_wgs_per_cu(int k_type, int v_type, int n_qtok);
 
 struct WorkspaceLayout {
   int64_t items;       // work-item capacity
@@ -82,36 +81,58 @@ struct WorkspaceLayout {
 
 PA_HD inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr int kRowsPerItem = 6 * kMaxQtok;   // partial rows reserved per work item
+// Partial rows of one work item: the 6 query heads x n_qtok tokens.
+PA_HD constexpr int rows_per_item(int n_qtok) { return 6 * n_qtok; }
 
-// Workspace: [0, 256) header (error word at 0); chunk log-sum-exps; chunk
-// outputs.  The layout depends only on the item capacity, never on the call's
-// n_seq or n_qtok, so one workspace serves calls of any shape it has room
-// for.  The error word must be zero before the first call.
-inline WorkspaceLayout workspace_layout_items(int64_t items) {
+// Workspace: [0, 256) header (error word at 0); chunk log-sum-exps
+// [items][6 n_qtok]; chunk outputs [items][6 n_qtok][256].  The layout
+// depends on the call's n_qtok and the item capacity only, so a workspace
+// sized for n_qtok tokens also serves every call of fewer tokens (more items
+// fit).  The error word must be zero before the first call.
+inline WorkspaceLayout workspace_layout_items(int64_t items, int n_qtok) {
+  const size_t rows = static_cast<size_t>(rows_per_item(n_qtok));
   WorkspaceLayout w;
   w.items = items;
   w.lse_off = 256;
-  w.o_off = align_up(w.lse_off + static_cast<size_t>(items) * kRowsPerItem * sizeof(float), 256);
-  w.total = align_up(w.o_off + static_cast<size_t>(items) * kRowsPerItem * kHeadDim * sizeof(float), 256);
+  w.o_off = align_up(w.lse_off + static_cast<size_t>(items) * rows * sizeof(float), 256);
+  w.total = align_up(w.o_off + static_cast<size_t>(items) * rows * kHeadDim * sizeof(float), 256);
   return w;
 }
 
-inline WorkspaceLayout workspace_layout(int64_t n_seq, int64_t target_items) {
-  return workspace_layout_items(max_work_items(n_seq, target_items));
+inline WorkspaceLayout workspace_layout(int64_t n_seq, int64_t target_items, int n_qtok) {
+  return workspace_layout_items(max_work_items(n_seq, target_items), n_qtok);
 }
 
-// The largest item capacity whose layout fits in `bytes`.
-inline WorkspaceLayout workspace_layout_for_bytes(size_t bytes) {
-  const size_t per = kRowsPerItem * sizeof(float) * (1 + kHeadDim);
+// The largest item capacity whose layout for n_qtok tokens fits in `bytes`.
+inline WorkspaceLayout workspace_layout_for_bytes(size_t bytes, int n_qtok) {
+  const size_t per = rows_per_item(n_qtok) * sizeof(float) * (1 + kHeadDim);
   int64_t items = static_cast<int64_t>(bytes / per) + 1;   // an upper bound; step down to the largest fit
-  while (items > 0 && workspace_layout_items(items).total > bytes) --items;
-  return workspace_layout_items(items);
+  while (items > 0 && workspace_layout_items(items, n_qtok).total > bytes) --items;
+  return workspace_layout_items(items, n_qtok);
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin,
                          hipEvent_t ev_end);
-hipError_t launch_split_mfma(const DecodeParams& p, hipStream_t stream);
+
+// Split kernels for n_qtok = T: each T is its own translation unit (the
+// matrix-core and vector sources are built once per T with -DPA_T=T), so
+// the instantiations of all K x V encodings compile in parallel.
+template <int T> hipError_t launch_split_mfma_t(const DecodeParams& p, hipStream_t stream);
+template <int T> int split_mfma_wgs_t(int k_type, int v_type);
+template <int T> hipError_t launch_split_valu_t(const DecodeParams& p, hipStream_t stream);
+#define PA_DECLARE_SPLIT_T(T)                                                            \
+  template <> hipError_t launch_split_mfma_t<T>(const DecodeParams& p, hipStream_t stream); \
+  template <> int split_mfma_wgs_t<T>(int k_type, int v_type);                             \
+  template <> hipError_t launch_split_valu_t<T>(const DecodeParams& p, hipStream_t stream);
+PA_DECLARE_SPLIT_T(1)
+PA_DECLARE_SPLIT_T(2)
+PA_DECLARE_SPLIT_T(3)
+PA_DECLARE_SPLIT_T(4)
+PA_DECLARE_SPLIT_T(5)
+PA_DECLARE_SPLIT_T(6)
+PA_DECLARE_SPLIT_T(7)
+PA_DECLARE_SPLIT_T(8)
+#undef PA_DECLARE_SPLIT_T
 
 // Staging layout for append: int32 block[n], int32 slot[n], then (16-byte
 // aligned) K rows [n][4][rb_k], then V rows [n][4][rb_v].

@@ -26,12 +26,20 @@
 //    per 16 dims (F16 / BF16); the per-key V scale is folded into the
 //    probabilities, P' = p * d_v, split hi + lo like q.
 // Accumulation is fp32 throughout.
+//
+// This source is built once per query-token count T (-DPA_T=T, 1..8): the
+// 6T query rows of a KV head take ceil(6T/16) B tiles of 16 columns (one
+// token packs hi and lo parts into one tile).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "pa_device.h"
 #include "pa_internal.h"
+
+#ifndef PA_T
+#error "build with -DPA_T=<query tokens>"
+#endif
 
 namespace pa {
 namespace {
@@ -910,7 +918,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int NT = C::NT;
   // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
   constexpr int kWaveBytes = (kDoubleBuffer<KT, VT, T> ? 2 : 1) * FV::kVbuf + F::kKarea;
-  constexpr int kRed = 4 * R * kHeadDim * 4;
+  constexpr int kRed = 4 * 16 * kHeadDim * 4;         // the combine, one B tile of rows at a time
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
@@ -1073,52 +1081,54 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   }
   if (lane == 0) sh_bad[wave] = __ballot(bad) ? 1 : 0;
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);       // [4 waves][R][256]
+  float* red = reinterpret_cast<float*>(lds);       // [4 waves][16 rows][256], one B tile at a time
+  const bool any_bad = (sh_bad[0] | sh_bad[1] | sh_bad[2] | sh_bad[3]) != 0;
+  const float nan = __builtin_nanf("");
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    if (nt > 0) __syncthreads();                     // the previous tile's rows have been read
     const int r = 16 * nt + n;
     if (r < R) {
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
       const float a = (m_run[nt] == kNegInf) ? 0.f : exp2f(m_run[nt] - M);
-      float* dst = red + (wave * R + r) * kHeadDim;
+      float* dst = red + (wave * 16 + n) * kHeadDim;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[out_dim<VT>(mt, g, i)] = o[nt][mt][i] * a;
       }
     }
-  }
-  __syncthreads();
-  const bool any_bad = (sh_bad[0] | sh_bad[1] | sh_bad[2] | sh_bad[3]) != 0;
-  const float nan = __builtin_nanf("");
-  for (int r = 0; r < R; ++r) {
-    const int t = r / 6, gq = r % 6;
-    float M = kNegInf;
+    __syncthreads();
+    const int r_end = min(R, 16 * nt + 16);
+    for (int rr = 16 * nt; rr < r_end; ++rr) {
+      const int t = rr / 6, gq = rr % 6, j = rr - 16 * nt;
+      float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
-    float ltot = 0.f;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][rr][0]);
+      float ltot = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = ml_lds[w][r][0];
-      ltot += (mw == kNegInf) ? 0.f : ml_lds[w][r][1] * exp2f(mw - M);
-    }
-    const float sum = red[(0 * R + r) * kHeadDim + tid] + red[(1 * R + r) * kHeadDim + tid] +
-                      red[(2 * R + r) * kHeadDim + tid] + red[(3 * R + r) * kHeadDim + tid];
-    float val = ltot > 0.f ? sum / ltot : 0.f;
-    float lse2 = ltot > 0.f ? M + __log2f(ltot) : kNegInf;
-    if (any_bad) {
-      val = nan;
-      lse2 = nan;
-    }
-    if (nc == 1) {
-      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + tid] = val;
-      if (p.lse_out && tid == 0)
-        p.lse_out[(static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq] = lse2 * kLn2;
-    } else {
-      p.part_o[(item * kRowsPerItem + r) * kHeadDim + tid] = val;
-      if (tid == 0) p.part_lse[item * kRowsPerItem + r] = lse2;
+      for (int w = 0; w < 4; ++w) {
+        const float mw = ml_lds[w][rr][0];
+        ltot += (mw == kNegInf) ? 0.f : ml_lds[w][rr][1] * exp2f(mw - M);
+      }
+      const float sum = red[(0 * 16 + j) * kHeadDim + tid] + red[(1 * 16 + j) * kHeadDim + tid] +
+                        red[(2 * 16 + j) * kHeadDim + tid] + red[(3 * 16 + j) * kHeadDim + tid];
+      float val = ltot > 0.f ? sum / ltot : 0.f;
+      float lse2 = ltot > 0.f ? M + __log2f(ltot) : kNegInf;
+      if (any_bad) {
+        val = nan;
+        lse2 = nan;
+      }
+      if (nc == 1) {
+        p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + tid] = val;
+        if (p.lse_out && tid == 0)
+          p.lse_out[(static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq] = lse2 * kLn2;
+      } else {
+        p.part_o[(item * R + rr) * kHeadDim + tid] = val;
+        if (tid == 0) p.part_lse[item * R + rr] = lse2;
+      }
     }
   }
   if (any_bad && tid == 0) atomicOr(p.err, 1u);
@@ -1126,14 +1136,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 
 template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.max_items), block(kThreads);
-  switch (p.n_qtok) {
-    case 1: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 3>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((split_mfma_kernel<KT, VT, 4>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  hipLaunchKernelGGL((split_mfma_kernel<KT, VT, PA_T>), dim3(p.max_items), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1148,49 +1151,42 @@ hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
   }
 }
 
-template <int KT, int VT, int T>
+// Resident workgroups per compute unit (the runtime's occupancy query).
+template <int KT, int VT>
 int wgs_per_cu() {
   static const int n = [] {
     int r = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, VT, T>, kThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, VT, PA_T>, kThreads, 0) != hipSuccess)
       r = 1;
     return r < 1 ? 1 : (r > 4 ? 4 : r);
   }();
   return n;
 }
 
-template <int KT, int VT>
-int wgs_kvt(int T) {
-  switch (T) {
-    case 1: return wgs_per_cu<KT, VT, 1>();
-    case 2: return wgs_per_cu<KT, VT, 2>();
-    case 3: return wgs_per_cu<KT, VT, 3>();
-    default: return wgs_per_cu<KT, VT, 4>();
-  }
-}
-
 template <int KT>
-int wgs_kt(int v_type, int T) {
+int wgs_kt(int v_type) {
   switch (v_type) {
-    case kF16: return wgs_kvt<KT, kF16>(T);
-    case kBF16: return wgs_kvt<KT, kBF16>(T);
-    case kQ8_0: return wgs_kvt<KT, kQ8_0>(T);
-    default: return wgs_kvt<KT, kQ4_0>(T);
+    case kF16: return wgs_per_cu<KT, kF16>();
+    case kBF16: return wgs_per_cu<KT, kBF16>();
+    case kQ8_0: return wgs_per_cu<KT, kQ8_0>();
+    default: return wgs_per_cu<KT, kQ4_0>();
   }
 }
 
 }  // namespace
 
-int split_mfma_wgs_per_cu(int k_type, int v_type, int n_qtok) {
+template <>
+int split_mfma_wgs_t<PA_T>(int k_type, int v_type) {
   switch (k_type) {
-    case kF16: return wgs_kt<kF16>(v_type, n_qtok);
-    case kBF16: return wgs_kt<kBF16>(v_type, n_qtok);
-    case kQ8_0: return wgs_kt<kQ8_0>(v_type, n_qtok);
-    default: return wgs_kt<kQ4_0>(v_type, n_qtok);
+    case kF16: return wgs_kt<kF16>(v_type);
+    case kBF16: return wgs_kt<kBF16>(v_type);
+    case kQ8_0: return wgs_kt<kQ8_0>(v_type);
+    default: return wgs_kt<kQ4_0>(v_type);
   }
 }
 
-hipError_t launch_split_mfma(const DecodeParams& p, hipStream_t stream) {
+template <>
+hipError_t launch_split_mfma_t<PA_T>(const DecodeParams& p, hipStream_t stream) {
   switch (p.k_type) {
     case kF16: return launch_kt<kF16>(p, stream);
     case kBF16: return launch_kt<kBF16>(p, stream);

@@ -178,7 +178,7 @@ def check_paged_equals_contiguous(paged_decode, contiguous_decode, pages=(16, 48
     for P in pages:
         for kind in kinds:
             lens = [int(x) for x in rng.integers(1, 3 * P, size=3)] + [0]
-            T = int(rng.integers(1, 5))
+            T = int(rng.integers(1, 9))
             w = synth.make_workload("t", lens, T, kind, kind, P, table="shuffled",
                                     seed=int(rng.integers(1 << 30)), n_blocks=sum(
                                         synth.blocks_needed(L, P) for L in lens) + 3)

@@ -122,7 +122,8 @@ def test_decode_host_checks_fail_before_device_work():
     st = lambda **kw: pb.decode_status(**{**dict(q=a, k_pool=a, v_pool=a, block_table=a, seq_lens=a, n_seq=1,
                                                   n_qtok=1, kv=kvq4, page_size=16, out=a, stream=0), **kw})
     assert st(n_qtok=0) == pb.ERR_INVALID
-    assert st(n_qtok=5) == pb.ERR_INVALID
+    assert st(n_qtok=9) == pb.ERR_INVALID
+    assert st(n_qtok=8) == pb.ERR_NOT_FOUND               # 8 tokens pass the checks
     assert st(n_seq=-1) == pb.ERR_INVALID
     assert st(kv=0x10000 | 4) == pb.ERR_INVALID
     assert st(kv=pb.kv_type("q4_0", "f16")) == pb.ERR_NOT_FOUND     # a mixed pair passes the type checks
@@ -165,17 +166,22 @@ def test_append_device_host_checks():
 
 def test_workspace_size_is_accepted_and_needed():
     # pa_decode must accept a workspace of exactly pa_decode_workspace_size()
-    # bytes for every n_seq / n_qtok, and refuse one a work item (24,672 bytes)
-    # smaller.  On a
+    # bytes for every n_seq / n_qtok, and refuse one a work item (6 n_qtok
+    # rows of 257 floats) smaller; a workspace sized for 8 tokens serves every
+    # n_qtok.  On a
     # machine without a GPU a call that passes every host check fails at the
     # launch with PA_ERR_HIP, never with PA_ERR_INVALID.
     a = 1 << 20
     for n_seq in list(range(1, 70)) + [127, 128, 129, 500, 512, 1000]:
-        for T in (1, 4):
+        for T in (1, 4, 5, 8):
             n = pb.workspace_size(n_seq, T, 0)
             ok = pb.make_ext(8, 64, 0.0, None, 1 << 30, n)
             st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q8_0"), 16, a, 0, ok)
             assert st != pb.ERR_INVALID, (n_seq, T, n)
-            small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 24672)
+            small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 6 * T * 257 * 4)
             st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q8_0"), 16, a, 0, small)
             assert st == pb.ERR_INVALID, (n_seq, T, n)
+        big = pb.make_ext(8, 64, 0.0, None, 1 << 30, pb.workspace_size(n_seq, 8, 0))
+        for T in range(1, 9):
+            st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q4_0"), 16, a, 0, big)
+            assert st != pb.ERR_INVALID, (n_seq, T)

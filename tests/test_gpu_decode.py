@@ -37,7 +37,7 @@ def test_config1_parity(engine):
 
 @pytest.mark.parametrize("engine", ENGINES)
 @pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_small_ragged_parity(kind, T, engine):
     # several chunks per sequence (the plan's granule is 64 keys), ragged
     # tails, empty and shorter-than-T sequences, pages of 48 positions
@@ -81,7 +81,7 @@ def test_value_magnitudes(kind, mag, engine):
 def test_paged_equals_contiguous_bitwise(P, engine):
     lens = [5 * P + 3, 2 * P, 1, 9 * P - 1]
     for kind in ("q4_0", "bf16", "q8_0", "f16"):
-        T = 1 + (P // 16) % 4
+        T = {16: 2, 48: 5, 128: 8, 256: 3, 512: 6}[P]
         w = synth.make_workload(f"pc_{kind}_{P}", lens, T, kind, kind, P, table="shuffled", seed=P)
         log(f"[case] paged==contiguous {kind} P={P} T={T} {engine}")
         kc = synth.contiguous_from_table(w["k_pool"], w["block_table"], lens, w["block_table"].shape[1] * P)
@@ -160,7 +160,7 @@ MIXED = [(k, v) for k in KINDS for v in KINDS if k != v]
 
 
 @pytest.mark.parametrize("engine", ENGINES)
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 7])
 @pytest.mark.parametrize("kv", MIXED, ids=lambda p: f"K{p[0]}-V{p[1]}")
 def test_mixed_types_parity(kv, T, engine):
     # K and V pools of different encodings (every off-diagonal pair)

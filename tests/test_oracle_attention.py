@@ -14,7 +14,7 @@ def _decoded_cases(seed, n, lens=(1, 2, 5, 17, 40), kinds=("f16", "bf16", "q8_0"
     out = []
     for i in range(n):
         L = int(lens[i % len(lens)])
-        T = 1 + i % 4
+        T = 1 + i % 8
         kind = kinds[i % len(kinds)]
         scale = [1 / 16, 1.0, 0.37][i % 3]
         q, kb, vb = random_sequence_case(rng, L, T, kind, kind)
@@ -99,9 +99,10 @@ def test_gqa_identical_queries_identical_outputs():
     assert not np.array_equal(out[:, 0], out[:, 6])
 
 
-def test_causal_decomposition():
+@pytest.mark.parametrize("T", [4, 8])
+def test_causal_decomposition(T):
     rng = np.random.default_rng(8)
-    L, T = 45, 4
+    L = 45
     q, kb, vb = random_sequence_case(rng, L, T, "bf16", "bf16")
     k, v = quant.decode(kb, "bf16"), quant.decode(vb, "bf16")
     out, lse = attention.decode_sequence(q, k, v, L, 1 / 16)
@@ -121,6 +122,14 @@ def test_empty_and_short_sequences():
     # L = 2, T = 4: tokens 0 and 1 see no key; token 2 sees key 0; token 3 keys 0..1
     assert np.all(out[1, :2] == 0) and np.all(np.isneginf(lse[1, :2]))
     assert np.all(np.isfinite(lse[1, 2:])) and np.all(np.isfinite(lse[2]))
+    # eight tokens over five stored rows: tokens 0..2 see nothing, token 3 key 0
+    w = synth.make_workload("e8", [5], 8, "q8_0", "q8_0", 16, seed=10)
+    out, lse = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q8_0", "q8_0",
+                                      w["block_table"], w["seq_lens"])
+    assert np.all(out[0, :3] == 0) and np.all(np.isneginf(lse[0, :3])) and np.all(np.isfinite(lse[0, 3:]))
+    v0 = quant.decode(pool_model.gather_rows(w["v_pool"], w["block_table"][0], 1), "q8_0")[:, 0]
+    for h in range(24):
+        assert np.array_equal(out[0, 3, h], v0[h // 6])          # a single visible key returns its V row
 
 
 def test_corrupt_table_gives_nan_for_that_sequence_only():
@@ -165,7 +174,7 @@ def test_planted_high_score_key_dominates():
 def test_split_merge_equals_single_pass_quick(seed):
     rng = np.random.default_rng(100 + seed)
     L = int(rng.integers(1, 90))
-    T = int(rng.integers(1, 5))
+    T = int(rng.integers(1, 9))
     q, kb, vb = random_sequence_case(rng, L, T, "q4_0", "q8_0")
     k, v = quant.decode(kb, "q4_0"), quant.decode(vb, "q8_0")
     cuts = sorted(set([0, L] + [int(x) for x in rng.integers(0, L + 1, size=3)]))
