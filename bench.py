@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention-step ms, effective K/V GB/s (% HBM peak), paged÷contiguous ratio"
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # dense fp16 / bf16 matrix peak
 SPLIT_KERNEL = "split_mfma_kernel"
 
 
@@ -32,13 +33,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ragged",
-                    choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16", "serving"],
+                    choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16", "serving", "prefill"],
                     help="ragged: 131072 + 7 x 8192 Q4_0 (the headline); ragged_q8k_q4v: same with Q8_0 K and Q4_0 V; "
                          "uniform: 8 x 4096 Q4_0; mtp: one 131072-position Q8_0 sequence, --qtok query tokens; "
                          "f16: one 1024-position F16 sequence; serving: 128 BF16 streams of 512..8192 positions in "
                          "64-position pages, each step a device append of one float32 K/V row per stream "
-                         "(encoded to BF16 into its page) followed by the decode")
-    ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp")
+                         "(encoded to BF16 into its page) followed by the decode; prefill: one --ctx-position "
+                         "sequence, Q8_0 K and Q4_0 V, whose last --qtok positions are the new tokens (pa_prefill)")
+    ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp / prefill")
+    ap.add_argument("--ctx", type=int, default=16384, help="context for --workload prefill")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,6 +147,8 @@ def main():
         w = synth.config4(ctx=131072, n_qtok=args.qtok)
     elif args.workload == "serving":
         w = synth.config5()
+    elif args.workload == "prefill":
+        w = synth.prefill_workload(ctx=args.ctx, n_qtok=args.qtok)
     else:
         w = synth.config1()
     print(f"[bench] workload {w['name']} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -159,7 +164,8 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
     bts = [torch.from_numpy(w["block_table"]).cuda() for _ in range(reps)]
     out = torch.empty((n_seq, T, 24, 256), device="cuda")
-    nbytes = pb.workspace_size(n_seq, T, 0)
+    prefill = args.workload == "prefill"
+    nbytes = pb.prefill_workspace_size(n_seq, T, 0) if prefill else pb.workspace_size(n_seq, T, 0)
     ws = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda")
     bt_stride = w["block_table"].shape[1]
     nblocks = w["k_pool"].shape[0]
@@ -211,15 +217,17 @@ def main():
             ap = (pool._h, n_seq, dst_block.data_ptr(), dst_slot.data_ptr(), xk.data_ptr(), xv.data_ptr(), pb.F32,
                   ws.data_ptr(), stream)
 
+        entry = lib.pa_prefill if prefill else lib.pa_decode
+
         def f(events):
             if ap is not None:
                 st = lib.pa_append_kv_device(*ap)
                 if st != pb.OK:
                     raise pb.PaError(st, "pa_append_kv_device")
             ext.split_events[0], ext.split_events[1] = (events if events else (None, None))
-            st = lib.pa_decode(*a, ext_ref)
+            st = entry(*a, ext_ref)
             if st != pb.OK:
-                raise pb.PaError(st, "pa_decode")
+                raise pb.PaError(st, "pa_prefill" if prefill else "pa_decode")
         f.keep = (ext, kp, vp, bt, pool)
         return f
 
@@ -264,6 +272,17 @@ def main():
 
     gbps = kv_bytes / (cold_ms * 1e-3) / 1e9
     achieved = kv_bytes / (cold_k * 1e-3) / 1e9
+    # algorithmic flops: QK^T and PV, 2 x 2 x 256 per (query row, visible key)
+    vis = sum(max(0, min(int(L), int(L) - T + t + 1)) for L in w["seq_lens"] for t in range(T))
+    flops = 4.0 * 256 * 24 * vis
+    roofline = {"kernel": SPLIT_KERNEL, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w["name"]),
+                "split_kernel_ms_mean": round(cold_k, 5), "split_kernel_ms_median": round(cold_k_med, 5)}
+    tflops = flops / (cold_k * 1e-3) / 1e12
+    if flops / kv_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):   # past the ridge point
+        roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                         "kv_gbps": round(achieved, 2), "algorithmic_flops": flops})
     line = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -280,6 +299,7 @@ def main():
         "config": {"workload": w["name"], "n_seq": n_seq,
                    "seq_lens": ("131072+7x8192" if args.workload.startswith("ragged") else
                                 "U{512..8192}+1" if serving else ",".join(str(int(x)) for x in w["seq_lens"])),
+                   "entry": "pa_prefill" if prefill else "pa_decode",
                    "n_qtok": T, "kv": w["k_kind"] if w["k_kind"] == w["v_kind"] else f"K {w['k_kind']} V {w['v_kind']}",
                    "page_size": P, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "kv_bytes": int(kv_bytes)},
         "attention_step_ms": round(cold_ms, 4),
@@ -291,10 +311,8 @@ def main():
         "hot": {"ms_per_step": round(hot_ms, 4), "split_kernel_ms": round(hot_k, 4),
                 "gbps": round(kv_bytes / (hot_ms * 1e-3) / 1e9, 2)},
         "replicas": reps,
-        "roofline": {"kernel": SPLIT_KERNEL, "bound": "hbm", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": load_traffic(w["name"]), "split_kernel_ms_mean": round(cold_k, 5),
-                     "split_kernel_ms_median": round(cold_k_med, 5)},
+        "roofline": roofline,
+        "split_tflops": round(tflops, 2),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -84,6 +84,7 @@ enum { PA_F16 = 1, PA_BF16 = 2, PA_Q8_0 = 3, PA_Q4_0 = 4 };
 #define PA_N_Q_HEADS  24
 #define PA_N_KV_HEADS 4
 #define PA_MAX_QTOK   8
+#define PA_MAX_PREFILL_TOKENS 65536
 
 /* Bytes of one row of encoding t (0 for an unknown t). */
 size_t pa_row_bytes(int32_t t);
@@ -306,6 +307,33 @@ pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
  * A workspace of this size also serves every call of n_seq or fewer
  * sequences with n_qtok or fewer tokens. */
 pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t *bytes);
+
+/* Paged chunked prefill: pa_decode for n_qtok = 1..PA_MAX_PREFILL_TOKENS new
+ * tokens per sequence (achyudh/llama.cpp pull 2: batches of more query tokens
+ * attend paged K/V chunk by chunk, each chunk writing its log-sum-exp, and the
+ * normalised parts are merged in f32; batches the large-tile kernel does not
+ * take run on the decode kernel's row tiles).  Arguments, layouts, causality
+ * (new token t at position seq_len - n_qtok + t sees positions up to it),
+ * masking, errors and the ext struct are those of pa_decode; q, out and
+ * lse_out hold n_qtok tokens per sequence, and the K/V rows of all n_qtok new
+ * tokens must already be in the pages (pa_append_kv / pa_append_kv_device).
+ *
+ * The tokens are taken in groups of 8 (48 query rows of a KV head per
+ * workgroup).  Work items are (sequence, KV head, context chunk, token
+ * group), the groups of one chunk run side by side so its K/V bytes are
+ * shared through the caches, and a group skips the keys past its last token.
+ * Chunk partials of every group are merged as in pa_decode.  The workspace
+ * (ext->workspace, or the pool's own when it is large enough) must hold
+ * pa_prefill_workspace_size() bytes.  Errors as pa_decode; n_qtok outside
+ * 1..PA_MAX_PREFILL_TOKENS gives PA_ERR_INVALID. */
+pa_status pa_prefill(const float *q, const void *k_pool, const void *v_pool,
+                     const int32_t *block_table, const int32_t *seq_lens,
+                     int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                     float *out, hipStream_t stream, const pa_decode_ext *ext);
+
+/* Bytes of workspace pa_prefill needs for n_seq sequences of n_qtok tokens on
+ * `device`. */
+pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t *bytes);
 
 /* Reads the error word of a workspace after the work on `stream` finishes
  * (this call waits for the stream) and, if clear != 0, zeroes it (enqueued on

@@ -33,7 +33,8 @@ POOL_HOST_ONLY = 1
 EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "pa_pool_destroy",
            "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_append_kv_device",
            "pa_decode",
-           "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather")
+           "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather", "pa_prefill",
+           "pa_prefill_workspace_size")
 
 
 def kv_type(k, v=0) -> int:
@@ -95,6 +96,8 @@ def _lib():
             "pa_append_kv_device": (I32, [P, I32, VP, VP, VP, VP, I32, VP, VP]),
             "pa_decode": (I32, [VP, VP, VP, VP, VP, I32, I32, I32, I32, VP, VP, ctypes.POINTER(DecodeExt)]),
             "pa_decode_workspace_size": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
+            "pa_prefill": (I32, [VP, VP, VP, VP, VP, I32, I32, I32, I32, VP, VP, ctypes.POINTER(DecodeExt)]),
+            "pa_prefill_workspace_size": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
             "pa_get_device_error": (I32, [P, VP, VP, I32, ctypes.POINTER(I32)]),
             "pa_debug_gather": (I32, [VP, I32, VP, I32, I32, I32, I32, I32, VP, VP, VP]),
         }
@@ -255,6 +258,21 @@ def decode_status(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv, p
     return _lib().pa_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
                             int(n_seq), int(n_qtok), kv if isinstance(kv, int) else kv_type(kv), int(page_size),
                             _ptr(out), _stream(stream), ctypes.byref(ext) if ext is not None else None)
+
+
+def prefill_status(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv, page_size, out,
+                   stream=None, ext: DecodeExt | None = None) -> int:
+    """pa_prefill; returns the status code."""
+    return _lib().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                             int(n_seq), int(n_qtok), kv if isinstance(kv, int) else kv_type(kv), int(page_size),
+                             _ptr(out), _stream(stream), ctypes.byref(ext) if ext is not None else None)
+
+
+def prefill_workspace_size(n_seq, n_qtok, device=0) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib().pa_prefill_workspace_size(int(n_seq), int(n_qtok), int(device), ctypes.byref(n)),
+           "pa_prefill_workspace_size")
+    return n.value
 
 
 def decode(q, k_pool, v_pool, block_table, seq_lens, n_qtok, kv, page_size, out, *, n_seq=None, stream=None,

@@ -305,13 +305,14 @@ __device__ inline float block_sum_f(float v, float* sh) {
   return (sh[4] + sh[5]) + (sh[6] + sh[7]);
 }
 
-template <int T>
-__device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
-  constexpr int R = 6 * T;
+__device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   constexpr int kEarly = 8;                              // chunk outputs per lane fetched before the weights
+  const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
   const int row_id = blockIdx.x;
   const int r = row_id % R;
   const int sh_id = row_id / R;
+  const int tg = r / 6, grp = tg / 8;                    // token, and its group of 8
+  const int lr = r - 48 * grp;                           // row within the group's partial rows
   const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
@@ -319,9 +320,10 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int nc = n_chunks_of(p.seq_lens[s], cap, chunk);
   if (nc <= 1) return;                                   // written by the split kernel
   const int base = plan_prefix(p.seq_lens, s, cap, chunk, sh.sum);
-  const size_t item0 = static_cast<size_t>(base) * kKvHeads + h;   // chunk c at item0 + c * 4
-  const float* base_o = p.part_o + (item0 * R + r) * kHeadDim + 4 * lane;
-  const size_t cstride = static_cast<size_t>(kKvHeads) * R * kHeadDim;   // floats between chunks
+  const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(base) * kKvHeads + h;
+  const size_t prows = static_cast<size_t>(p.part_rows);
+  const float* base_o = p.part_o + (item0 * prows + lr) * kHeadDim + 4 * lane;   // chunk c at item0 + 4c
+  const size_t cstride = static_cast<size_t>(kKvHeads) * prows * kHeadDim;     // floats between chunks
   // the first chunk outputs of this wave go out now, before the weights
   float4 early[kEarly];
 #pragma unroll
@@ -334,7 +336,7 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
   float mx = kNegInf;
   bool nan = false;
   for (int c = tid; c < nc; c += kThreads) {
-    const float x = p.part_lse[(item0 + static_cast<size_t>(c) * kKvHeads) * R + r];
+    const float x = p.part_lse[(item0 + static_cast<size_t>(c) * kKvHeads) * prows + lr];
     sh.w[c] = x;
     nan |= (x != x);
     mx = fmaxf(mx, x);
@@ -396,10 +398,10 @@ __device__ void merge_row(const DecodeParams& p, MergeShared& sh) {
       val = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
       lse2 = M + __log2f(ws);
     }
-    const int tt = r / 6, g = r % 6;
-    *reinterpret_cast<float4*>(p.out + ((static_cast<size_t>(s) * T + tt) * kQHeads + h * kGroup + g) * kHeadDim +
-                               4 * lane) = val;
-    if (p.lse_out && lane == 0) p.lse_out[(static_cast<size_t>(s) * T + tt) * kQHeads + h * kGroup + g] = lse2 * kLn2;
+    const int g = r % 6;
+    const size_t orow = static_cast<size_t>(s) * p.tok_total + tg;
+    *reinterpret_cast<float4*>(p.out + (orow * kQHeads + h * kGroup + g) * kHeadDim + 4 * lane) = val;
+    if (p.lse_out && lane == 0) p.lse_out[orow * kQHeads + h * kGroup + g] = lse2 * kLn2;
   }
 }
 

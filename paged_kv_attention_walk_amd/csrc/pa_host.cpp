@@ -148,7 +148,7 @@ size_t pa_row_bytes(int32_t t) { return static_cast<size_t>(pa::row_bytes_of(t))
 
 pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
   if (!bytes || n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_QTOK) return PA_ERR_INVALID;
-  *bytes = pa::workspace_layout(n_seq, target_items(device), n_qtok).total;
+  *bytes = pa::workspace_layout_items(pa::max_work_items(n_seq, target_items(device)), n_qtok).total;
   return PA_OK;
 }
 
@@ -375,10 +375,37 @@ pa_status pa_append_kv_device(pa_pool* p, int32_t n_rows, const int32_t* dst_blo
   return hip_status(pa::launch_append_encode(l, stream));
 }
 
-pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
-                    const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
-                    float* out, hipStream_t stream, const pa_decode_ext* ext) {
-  if (n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_QTOK) return PA_ERR_INVALID;
+namespace {
+
+constexpr int kGroupTokens = 8;   // query tokens of one prefill row tile
+
+int n_groups_of(int n_qtok) { return (n_qtok + kGroupTokens - 1) / kGroupTokens; }
+
+// Item target the workspace of a call is sized for: decode, the whole
+// target; prefill, the target shared among the token groups.
+int64_t sizing_target(int n_qtok, bool prefill, int device) {
+  const int64_t t = target_items(device);
+  if (!prefill) return t;
+  const int64_t g = n_groups_of(n_qtok);
+  return (t + g - 1) / g;
+}
+
+// Work items (of 6 n_qtok partial rows for decode, 48 for prefill) the
+// workspace must hold.
+int64_t workspace_items(int64_t n_seq, int n_qtok, bool prefill, int device) {
+  const int64_t per_group = pa::max_work_items(n_seq, sizing_target(n_qtok, prefill, device));
+  return prefill ? per_group * n_groups_of(n_qtok) : per_group;
+}
+
+int workspace_rows_tokens(int n_qtok, bool prefill) { return prefill ? kGroupTokens : n_qtok; }
+
+// Decode and prefill: one implementation, the prefill taking its query
+// tokens in groups of 8 (one token group per workgroup).
+pa_status attend(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                 const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                 float* out, hipStream_t stream, const pa_decode_ext* ext, bool prefill) {
+  const int max_tok = prefill ? PA_MAX_PREFILL_TOKENS : PA_MAX_QTOK;
+  if (n_seq < 0 || n_qtok < 1 || n_qtok > max_tok) return PA_ERR_INVALID;
   int kt = 0, vt = 0;
   const pa_status ts = parse_kv_type(kv_type, &kt, &vt);
   if (ts != PA_OK) return ts;
@@ -441,12 +468,13 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
     }
   }
   if (static_cast<int64_t>(bt_stride) * page_size > (1ll << 30)) return PA_ERR_INVALID;
-  const int target = target_items(device);
+  const int64_t target = sizing_target(n_qtok, prefill, device);
   if (!ws || !aligned(ws, 256)) return PA_ERR_INVALID;
-  const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes, n_qtok);
-  const int64_t items = pa::max_work_items(n_seq, target);
+  const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes, workspace_rows_tokens(n_qtok, prefill));
+  const int64_t items = workspace_items(n_seq, n_qtok, prefill, device);
   if (wl.items < items) return PA_ERR_INVALID;
-  if (items > (1ll << 31) - 1) return PA_ERR_UNSUPPORTED;
+  if (items > (1ll << 31) - 1 || static_cast<int64_t>(n_seq) * 24 * n_qtok > (1ll << 31) - 1)
+    return PA_ERR_UNSUPPORTED;
 
   pa::DecodeParams prm{};
   prm.q = q;
@@ -465,19 +493,50 @@ pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, cons
   prm.bt_stride = bt_stride;
   prm.page_size = page_size;
   prm.n_pool_blocks = block_table ? n_pool_blocks : 0;
-  // The plan aims at one round of resident workgroups; the workspace check
-  // above used the larger capacity target, so these items always fit.
+  // The plan aims at one round of resident workgroups (shared among the
+  // token groups of a prefill); the workspace check above used the larger
+  // capacity target, so these items always fit.
+  const int groups = prefill ? n_groups_of(n_qtok) : 1;
+  const int kernel_tok = n_qtok < kGroupTokens ? n_qtok : kGroupTokens;
   const int cu = cu_count(device);
-  const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, n_qtok, engine);
-  const int64_t plan = pa::plan_target(n_seq, slots, target);
+  const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, kernel_tok, engine);
+  const int64_t per_group_slots = slots / groups > 0 ? slots / groups : 1;
+  const int64_t plan = pa::plan_target(n_seq, per_group_slots, target);
   prm.target_items = static_cast<int32_t>(plan);
   prm.max_items = static_cast<int32_t>(pa::max_work_items(n_seq, plan));
+  prm.tok_total = n_qtok;
+  prm.tok0 = 0;
+  prm.n_groups = 1;
+  prm.part_rows = 6 * workspace_rows_tokens(n_qtok, prefill);
+  prm.part_items = prm.max_items;
   prm.k_type = kt;
   prm.v_type = vt;
   prm.engine = engine;
   const float sc = (scale == 0.f) ? 1.0f / 16.0f : scale;
   prm.scale_log2 = sc * 1.4426950408889634f;
   return hip_status(pa::launch_decode(prm, stream, ev0, ev1));
+}
+
+}  // namespace
+
+pa_status pa_decode(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                    const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                    float* out, hipStream_t stream, const pa_decode_ext* ext) {
+  return attend(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv_type, page_size, out, stream, ext,
+                false);
+}
+
+pa_status pa_prefill(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                     const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                     float* out, hipStream_t stream, const pa_decode_ext* ext) {
+  return attend(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv_type, page_size, out, stream, ext,
+                true);
+}
+
+pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
+  if (!bytes || n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_PREFILL_TOKENS) return PA_ERR_INVALID;
+  *bytes = pa::workspace_layout_items(workspace_items(n_seq, n_qtok, true, device), kGroupTokens).total;
+  return PA_OK;
 }
 
 pa_status pa_get_device_error(pa_pool* pool, void* workspace, hipStream_t stream, int32_t clear, int32_t* err) {

@@ -46,7 +46,15 @@ struct DecodeParams {
   uint32_t* err;           // error word
   int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
   int32_t target_items;    // item target of the chunk plan (plan_target)
-  int32_t max_items;       // work items the grid covers
+  int32_t max_items;       // work items of the plan the grid covers (per token group)
+  // Token groups: q / out / lse_out hold tok_total tokens per sequence; a
+  // launch covers n_groups groups of the kernel's token count starting at
+  // token tok0 (decode: one group, tok0 = 0, tok_total = n_qtok).  The grid is
+  // max_items x n_groups workgroups, the group index varying fastest.
+  int32_t tok_total, tok0, n_groups;
+  // Chunk partials of token group g (tokens 8g..) and plan item i start at
+  // row (g * part_items + i) * part_rows of part_o / part_lse.
+  int32_t part_rows, part_items;
   int32_t k_type, v_type;
   int32_t engine;          // 0: matrix-core path, 1: fp32 vector reference path
   float scale_log2;        // softmax scale * log2(e)

@@ -79,25 +79,14 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
 
 // ------------------------------------------------------------- dispatch
 
-template <int T>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   __shared__ MergeShared sh;
-  merge_row<T>(p, sh);
+  merge_row(p, sh);
 }
 
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.n_seq * kKvHeads * 6 * p.n_qtok), block(kThreads);
-  switch (p.n_qtok) {
-    case 1: hipLaunchKernelGGL((merge_kernel<1>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((merge_kernel<2>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((merge_kernel<3>), grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((merge_kernel<4>), grid, block, 0, stream, p); break;
-    case 5: hipLaunchKernelGGL((merge_kernel<5>), grid, block, 0, stream, p); break;
-    case 6: hipLaunchKernelGGL((merge_kernel<6>), grid, block, 0, stream, p); break;
-    case 7: hipLaunchKernelGGL((merge_kernel<7>), grid, block, 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((merge_kernel<8>), grid, block, 0, stream, p); break;
-    default: return hipErrorInvalidValue;
-  }
+  const dim3 grid(static_cast<unsigned>(p.n_seq) * kKvHeads * 6 * static_cast<unsigned>(p.tok_total)), block(kThreads);
+  hipLaunchKernelGGL(merge_kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -137,7 +126,28 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t e
   hipError_t e = hipSuccess;
   if (ev_begin) e = hipEventRecord(ev_begin, stream);
   if (e != hipSuccess) return e;
-  e = launch_split(p, stream);
+  if (p.tok_total <= kMaxQtok) {
+    DecodeParams a = p;
+    a.n_qtok = p.tok_total;
+    a.n_groups = 1;
+    a.tok0 = 0;
+    e = launch_split(a, stream);
+  } else {
+    // prefill: full groups of kMaxQtok tokens in one launch, the rest in another
+    const int full = p.tok_total / kMaxQtok, rest = p.tok_total % kMaxQtok;
+    DecodeParams a = p;
+    a.n_qtok = kMaxQtok;
+    a.n_groups = full;
+    a.tok0 = 0;
+    e = launch_split(a, stream);
+    if (e == hipSuccess && rest > 0) {
+      DecodeParams b = p;
+      b.n_qtok = rest;
+      b.n_groups = 1;
+      b.tok0 = full * kMaxQtok;
+      e = launch_split(b, stream);
+    }
+  }
   if (e != hipSuccess) return e;
   if (ev_end) e = hipEventRecord(ev_end, stream);
   if (e != hipSuccess) return e;

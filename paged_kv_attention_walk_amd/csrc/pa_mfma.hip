@@ -848,7 +848,7 @@ __device__ inline int out_dim(int mt, int g, int i) {
 // hi part of row n, lane n + 8 the lo part (one tile, one part).  More
 // tokens: hi and lo in separate parts.  Wave w builds blocks 2w and 2w+1.
 template <int KT, int T>
-__device__ inline void build_q(const DecodeParams& p, int s, int h, int wave, uint8_t* q_lds) {
+__device__ inline void build_q(const DecodeParams& p, int s, int h, int tok0, int wave, uint8_t* q_lds) {
   using C = Cols<T>;
   constexpr int R = C::R;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
@@ -856,8 +856,8 @@ __device__ inline void build_q(const DecodeParams& p, int s, int h, int wave, ui
   for (int nt = 0; nt < C::NT; ++nt) {
     const int r = C::kPack ? (n & 7) : 16 * nt + n;
     const bool live = r < R;
-    const float* qrow = p.q + ((static_cast<size_t>(s) * T + (live ? r / 6 : 0)) * kQHeads + h * kGroup +
-                               (live ? r % 6 : 0)) * kHeadDim;
+    const float* qrow = p.q + ((static_cast<size_t>(s) * p.tok_total + tok0 + (live ? r / 6 : 0)) * kQHeads +
+                               h * kGroup + (live ? r % 6 : 0)) * kHeadDim;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int b = 2 * wave + bb;
@@ -934,37 +934,45 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   const int n = lane & 15, g = lane >> 4;
   const int cap = p.bt_stride * p.page_size;
   const int chunk = __builtin_amdgcn_readfirstlane(plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum));
-  const int jj = blockIdx.x / kKvHeads, h = blockIdx.x % kKvHeads;
+  // token group fastest: the groups of one chunk run side by side
+  const int grp = blockIdx.x % p.n_groups;
+  const int item_id = blockIdx.x / p.n_groups;
+  const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
+  const int jj = item_id / kKvHeads, h = item_id % kKvHeads;
   plan_locate(p.seq_lens, p.n_seq, cap, chunk, jj, sh_loc);
   // every value that places loads is wave-uniform (scalar registers)
   const int s = __builtin_amdgcn_readfirstlane(sh_loc[0]), c = __builtin_amdgcn_readfirstlane(sh_loc[1]);
   if (s < 0) return;
   const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
   const int nc = n_chunks_of(L, cap, chunk);
-  const size_t item = blockIdx.x;
+  // this chunk's partial rows in the workspace
+  const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
+  const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of token 0 of the group
 
   if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
     const float nan = __builtin_nanf("");
     for (int i = tid; i < R * kHeadDim; i += kThreads) {
       const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, gq = r % 6;
-      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + d] = nan;
+      p.out[((orow + t) * kQHeads + h * kGroup + gq) * kHeadDim + d] = nan;
     }
-    if (p.lse_out && tid < R)
-      p.lse_out[(static_cast<size_t>(s) * T + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
+    if (p.lse_out && tid < R) p.lse_out[(orow + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
     if (tid == 0) atomicOr(p.err, 2u);
     return;
   }
+  // token t of the group sits at position L - tok_total + tok0 + t and sees
+  // the positions up to it; keys past the group's last token are skipped
+  const int lim_base = L - p.tok_total + tok0;
   const int k0 = c * chunk;
-  const int k1 = min(L, k0 + chunk);
+  const int k1 = max(k0, min(min(L, k0 + chunk), lim_base + T));
 
   QSrc<T> qs;
   qs.base = q_lds;
   int lim[NT];
-  const int lim_min = L - T;                           // the first token's limit: every row sees <= lim_min
+  const int lim_min = lim_base;                        // the first token's limit: every row sees <= lim_min
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = C::kPack ? (n & 7) : 16 * nt + n;    // query row of this lane's column
-    lim[nt] = L - T + r / 6;                           // its token sees positions <= lim
+    lim[nt] = lim_base + r / 6;                        // its token sees positions <= lim
   }
 
   f4 o[NT][16];
@@ -1003,7 +1011,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     int ti = wave;
     const int my_total = (n_tiles - wave + 3) / 4;
     if (ti < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
-    build_q<KT, T>(p, s, h, wave, q_lds);
+    build_q<KT, T>(p, s, h, tok0, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
     if (ti < n_tiles) {
@@ -1047,7 +1055,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     }
   } else {
     uint8_t* wk = wl + FV::kVbuf;
-    build_q<KT, T>(p, s, h, wave, q_lds);
+    build_q<KT, T>(p, s, h, tok0, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
     for (int ti = wave; ti < n_tiles; ti += 4) {
@@ -1122,12 +1130,11 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
         lse2 = nan;
       }
       if (nc == 1) {
-        p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq) * kHeadDim + tid] = val;
-        if (p.lse_out && tid == 0)
-          p.lse_out[(static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + gq] = lse2 * kLn2;
+        p.out[((orow + t) * kQHeads + h * kGroup + gq) * kHeadDim + tid] = val;
+        if (p.lse_out && tid == 0) p.lse_out[(orow + t) * kQHeads + h * kGroup + gq] = lse2 * kLn2;
       } else {
-        p.part_o[(item * R + rr) * kHeadDim + tid] = val;
-        if (tid == 0) p.part_lse[item * R + rr] = lse2;
+        p.part_o[(part + rr) * kHeadDim + tid] = val;
+        if (tid == 0) p.part_lse[part + rr] = lse2;
       }
     }
   }
@@ -1136,7 +1143,8 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 
 template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((split_mfma_kernel<KT, VT, PA_T>), dim3(p.max_items), dim3(kThreads), 0, stream, p);
+  const dim3 grid(static_cast<unsigned>(p.max_items) * static_cast<unsigned>(p.n_groups));
+  hipLaunchKernelGGL((split_mfma_kernel<KT, VT, PA_T>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -48,31 +48,37 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
   const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum);
-  const int j = blockIdx.x / kKvHeads, h = blockIdx.x % kKvHeads;
+  const int grp = blockIdx.x % p.n_groups;           // token group fastest
+  const int item_id = blockIdx.x / p.n_groups;
+  const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
+  const int j = item_id / kKvHeads, h = item_id % kKvHeads;
   plan_locate(p.seq_lens, p.n_seq, cap, chunk, j, sh_loc);
   const int s = sh_loc[0], c = sh_loc[1];
   if (s < 0) return;
   const int L = p.seq_lens[s];
   const int nc = n_chunks_of(L, cap, chunk);
-  const size_t item = blockIdx.x;
+  const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
+  const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of the group's token 0
 
   if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
     const float nan = __builtin_nanf("");
     for (int i = tid; i < R * kHeadDim; i += kThreads) {
       const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, g = r % 6;
-      p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + g) * kHeadDim + d] = nan;
+      p.out[((orow + t) * kQHeads + h * kGroup + g) * kHeadDim + d] = nan;
     }
-    if (p.lse_out && tid < R)
-      p.lse_out[(static_cast<size_t>(s) * T + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
+    if (p.lse_out && tid < R) p.lse_out[(orow + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
     if (tid == 0) atomicOr(p.err, kErrLength);
     return;
   }
 
+  // token t of the group sits at position lim_base + t and sees the
+  // positions up to it; keys past the group's last token are skipped
+  const int lim_base = L - p.tok_total + tok0;
   const int k0 = c * chunk;
-  const int k1 = min(L, k0 + chunk);
+  const int k1 = max(k0, min(min(L, k0 + chunk), lim_base + T));
   for (int i = tid; i < R * kHeadDim; i += kThreads) {
     const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, g = r % 6;
-    q_lds[i] = p.q[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + g) * kHeadDim + d] * p.scale_log2;
+    q_lds[i] = p.q[((orow + t) * kQHeads + h * kGroup + g) * kHeadDim + d] * p.scale_log2;
   }
   __syncthreads();
 
@@ -103,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int lim = L - T + r / 6;      // token t = r / 6 sees positions <= lim
+      const int lim = lim_base + r / 6;   // token t = r / 6 sees positions <= lim
       if (pos > lim) sc[r] = kNegInf;
     }
     vrow_lds[wave][lane] = p.v + ((in && ok) ? ridx * RBV : 0);
@@ -179,12 +185,11 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
         lse2 = nan;
       }
       if (nc == 1) {
-        p.out[((static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + g) * kHeadDim + tid] = val;
-        if (p.lse_out && tid == 0)
-          p.lse_out[(static_cast<size_t>(s) * T + t) * kQHeads + h * kGroup + g] = lse2 * kLn2;
+        p.out[((orow + t) * kQHeads + h * kGroup + g) * kHeadDim + tid] = val;
+        if (p.lse_out && tid == 0) p.lse_out[(orow + t) * kQHeads + h * kGroup + g] = lse2 * kLn2;
       } else {
-        p.part_o[(item * R + r) * kHeadDim + tid] = val;
-        if (tid == 0) p.part_lse[item * R + r] = lse2;
+        p.part_o[(part + r) * kHeadDim + tid] = val;
+        if (tid == 0) p.part_lse[part + r] = lse2;
       }
     }
     __syncthreads();
@@ -194,7 +199,8 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
 
 template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((split_valu_kernel<KT, VT, PA_T>), dim3(p.max_items), dim3(kThreads), 0, stream, p);
+  const dim3 grid(static_cast<unsigned>(p.max_items) * static_cast<unsigned>(p.n_groups));
+  hipLaunchKernelGGL((split_valu_kernel<KT, VT, PA_T>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -255,6 +255,13 @@ def config4(ctx=32768, n_qtok=1, seed=4):
                          table="shuffled", seed=seed)
 
 
+def prefill_workload(ctx=16384, n_qtok=65, seed=6):
+    """One sequence of `ctx` stored positions whose last `n_qtok` are the new
+    query tokens, Q8_0 K and Q4_0 V in 256-token shuffled pages."""
+    return make_workload(f"q8_0k_q4_0v_1x{ctx}_t{n_qtok}_p256_shuffled", [ctx], n_qtok, "q8_0", "q4_0", 256,
+                         table="shuffled", seed=seed)
+
+
 def config5_lengths(seed=5, n_seq=128):
     """Lengths before the step: uniform integers in [512, 8192]."""
     return np.random.default_rng(seed).integers(512, 8192, size=n_seq, endpoint=True).astype(np.int32)

@@ -23,7 +23,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     names = _declared()
     assert "pa_decode" in names and "pa_append_kv" in names and "pa_append_kv_device" in names
-    assert len(names) >= 14
+    assert "pa_prefill" in names and len(names) >= 16
     lib = pb.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -162,6 +162,27 @@ def test_append_device_host_checks():
         assert st(src_type=src) == pb.ERR_INVALID
     pool.destroy()
     assert pb.lib().pa_append_kv_device(None, 1, a, a, a, a, pb.F32, None, None) == pb.ERR_INVALID
+
+
+def test_prefill_host_checks_and_workspace():
+    a = 1 << 20
+    kvq = pb.kv_type("q4_0")
+    st = lambda **kw: pb.prefill_status(**{**dict(q=a, k_pool=a, v_pool=a, block_table=a, seq_lens=a, n_seq=1,
+                                                   n_qtok=100, kv=kvq, page_size=16, out=a, stream=0), **kw})
+    assert st(n_qtok=0) == pb.ERR_INVALID
+    assert st(n_qtok=65537) == pb.ERR_INVALID
+    assert st() == pb.ERR_NOT_FOUND                       # passes the checks; no ext and no pool
+    assert st(n_qtok=65536) == pb.ERR_NOT_FOUND
+    assert st(q=a + 4) == pb.ERR_INVALID
+    # a workspace of exactly pa_prefill_workspace_size() bytes is accepted, one
+    # item (48 rows of 257 floats) less is not
+    for n_seq in (1, 3, 64):
+        for T in (1, 9, 17, 100, 4096):
+            n = pb.prefill_workspace_size(n_seq, T, 0)
+            ok = pb.make_ext(8, 64, 0.0, None, 1 << 30, n)
+            assert pb.prefill_status(a, a, a, a, a, n_seq, T, kvq, 16, a, 0, ok) != pb.ERR_INVALID, (n_seq, T)
+            small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 48 * 257 * 4)
+            assert pb.prefill_status(a, a, a, a, a, n_seq, T, kvq, 16, a, 0, small) == pb.ERR_INVALID, (n_seq, T)
 
 
 def test_workspace_size_is_accepted_and_needed():
