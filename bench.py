@@ -31,7 +31,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=400,
+                    help="untimed steps before each timed run; the GPU reaches its steady clock only after "
+                         "some milliseconds of work, so the default covers that")
     ap.add_argument("--workload", default="ragged",
                     choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16", "serving", "prefill"],
                     help="ragged: 131072 + 7 x 8192 Q4_0 (the headline); ragged_q8k_q4v: same with Q8_0 K and Q4_0 V; "

@@ -69,9 +69,38 @@ __device__ inline long long block_sum(long long v, long long* sh) {
   return sh[0] + sh[1] + sh[2] + sh[3];
 }
 
-// Tokens per chunk: the total live length times the KV-head count spread
-// over `target` items, rounded up to the granule, at least one granule.
-__device__ inline int plan_chunk(const int32_t* __restrict__ lens, int n_seq, int cap, int target,
+// Block-wide sums of kPlanCand per-thread values (256 threads); `sh` holds
+// kPlanShared slots.
+__device__ inline void block_sum_vec(long long (&v)[kPlanCand], long long* sh) {
+#pragma unroll
+  for (int k = 0; k < kPlanCand; ++k)
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v[k] += __shfl_xor(v[k], d, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < kPlanCand; ++k) sh[(threadIdx.x >> 6) * kPlanCand + k] = v[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPlanCand; ++k)
+    v[k] = sh[k] + sh[kPlanCand + k] + sh[2 * kPlanCand + k] + sh[3 * kPlanCand + k];
+}
+
+__device__ inline long long round_granule(long long c) {
+  c = (c + kChunkGranule - 1) / kChunkGranule * kChunkGranule;
+  if (c < kChunkGranule) c = kChunkGranule;
+  return c > (1ll << 30) ? (1ll << 30) : c;
+}
+
+// Tokens per chunk, a multiple of the granule (32 keys for each of the 4
+// waves of a workgroup).  From `target`: the total live length times the
+// KV-head count spread over target items, rounded up -- the items then number
+// at most target + 4 n_seq.  With budget > 0 (all items fit in one round of
+// resident workgroups): the shortest chunk among the kPlanCand lengths from
+// the lower bound 4 sum(L) / budget up whose items fit in the budget, if one
+// of them is shorter than the length from target.  Shorter chunks give each
+// wave fewer tiles.  `sh` holds kPlanShared slots.
+__device__ inline int plan_chunk(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
                                  long long* sh) {
   long long acc = 0;
   for (int i = threadIdx.x; i < n_seq; i += kThreads) {
@@ -79,10 +108,24 @@ __device__ inline int plan_chunk(const int32_t* __restrict__ lens, int n_seq, in
     if (L > 0 && L <= cap) acc += L;
   }
   const long long total = block_sum(acc, sh);
-  long long c = (total * kKvHeads + target - 1) / target;
-  c = (c + kChunkGranule - 1) / kChunkGranule * kChunkGranule;
-  if (c < kChunkGranule) c = kChunkGranule;
-  if (c > (1ll << 30)) c = 1ll << 30;
+  const long long c = round_granule((total * kKvHeads + target - 1) / target);
+  if (budget <= 0 || total == 0) return static_cast<int>(c);
+  const long long c0 = round_granule((total * kKvHeads + budget - 1) / budget);
+  if (c0 >= c) return static_cast<int>(c);
+  long long cnt[kPlanCand];
+#pragma unroll
+  for (int k = 0; k < kPlanCand; ++k) cnt[k] = 0;
+  for (int i = threadIdx.x; i < n_seq; i += kThreads) {
+    const int L = lens[i];
+#pragma unroll
+    for (int k = 0; k < kPlanCand; ++k) cnt[k] += n_chunks_of(L, cap, static_cast<int>(c0) + kChunkGranule * k);
+  }
+  block_sum_vec(cnt, sh);
+#pragma unroll
+  for (int k = 0; k < kPlanCand; ++k) {
+    const long long ck = c0 + kChunkGranule * k;
+    if (ck < c && kKvHeads * cnt[k] <= budget) return static_cast<int>(ck);
+  }
   return static_cast<int>(c);
 }
 
@@ -278,7 +321,8 @@ constexpr int kMaxMergeChunks = 2048;
 struct MergeShared {
   float w[kMaxMergeChunks];
   float4 part[4][64];
-  long long sum[4];
+  long long sum[kPlanShared];
+  int ints[4];
   float red[8];
 };
 
@@ -305,6 +349,93 @@ __device__ inline float block_sum_f(float v, float* sh) {
   return (sh[4] + sh[5]) + (sh[6] + sh[7]);
 }
 
+// The plan as one workgroup needs it: the chunk length, and either the
+// (sequence, chunk) of work item j (j >= 0) or the number of (sequence,
+// chunk) pairs before sequence s_pref (s_pref >= 0).  Up to 64 sequences,
+// wave 0 computes everything with wave-level reductions and one barrier
+// publishes it; the same integer arithmetic as plan_chunk / plan_locate /
+// plan_prefix, which serve longer batches.  `sh` holds kPlanShared slots,
+// `shi` 4 ints.
+struct PlanWG {
+  int chunk, s, c, prefix;
+};
+
+__device__ inline long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+__device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
+                                 int j, int s_pref, long long* sh, int* shi) {
+  PlanWG r{0, -1, 0, 0};
+  if (n_seq > 64) {
+    r.chunk = plan_chunk(lens, n_seq, cap, target, budget, sh);
+    if (j >= 0) {
+      plan_locate(lens, n_seq, cap, r.chunk, j, shi);
+      r.s = shi[0];
+      r.c = shi[1];
+    }
+    if (s_pref >= 0) r.prefix = plan_prefix(lens, s_pref, cap, r.chunk, sh);
+    return r;
+  }
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const bool has = lane < n_seq;
+    const int L = has ? lens[lane] : 0;
+    const long long total = wave_sum_ll((has && L > 0 && L <= cap) ? L : 0);
+    long long chunk = round_granule((total * kKvHeads + target - 1) / target);
+    if (budget > 0 && total > 0) {
+      const long long c0 = round_granule((total * kKvHeads + budget - 1) / budget);
+      if (c0 < chunk) {
+        int cnt[kPlanCand];
+#pragma unroll
+        for (int k = 0; k < kPlanCand; ++k)
+          cnt[k] = wave_sum_i(has ? n_chunks_of(L, cap, static_cast<int>(c0) + kChunkGranule * k) : 0);
+        long long pick = chunk;
+#pragma unroll
+        for (int k = kPlanCand - 1; k >= 0; --k) {
+          const long long ck = c0 + kChunkGranule * k;
+          if (ck < chunk && static_cast<long long>(kKvHeads) * cnt[k] <= budget) pick = ck;
+        }
+        chunk = pick;
+      }
+    }
+    const int nc = has ? n_chunks_of(L, cap, static_cast<int>(chunk)) : 0;
+    int fs = -1, fc = 0, pref = 0;
+    if (j >= 0) {
+      const int inc = wave_incl_scan(nc);
+      const int excl = inc - nc;
+      const bool hit = nc > 0 && j >= excl && j < inc;
+      const unsigned long long m = __ballot(hit);
+      if (m) {
+        const int src = __ffsll(static_cast<long long>(m)) - 1;
+        fs = src;
+        fc = j - __shfl(excl, src, 64);
+      }
+    }
+    if (s_pref >= 0) pref = wave_sum_i(lane < s_pref ? nc : 0);
+    if (lane == 0) {
+      shi[0] = static_cast<int>(chunk);
+      shi[1] = fs;
+      shi[2] = fc;
+      shi[3] = pref;
+    }
+  }
+  __syncthreads();
+  r.chunk = shi[0];
+  r.s = shi[1];
+  r.c = shi[2];
+  r.prefix = shi[3];
+  return r;
+}
+
 __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   constexpr int kEarly = 8;                              // chunk outputs per lane fetched before the weights
   const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
@@ -316,10 +447,11 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
-  const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh.sum);
+  const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, -1, s, sh.sum, sh.ints);
+  const int chunk = pl.chunk;
   const int nc = n_chunks_of(p.seq_lens[s], cap, chunk);
   if (nc <= 1) return;                                   // written by the split kernel
-  const int base = plan_prefix(p.seq_lens, s, cap, chunk, sh.sum);
+  const int base = pl.prefix;
   const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(base) * kKvHeads + h;
   const size_t prows = static_cast<size_t>(p.part_rows);
   const float* base_o = p.part_o + (item0 * prows + lr) * kHeadDim + 4 * lane;   // chunk c at item0 + 4c

@@ -504,6 +504,9 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   const int64_t plan = pa::plan_target(n_seq, per_group_slots, target);
   prm.target_items = static_cast<int32_t>(plan);
   prm.max_items = static_cast<int32_t>(pa::max_work_items(n_seq, plan));
+  // when every item fits one round, the plan may shorten the chunk as long
+  // as the items stay within the grid (max_items)
+  prm.plan_budget = (2 * static_cast<int64_t>(pa::kKvHeads) * n_seq <= per_group_slots) ? prm.max_items : 0;
   prm.tok_total = n_qtok;
   prm.tok0 = 0;
   prm.n_groups = 1;

@@ -15,7 +15,9 @@ constexpr int kQHeads = 24;
 constexpr int kKvHeads = 4;
 constexpr int kGroup = kQHeads / kKvHeads;  // query heads per KV head
 constexpr int kMaxQtok = 8;
-constexpr int kChunkGranule = 64;           // chunk lengths are multiples of this
+constexpr int kChunkGranule = 128;          // chunk lengths are multiples of this (32 keys x 4 waves)
+constexpr int kPlanCand = 4;                // chunk lengths the plan tries at once
+constexpr int kPlanShared = 4 * kPlanCand;  // long long slots of the plan's shared scratch
 
 enum KvType { kF16 = 1, kBF16 = 2, kQ8_0 = 3, kQ4_0 = 4 };
 
@@ -46,6 +48,7 @@ struct DecodeParams {
   uint32_t* err;           // error word
   int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
   int32_t target_items;    // item target of the chunk plan (plan_target)
+  int32_t plan_budget;     // > 0: the plan takes the shortest chunk whose items fit in it
   int32_t max_items;       // work items of the plan the grid covers (per token group)
   // Token groups: q / out / lse_out hold tok_total tokens per sequence; a
   // launch covers n_groups groups of the kernel's token count starting at

@@ -847,8 +847,15 @@ __device__ inline int out_dim(int mt, int g, int i) {
 // (tile, part, block).  One token: lane n < 8 of a column group carries the
 // hi part of row n, lane n + 8 the lo part (one tile, one part).  More
 // tokens: hi and lo in separate parts.  Wave w builds blocks 2w and 2w+1.
+// The loads are issued first (QLoad) and consumed later, so that the first
+// tile's loads, issued in between, stay in flight while q is converted.
+template <int T>
+struct QLoad {
+  float4 v[Cols<T>::NT][2][2];
+};
+
 template <int KT, int T>
-__device__ inline void build_q(const DecodeParams& p, int s, int h, int tok0, int wave, uint8_t* q_lds) {
+__device__ inline void load_q(const DecodeParams& p, int s, int h, int tok0, int wave, QLoad<T>& ql) {
   using C = Cols<T>;
   constexpr int R = C::R;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
@@ -861,15 +868,36 @@ __device__ inline void build_q(const DecodeParams& p, int s, int h, int tok0, in
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int b = 2 * wave + bb;
+      if constexpr (KT == kQ4_0) {
+        ql.v[nt][bb][0] = *reinterpret_cast<const float4*>(qrow + 32 * b + 4 * g);
+        ql.v[nt][bb][1] = *reinterpret_cast<const float4*>(qrow + 32 * b + 16 + 4 * g);
+      } else {
+        ql.v[nt][bb][0] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * g);
+        ql.v[nt][bb][1] = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * g + 4);
+      }
+    }
+  }
+}
+
+template <int KT, int T>
+__device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wave, uint8_t* q_lds) {
+  using C = Cols<T>;
+  constexpr int R = C::R;
+  const int lane = threadIdx.x & 63, n = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < C::NT; ++nt) {
+    const int r = C::kPack ? (n & 7) : 16 * nt + n;
+    const bool live = r < R;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * wave + bb;
       float x[8];
       if constexpr (KT == kQ4_0) {
-        const float4 lo = *reinterpret_cast<const float4*>(qrow + 32 * b + 4 * g);
-        const float4 hi = *reinterpret_cast<const float4*>(qrow + 32 * b + 16 + 4 * g);
+        const float4 lo = ql.v[nt][bb][0], hi = ql.v[nt][bb][1];
         x[0] = lo.x; x[1] = lo.z; x[2] = hi.x * 0.0625f; x[3] = hi.z * 0.0625f;
         x[4] = lo.y; x[5] = lo.w; x[6] = hi.y * 0.0625f; x[7] = hi.w * 0.0625f;
       } else {
-        const float4 a = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * g);
-        const float4 bq = *reinterpret_cast<const float4*>(qrow + 32 * b + 8 * g + 4);
+        const float4 a = ql.v[nt][bb][0], bq = ql.v[nt][bb][1];
         if constexpr (KT == kQ8_0) {
           x[0] = a.x; x[1] = a.z; x[2] = a.y; x[3] = a.w; x[4] = bq.x; x[5] = bq.z; x[6] = bq.y; x[7] = bq.w;
         } else {
@@ -918,30 +946,35 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int NT = C::NT;
   // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
   constexpr int kWaveBytes = (kDoubleBuffer<KT, VT, T> ? 2 : 1) * FV::kVbuf + F::kKarea;
-  constexpr int kRed = 4 * 16 * kHeadDim * 4;         // the combine, one B tile of rows at a time
+  // the combine, one B tile of rows at a time: [4 waves][16 rows][256 + 1]
+  // floats (the pad puts the 16 rows a column group writes in different banks)
+  constexpr int kRedStride = kHeadDim + 1;
+  constexpr int kRed = 4 * 16 * kRedStride * 4;
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
   __shared__ int tbl_lds[kTblCap];
   __shared__ float ml_lds[4][R][2];
-  __shared__ long long sh_sum[4];
-  __shared__ int sh_loc[2];
+  __shared__ float row_stat[2][R];                   // per row: 1 / sum of weights, log2-sum-exp
+  __shared__ long long sh_sum[kPlanShared];
+  __shared__ int sh_loc[4];
   __shared__ int sh_bad[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int cap = p.bt_stride * p.page_size;
-  const int chunk = __builtin_amdgcn_readfirstlane(plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum));
+
   // token group fastest: the groups of one chunk run side by side
   const int grp = blockIdx.x % p.n_groups;
   const int item_id = blockIdx.x / p.n_groups;
   const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
   const int jj = item_id / kKvHeads, h = item_id % kKvHeads;
-  plan_locate(p.seq_lens, p.n_seq, cap, chunk, jj, sh_loc);
+  const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, jj, -1, sh_sum, sh_loc);
   // every value that places loads is wave-uniform (scalar registers)
-  const int s = __builtin_amdgcn_readfirstlane(sh_loc[0]), c = __builtin_amdgcn_readfirstlane(sh_loc[1]);
+  const int chunk = __builtin_amdgcn_readfirstlane(pl.chunk);
+  const int s = __builtin_amdgcn_readfirstlane(pl.s), c = __builtin_amdgcn_readfirstlane(pl.c);
   if (s < 0) return;
   const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
   const int nc = n_chunks_of(L, cap, chunk);
@@ -993,13 +1026,33 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   // has passed); the first tile, loaded before it, reads the table itself.
   Pages pg{(lds_int*)(tbl_lds), 0, false};
   bool tbl_fits = false;
+  // The entries are loaded into registers here and written to LDS once q and
+  // the first tile are in flight as well (loads return in order, so the
+  // writes wait for the table alone).
+  constexpr int kTblPer = kTblCap / kThreads;
+  int tbl_v[kTblPer];
+  int n_tbl = 0;
   if (p.bt != nullptr && k1 > k0) {
     pg.lp0 = k0 / p.page_size;
-    const int n_tbl = (k1 - 1) / p.page_size - pg.lp0 + 1;
+    n_tbl = (k1 - 1) / p.page_size - pg.lp0 + 1;
     tbl_fits = n_tbl <= kTblCap;
-    if (tbl_fits)
-      for (int i = tid; i < n_tbl; i += kThreads) tbl_lds[i] = p.bt[static_cast<size_t>(s) * p.bt_stride + pg.lp0 + i];
+    if (tbl_fits) {
+#pragma unroll
+      for (int k = 0; k < kTblPer; ++k) {
+        const int i = tid + kThreads * k;
+        if (i < n_tbl) tbl_v[k] = p.bt[static_cast<size_t>(s) * p.bt_stride + pg.lp0 + i];
+      }
+    }
   }
+  auto stage_table = [&]() {
+    if (tbl_fits) {
+#pragma unroll
+      for (int k = 0; k < kTblPer; ++k) {
+        const int i = tid + kThreads * k;
+        if (i < n_tbl) tbl_lds[i] = tbl_v[k];
+      }
+    }
+  };
   if constexpr (kDoubleBuffer<KT, VT, T>) {
     // Registers hold the next tile's loads while the current one is worked
     // on, and PV runs one tile behind: while tile i is staged, its QK^T and
@@ -1010,8 +1063,11 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     Tile<KT, VT> ta, tb2;
     int ti = wave;
     const int my_total = (n_tiles - wave + 3) / 4;
+    QLoad<T> ql;
+    load_q<KT, T>(p, s, h, tok0, wave, ql);
     if (ti < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
-    build_q<KT, T>(p, s, h, tok0, wave, q_lds);
+    stage_table();
+    build_q<KT, T>(p, ql, wave, q_lds);
     __syncthreads();
     pg.in_lds = tbl_fits;
     if (ti < n_tiles) {
@@ -1055,7 +1111,12 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     }
   } else {
     uint8_t* wk = wl + FV::kVbuf;
-    build_q<KT, T>(p, s, h, tok0, wave, q_lds);
+    {
+      QLoad<T> ql;
+      load_q<KT, T>(p, s, h, tok0, wave, ql);
+      stage_table();
+      build_q<KT, T>(p, ql, wave, q_lds);
+    }
     __syncthreads();
     pg.in_lds = tbl_fits;
     for (int ti = wave; ti < n_tiles; ti += 4) {
@@ -1089,7 +1150,22 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   }
   if (lane == 0) sh_bad[wave] = __ballot(bad) ? 1 : 0;
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);       // [4 waves][16 rows][256], one B tile at a time
+  // per-row statistics of the 4 waves' states, once per row (read after the
+  // next barrier)
+  if (tid < R) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][tid][0]);
+    float ltot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = ml_lds[w][tid][0];
+      ltot += (mw == kNegInf) ? 0.f : ml_lds[w][tid][1] * exp2f(mw - M);
+    }
+    row_stat[0][tid] = ltot > 0.f ? 1.f / ltot : 0.f;
+    row_stat[1][tid] = ltot > 0.f ? M + __log2f(ltot) : kNegInf;
+  }
+  float* red = reinterpret_cast<float*>(lds);
   const bool any_bad = (sh_bad[0] | sh_bad[1] | sh_bad[2] | sh_bad[3]) != 0;
   const float nan = __builtin_nanf("");
 #pragma unroll
@@ -1101,7 +1177,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
       const float a = (m_run[nt] == kNegInf) ? 0.f : exp2f(m_run[nt] - M);
-      float* dst = red + (wave * 16 + n) * kHeadDim;
+      float* dst = red + (wave * 16 + n) * kRedStride;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
@@ -1109,22 +1185,15 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       }
     }
     __syncthreads();
-    const int r_end = min(R, 16 * nt + 16);
-    for (int rr = 16 * nt; rr < r_end; ++rr) {
-      const int t = rr / 6, gq = rr % 6, j = rr - 16 * nt;
-      float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][rr][0]);
-      float ltot = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = ml_lds[w][rr][0];
-        ltot += (mw == kNegInf) ? 0.f : ml_lds[w][rr][1] * exp2f(mw - M);
-      }
-      const float sum = red[(0 * 16 + j) * kHeadDim + tid] + red[(1 * 16 + j) * kHeadDim + tid] +
-                        red[(2 * 16 + j) * kHeadDim + tid] + red[(3 * 16 + j) * kHeadDim + tid];
-      float val = ltot > 0.f ? sum / ltot : 0.f;
-      float lse2 = ltot > 0.f ? M + __log2f(ltot) : kNegInf;
+    for (int j = 0; j < 16; ++j) {
+      const int rr = 16 * nt + j;
+      if (rr >= R) break;
+      const int t = rr / 6, gq = rr % 6;
+      const float sum = red[(0 * 16 + j) * kRedStride + tid] + red[(1 * 16 + j) * kRedStride + tid] +
+                        red[(2 * 16 + j) * kRedStride + tid] + red[(3 * 16 + j) * kRedStride + tid];
+      float val = sum * row_stat[0][rr];
+      float lse2 = row_stat[1][rr];
       if (any_bad) {
         val = nan;
         lse2 = nan;

@@ -41,19 +41,19 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
   __shared__ const uint8_t* vrow_lds[4][64];
   __shared__ __attribute__((aligned(16))) float red[4][6][kHeadDim];
   __shared__ float ml_lds[4][R][2];
-  __shared__ long long sh_sum[4];
-  __shared__ int sh_loc[2];
+  __shared__ long long sh_sum[kPlanShared];
+  __shared__ int sh_loc[4];
   __shared__ int sh_bad[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
-  const int chunk = plan_chunk(p.seq_lens, p.n_seq, cap, p.target_items, sh_sum);
+
   const int grp = blockIdx.x % p.n_groups;           // token group fastest
   const int item_id = blockIdx.x / p.n_groups;
   const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
   const int j = item_id / kKvHeads, h = item_id % kKvHeads;
-  plan_locate(p.seq_lens, p.n_seq, cap, chunk, j, sh_loc);
-  const int s = sh_loc[0], c = sh_loc[1];
+  const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, j, -1, sh_sum, sh_loc);
+  const int chunk = pl.chunk, s = pl.s, c = pl.c;
   if (s < 0) return;
   const int L = p.seq_lens[s];
   const int nc = n_chunks_of(L, cap, chunk);
