@@ -173,7 +173,12 @@ def main():
     nblocks = w["k_pool"].shape[0]
 
     def timed(calls, steps, warmup):
-        """calls: list of callables taking an event pair; returns (ms/step, split-kernel ms avg)."""
+        """calls: list of callables taking an event pair or None.  Times `steps`
+        steps with no events (wall clock, ms/step), then the same steps again
+        with HIP events recorded on the launch stream just before and after
+        each split kernel.  Returns (ms/step, split-kernel ms mean, median).
+        An event pair costs several microseconds of step time, so the step
+        time comes from the pass without them."""
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in evs:          # create the events on this stream
             a.record()
@@ -183,9 +188,12 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            calls[i % len(calls)]((evs[i][0].cuda_event, evs[i][1].cuda_event))
+            calls[i % len(calls)](None)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) * 1e3 / steps
+        for i in range(steps):
+            calls[i % len(calls)]((evs[i][0].cuda_event, evs[i][1].cuda_event))
+        torch.cuda.synchronize()
         ks = [a.elapsed_time(b) for a, b in evs]
         return dt, float(np.mean(ks)), float(np.median(ks))
 

@@ -314,16 +314,18 @@ __device__ inline void v_dims4(const uint8_t* __restrict__ row, int lane, float 
 // 0 with lse -inf (llama.cpp pull 2, pd_combine fix: an all-masked row is 0,
 // not 0/0); a NaN partial (corrupt table) gives NaN; otherwise
 // out = sum_c w_c o_c / sum_c w_c with w_c = 2^(lse_c - M) (lse in base 2).
-// The 4 waves take chunks c = w, w+4, ... (lane = 4 dims, float4 loads) and
-// are added in wave order, so the result is bitwise repeatable.
-constexpr int kMaxMergeChunks = 2048;
+// Wave w takes chunks c = w, w+4, ... (lane = 4 dims, float4 loads), up to
+// kMergeBatch at once: their log-sum-exps give the batch's base, then the
+// weighted outputs are summed in chunk order (a running base across
+// batches); the 4 waves' states are combined in wave order, so the result is
+// bitwise repeatable.
+constexpr int kMergeBatch = 24;     // chunk outputs per lane in flight
 
 struct MergeShared {
-  float w[kMaxMergeChunks];
   float4 part[4][64];
+  float ml[4][2];
   long long sum[kPlanShared];
   int ints[4];
-  float red[8];
 };
 
 // Number of (sequence, chunk) pairs before sequence s.
@@ -331,22 +333,6 @@ __device__ inline int plan_prefix(const int32_t* __restrict__ lens, int s, int c
   long long acc = 0;
   for (int i = threadIdx.x; i < s; i += kThreads) acc += n_chunks_of(lens[i], cap, chunk);
   return static_cast<int>(block_sum(acc, sh));
-}
-
-__device__ inline float block_max_f(float v, float* sh) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-}
-
-__device__ inline float block_sum_f(float v, float* sh) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[4 + (threadIdx.x >> 6)] = v;
-  __syncthreads();
-  return (sh[4] + sh[5]) + (sh[6] + sh[7]);
 }
 
 // The plan as one workgroup needs it: the chunk length, and either the
@@ -437,7 +423,6 @@ __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, in
 }
 
 __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
-  constexpr int kEarly = 8;                              // chunk outputs per lane fetched before the weights
   const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
   const int row_id = blockIdx.x;
   const int r = row_id % R;
@@ -447,75 +432,77 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
-  const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, -1, s, sh.sum, sh.ints);
-  const int chunk = pl.chunk;
+  int chunk, first;
+  if (p.n_seq <= kHdrSeqs) {                             // the split kernel left the plan in the header
+    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.err);
+    chunk = hdr[1];
+    first = hdr[2 + s];
+  } else {
+    const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, -1, s, sh.sum, sh.ints);
+    chunk = pl.chunk;
+    first = pl.prefix;
+  }
   const int nc = n_chunks_of(p.seq_lens[s], cap, chunk);
   if (nc <= 1) return;                                   // written by the split kernel
-  const int base = pl.prefix;
-  const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(base) * kKvHeads + h;
+  const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(first) * kKvHeads + h;
   const size_t prows = static_cast<size_t>(p.part_rows);
   const float* base_o = p.part_o + (item0 * prows + lr) * kHeadDim + 4 * lane;   // chunk c at item0 + 4c
-  const size_t cstride = static_cast<size_t>(kKvHeads) * prows * kHeadDim;     // floats between chunks
-  // the first chunk outputs of this wave go out now, before the weights
-  float4 early[kEarly];
-#pragma unroll
-  for (int u = 0; u < kEarly; ++u) {
-    const int c = wave + 4 * u;
-    early[u] = c < nc ? *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c) * cstride)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  // weights
-  float mx = kNegInf;
+  const float* base_l = p.part_lse + item0 * prows + lr;
+  const size_t cstride = static_cast<size_t>(kKvHeads) * prows;                 // rows between chunks
+  // each batch: all its chunk outputs and log-sum-exps in flight at once,
+  // then this wave's base m, weights 2^(x - m) and sums
+  float m = kNegInf, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   bool nan = false;
-  for (int c = tid; c < nc; c += kThreads) {
-    const float x = p.part_lse[(item0 + static_cast<size_t>(c) * kKvHeads) * prows + lr];
-    sh.w[c] = x;
-    nan |= (x != x);
-    mx = fmaxf(mx, x);
+  for (int c0 = wave; c0 < nc; c0 += 4 * kMergeBatch) {
+    float4 o[kMergeBatch];
+    float x[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int c = c0 + 4 * u;
+      const bool in = c < nc;
+      o[u] = in ? *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c) * cstride * kHeadDim)
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+      x[u] = in ? base_l[static_cast<size_t>(c) * cstride] : kNegInf;
+    }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      nan |= (x[u] != x[u]);
+      mb = fmaxf(mb, x[u]);                              // fmaxf ignores a NaN operand
+    }
+    if (mb == kNegInf) continue;                         // no visible key in any chunk so far
+    const float a = (m == kNegInf) ? 0.f : exp2f(m - mb);
+    acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
+    l *= a;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float b = (x[u] == kNegInf || x[u] != x[u]) ? 0.f : exp2f(x[u] - mb);
+      acc.x += b * o[u].x; acc.y += b * o[u].y; acc.z += b * o[u].z; acc.w += b * o[u].w;
+      l += b;
+    }
+    m = mb;
   }
   const bool any_nan = __syncthreads_or(nan);
-  const float M = block_max_f(mx, sh.red);
-  float ws = 0.f;
-  for (int c = tid; c < nc; c += kThreads) {
-    const float x = sh.w[c];
-    const float wc = (M == kNegInf || x == kNegInf) ? 0.f : exp2f(x - M);
-    sh.w[c] = wc;
-    ws += wc;
-  }
-  ws = block_sum_f(ws, sh.red);          // ends with a barrier: sh.w is complete
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int u = 0; u < kEarly; ++u) {
-    const int c = wave + 4 * u;
-    if (c < nc) {
-      const float wc = sh.w[c];
-      acc.x += wc * early[u].x; acc.y += wc * early[u].y; acc.z += wc * early[u].z; acc.w += wc * early[u].w;
-    }
-  }
-  int c = wave + 4 * kEarly;
-  for (; c + 28 < nc; c += 32) {          // 8 independent loads in flight per lane
-    float4 o[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c + 4 * u) * cstride);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wc = sh.w[c + 4 * u];
-      acc.x += wc * o[u].x; acc.y += wc * o[u].y; acc.z += wc * o[u].z; acc.w += wc * o[u].w;
-    }
-  }
-  for (; c < nc; c += 4) {
-    const float wc = sh.w[c];
-    const float4 o = *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c) * cstride);
-    acc.x += wc * o.x; acc.y += wc * o.y; acc.z += wc * o.z; acc.w += wc * o.w;
-  }
   sh.part[wave][lane] = acc;
+  if (lane == 0) {
+    sh.ml[wave][0] = m;
+    sh.ml[wave][1] = l;
+  }
   __syncthreads();
   if (wave == 0) {
-    float4 t = sh.part[0][lane];
+    float M = kNegInf;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) {
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.ml[w][0]);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sh.ml[w][0];
+      const float f = (mw == kNegInf) ? 0.f : exp2f(mw - M);
       const float4 u = sh.part[w][lane];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      t.x += f * u.x; t.y += f * u.y; t.z += f * u.z; t.w += f * u.w;
+      lt += f * sh.ml[w][1];
     }
     float4 val;
     float lse2;
@@ -526,9 +513,9 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
       val = make_float4(0.f, 0.f, 0.f, 0.f);
       lse2 = kNegInf;
     } else {
-      const float inv = 1.f / ws;
+      const float inv = 1.f / lt;
       val = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-      lse2 = M + __log2f(ws);
+      lse2 = M + __log2f(lt);
     }
     const int g = r % 6;
     const size_t orow = static_cast<size_t>(s) * p.tok_total + tg;

@@ -95,6 +95,11 @@ PA_HD inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Partial rows of one work item: the 6 query heads x n_qtok tokens.
 PA_HD constexpr int rows_per_item(int n_qtok) { return 6 * n_qtok; }
 
+// The workspace header's int32 words: [0] the device error word, [1] the
+// call's chunk length and [2 + s] the plan index of sequence s's first chunk
+// for s < kHdrSeqs, written by the split kernel for the merge kernel.
+constexpr int kHdrSeqs = 62;
+
 // Workspace: [0, 256) header (error word at 0); chunk log-sum-exps
 // [items][6 n_qtok]; chunk outputs [items][6 n_qtok][256].  The layout
 // depends on the call's n_qtok and the item capacity only, so a workspace

@@ -976,6 +976,11 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   const int chunk = __builtin_amdgcn_readfirstlane(pl.chunk);
   const int s = __builtin_amdgcn_readfirstlane(pl.s), c = __builtin_amdgcn_readfirstlane(pl.c);
   if (s < 0) return;
+  if (tid == 0 && c == 0 && h == 0 && tok0 == 0) {      // the plan, for the merge kernel
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.err);
+    if (s < kHdrSeqs) hdr[2 + s] = jj;
+    if (s == 0) hdr[1] = chunk;
+  }
   const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
   const int nc = n_chunks_of(L, cap, chunk);
   // this chunk's partial rows in the workspace

@@ -55,6 +55,11 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
   const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, j, -1, sh_sum, sh_loc);
   const int chunk = pl.chunk, s = pl.s, c = pl.c;
   if (s < 0) return;
+  if (tid == 0 && c == 0 && h == 0 && tok0 == 0) {      // the plan, for the merge kernel
+    int32_t* hdr = reinterpret_cast<int32_t*>(p.err);
+    if (s < kHdrSeqs) hdr[2 + s] = j;
+    if (s == 0) hdr[1] = chunk;
+  }
   const int L = p.seq_lens[s];
   const int nc = n_chunks_of(L, cap, chunk);
   const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
