@@ -492,6 +492,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.n_qtok = n_qtok;
   prm.bt_stride = bt_stride;
   prm.page_size = page_size;
+  prm.page_shift = ((page_size & (page_size - 1)) == 0) ? __builtin_ctz(static_cast<unsigned>(page_size)) : -1;
   prm.n_pool_blocks = block_table ? n_pool_blocks : 0;
   // The plan aims at one round of resident workgroups (shared among the
   // token groups of a prefill); the workspace check above used the larger

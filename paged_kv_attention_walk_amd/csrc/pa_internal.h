@@ -47,6 +47,7 @@ struct DecodeParams {
   float* part_lse;         // [item capacity][24]   (log2 units)
   uint32_t* err;           // error word
   int32_t n_seq, n_qtok, bt_stride, page_size, n_pool_blocks;
+  int32_t page_shift;      // log2(page_size) when it is a power of two, else -1
   int32_t target_items;    // item target of the chunk plan (plan_target)
   int32_t plan_budget;     // > 0: the plan takes the shortest chunk whose items fit in it
   int32_t max_items;       // work items of the plan the grid covers (per token group)

@@ -273,7 +273,9 @@ __device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int
     r.live = in;
     return r;
   }
-  const int lp = pos / p.page_size;
+  // page and slot of pos (a shift for power-of-two pages: this runs twice per tile)
+  const int lp = (p.page_shift >= 0) ? (pos >> p.page_shift) : pos / p.page_size;
+  const int slot = pos - lp * p.page_size;
   int phys;
   if (pg.in_lds) {
     phys = __builtin_amdgcn_readfirstlane(pg.tbl[lp - pg.lp0]);
@@ -283,7 +285,7 @@ __device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int
   }
   const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(p.n_pool_blocks);
   if (in && !ok) bad = true;
-  r.row = ok ? (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + (pos - lp * p.page_size) : 0;
+  r.row = ok ? (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + slot : 0;
   r.live = in && ok;
   return r;
 }
