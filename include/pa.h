@@ -7,7 +7,8 @@
  * size 256 and grouped queries -- 24 query heads over 4 KV heads, so one KV
  * head serves 6 query heads -- for 1 to 4 new query tokens per sequence
  * (and, as achyudh/llama.cpp pull 2 extends its decode kernel to verify
- * batches of up to 8 query tokens, for 5 to 8 as well), with K and V stored as F16, BF16, Q8_0 or Q4_0 rows in fixed-size pages that a
+ * batches of up to 8 query tokens, for 5 to 8 as well; pa_prefill takes
+ * more), with K and V stored as F16, BF16, Q8_0 or Q4_0 rows in fixed-size pages that a
  * per-sequence block table scatters through one pool.  Each sequence's
  * context is split into chunks; every chunk produces a normalised partial
  * output and its log-sum-exp, and a stable merge combines them.

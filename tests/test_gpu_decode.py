@@ -39,7 +39,7 @@ def test_config1_parity(engine):
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_small_ragged_parity(kind, T, engine):
-    # several chunks per sequence (the plan's granule is 64 keys), ragged
+    # several chunks per sequence (the plan's granule is 128 keys), ragged
     # tails, empty and shorter-than-T sequences, pages of 48 positions
     lens = [0, 2, 63, 64, 65, 700, 1500, 3001]
     w = synth.make_workload(f"small_{kind}_{T}", lens, T, kind, kind, 48, table="shuffled", seed=11 + T)
