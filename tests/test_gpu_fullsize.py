@@ -1,0 +1,118 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (pa_decode with an explicit workspace, the same plan):
+uniform 8 x 4096 Q4_0 checked whole; the ragged 131072 + 7 x 8192 Q4_0 step,
+the single-sequence Q8_0 verify contexts and the 128-stream BF16 serving step
+(device append, then decode) checked on sampled (sequence, KV head) blocks,
+which the oracle computes one KV head at a time.  Also batches of more than
+62 / 64 sequences, which take the block-wide plan and the merge's own plan."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, encode, pool_model, quant
+from paged_kv_attention_walk_amd import binding as pb
+from paged_kv_attention_walk_amd import synth
+from gpu_util import dev, log, parity, run
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_head(w, s, h, patch=None):
+    """Oracle output [T][6][256] of sequence s, KV head h (its 6 query heads).
+    ``patch`` = (position, K row bytes, V row bytes) replaces one stored row."""
+    L = int(w["seq_lens"][s])
+    kb = pool_model.gather_rows(w["k_pool"][:, h:h + 1], w["block_table"][s], L)
+    vb = pool_model.gather_rows(w["v_pool"][:, h:h + 1], w["block_table"][s], L)
+    if patch is not None:
+        pos, krow, vrow = patch
+        kb[0, pos] = krow
+        vb[0, pos] = vrow
+    k = quant.decode(kb, w["k_kind"])
+    v = quant.decode(vb, w["v_kind"])
+    out, _ = attention.decode_sequence(w["q"][s][:, 6 * h:6 * h + 6], k, v, L, w["scale"])
+    return out
+
+
+def test_uniform_8x4096_q4_0_whole():
+    w = synth.config2()
+    log("[case] uniform 8 x 4096 Q4_0, whole output")
+    out, _, err = run(w)
+    assert err == 0
+    ref, _ = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q4_0", "q4_0", w["block_table"],
+                                    w["seq_lens"], w["scale"])
+    parity(out, ref, what="uniform 8x4096")
+
+
+@pytest.mark.parametrize("engine", ["mfma", "valu"])
+def test_ragged_128k_7x8k_q4_0_sampled(engine):
+    w = synth.config3()
+    log(f"[case] ragged 131072 + 7 x 8192 Q4_0, sampled heads, {engine}")
+    out, _, err = run(w, engine=engine)
+    assert err == 0
+    for s, h in [(0, 0), (0, 3), (1, 1), (7, 2)]:
+        ref = _oracle_head(w, s, h)
+        parity(out[s][:, 6 * h:6 * h + 6][None], ref[None], what=f"ragged seq {s} head {h}")
+
+
+@pytest.mark.parametrize("ctx,T", [(32768, 4), (131072, 1), (131072, 3), (262144, 2)])
+def test_mtp_q8_0_sampled(ctx, T):
+    w = synth.config4(ctx=ctx, n_qtok=T)
+    log(f"[case] Q8_0 single sequence ctx={ctx} T={T}, sampled heads")
+    out, _, err = run(w)
+    assert err == 0
+    for h in (1, 2):
+        parity(out[0][:, 6 * h:6 * h + 6][None], _oracle_head(w, 0, h)[None], what=f"mtp ctx={ctx} T={T} head {h}")
+
+
+def test_serving_128_streams_append_then_decode_sampled():
+    # the benchmark's serving step: one float32 row per stream appended on the
+    # device at its last position, then the decode
+    w = synth.config5()
+    n_seq, P = len(w["seq_lens"]), w["page_size"]
+    log("[case] 128-stream BF16 serving step (device append + decode), sampled streams")
+    last = w["seq_lens"].astype(np.int64) - 1
+    blocks = w["block_table"][np.arange(n_seq), last // P].astype(np.int32)
+    slots = (last % P).astype(np.int32)
+    xk = synth.normal((n_seq, 4, 256), seed=505)
+    xv = synth.normal((n_seq, 4, 256), seed=506)
+    kp, vp = dev(w["k_pool"]), dev(w["v_pool"])
+    pool = pb.Pool(w["k_pool"].shape[0], P, "bf16", k_pool=kp, v_pool=vp, max_seqs=1,
+                   max_blocks_per_seq=w["block_table"].shape[1])
+    pool.append_kv_device(dev(blocks), dev(slots), dev(xk), dev(xv), "f32")
+    torch.cuda.synchronize()
+    assert pool.device_error() == 0
+    out, _, err = run(w, dk=kp, dv=vp)
+    assert err == 0
+    rng = np.random.default_rng(12)
+    picks = [int(x) for x in rng.choice(n_seq, size=6, replace=False)]
+    # the oracle's rows: the generated pages, with the appended row encoded by the oracle encoder
+    for s in picks:
+        h = s % 4
+        patch = (int(last[s]), encode.encode(xk[s][h], "bf16"), encode.encode(xv[s][h], "bf16"))
+        ref = _oracle_head(w, s, h, patch=patch)
+        parity(out[s][:, 6 * h:6 * h + 6][None], ref[None], what=f"serving stream {s} head {h}")
+    pool.destroy()
+
+
+@pytest.mark.parametrize("engine", ["mfma", "valu"])
+@pytest.mark.parametrize("n_seq", [62, 63, 64, 65, 130])
+def test_many_sequences_with_long_ones(n_seq, engine):
+    # mostly short sequences and a few long ones, so the long ones split into
+    # several chunks: the plan runs block-wide past 64 sequences and the merge
+    # plans for itself past 62
+    rng = np.random.default_rng(n_seq)
+    lens = [int(x) for x in rng.integers(0, 200, size=n_seq)]
+    for i in rng.choice(n_seq, size=4, replace=False):
+        lens[int(i)] = int(rng.integers(15000, 25000))
+    lens[0] = 0
+    w = synth.make_workload(f"many_{n_seq}", lens, 2, "q4_0", "q8_0", 16, table="shuffled", seed=900 + n_seq)
+    log(f"[case] {n_seq} sequences (4 long), {engine}")
+    out, lse, err = run(w, lse=True, engine=engine)
+    assert err == 0
+    ref, rlse = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q4_0", "q8_0", w["block_table"],
+                                       w["seq_lens"], w["scale"])
+    parity(out, ref, what=f"{n_seq} sequences")
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-3
