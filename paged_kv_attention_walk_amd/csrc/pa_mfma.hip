@@ -948,10 +948,13 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int NT = C::NT;
   // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
   constexpr int kWaveBytes = (kDoubleBuffer<KT, VT, T> ? 2 : 1) * FV::kVbuf + F::kKarea;
-  // the combine, one B tile of rows at a time: [4 waves][16 rows][256 + 1]
-  // floats (the pad puts the 16 rows a column group writes in different banks)
+  // the combine, one B tile of rows at a time: [4 waves][kRT rows][256 + 1]
+  // floats (the pad puts the rows a column group writes in different banks;
+  // only a tile's live rows are kept, so one or two tokens leave room for a
+  // second workgroup per compute unit)
   constexpr int kRedStride = kHeadDim + 1;
-  constexpr int kRed = 4 * 16 * kRedStride * 4;
+  constexpr int kRT = (R < 16) ? R : 16;
+  constexpr int kRed = 4 * kRT * kRedStride * 4;
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
@@ -1184,7 +1187,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
       const float a = (m_run[nt] == kNegInf) ? 0.f : exp2f(m_run[nt] - M);
-      float* dst = red + (wave * 16 + n) * kRedStride;
+      float* dst = red + (wave * kRT + n) * kRedStride;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
@@ -1197,8 +1200,8 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       const int rr = 16 * nt + j;
       if (rr >= R) break;
       const int t = rr / 6, gq = rr % 6;
-      const float sum = red[(0 * 16 + j) * kRedStride + tid] + red[(1 * 16 + j) * kRedStride + tid] +
-                        red[(2 * 16 + j) * kRedStride + tid] + red[(3 * 16 + j) * kRedStride + tid];
+      const float sum = red[(0 * kRT + j) * kRedStride + tid] + red[(1 * kRT + j) * kRedStride + tid] +
+                        red[(2 * kRT + j) * kRedStride + tid] + red[(3 * kRT + j) * kRedStride + tid];
       float val = sum * row_stat[0][rr];
       float lse2 = row_stat[1][rr];
       if (any_bad) {
