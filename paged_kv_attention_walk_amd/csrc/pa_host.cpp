@@ -473,7 +473,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes, workspace_rows_tokens(n_qtok, prefill));
   const int64_t items = workspace_items(n_seq, n_qtok, prefill, device);
   if (wl.items < items) return PA_ERR_INVALID;
-  if (items > (1ll << 31) - 1 || static_cast<int64_t>(n_seq) * 24 * n_qtok > (1ll << 31) - 1)
+  if (items > (1ll << 31) - 1 || static_cast<int64_t>(n_seq) * PA_N_Q_HEADS * n_qtok > (1ll << 31) - 1)   // merge grid
     return PA_ERR_UNSUPPORTED;
 
   pa::DecodeParams prm{};
