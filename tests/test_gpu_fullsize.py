@@ -116,3 +116,40 @@ def test_many_sequences_with_long_ones(n_seq, engine):
     fin = np.isfinite(rlse)
     assert np.array_equal(fin, np.isfinite(lse))
     assert np.max(np.abs(lse[fin] - rlse[fin])) < 1e-3
+
+
+def test_600_sequences_three_tokens():
+    # the plan's scan walks ten blocks of 64 sequences
+    rng = np.random.default_rng(600)
+    lens = [int(x) for x in rng.integers(0, 96, size=600)]
+    for i in rng.choice(600, size=3, replace=False):
+        lens[int(i)] = int(rng.integers(20000, 30000))
+    w = synth.make_workload("many_600", lens, 3, "q8_0", "q4_0", 32, table="shuffled", seed=1600)
+    log("[case] 600 sequences (3 long), T=3")
+    out, _, err = run(w)
+    assert err == 0
+    ref, _ = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q8_0", "q4_0", w["block_table"],
+                                    w["seq_lens"], w["scale"])
+    parity(out, ref, what="600 sequences")
+
+
+def test_prefill_70_sequences():
+    # prefill past 62 sequences: the merge plans for itself, every token group
+    rng = np.random.default_rng(70)
+    lens = [int(x) for x in rng.integers(12, 160, size=70)]
+    lens[5], lens[40] = 9000, 12000
+    T = 12
+    w = synth.make_workload("prefill_70", lens, T, "q4_0", "q4_0", 16, table="shuffled", seed=1700)
+    log("[case] prefill, 70 sequences, T=12")
+    n_seq = len(lens)
+    n = pb.prefill_workspace_size(n_seq, T, torch.cuda.current_device())
+    ws = torch.zeros(n // 4 + 64, dtype=torch.int32, device="cuda")
+    out = torch.empty((n_seq, T, 24, 256), dtype=torch.float32, device="cuda")
+    ext = pb.make_ext(w["block_table"].shape[1], w["k_pool"].shape[0], w["scale"], None, ws, ws.numel() * 4)
+    st = pb.prefill_status(dev(w["q"]), dev(w["k_pool"]), dev(w["v_pool"]), dev(w["block_table"]),
+                           dev(w["seq_lens"]), n_seq, T, pb.kv_type("q4_0"), 16, out, ext=ext)
+    assert st == pb.OK
+    assert pb.device_error(ws) == 0
+    ref, _ = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q4_0", "q4_0", w["block_table"],
+                                    w["seq_lens"], w["scale"])
+    parity(out.cpu().numpy(), ref, what="prefill 70 sequences")
