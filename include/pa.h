@@ -46,7 +46,7 @@ typedef int32_t pa_status;
 #define PA_ERR_INVALID     (-1) /* an argument is out of range or inconsistent   */
 #define PA_ERR_NOMEM       (-2) /* not enough free pool blocks / device memory     */
 #define PA_ERR_STALE       (-3) /* a handle is stale, already free or repeated     */
-#define PA_ERR_UNSUPPORTED (-4) /* a type, page size or shape this build lacks     */
+#define PA_ERR_UNSUPPORTED (-4) /* a type, page size or shape the library lacks    */
 #define PA_ERR_HIP         (-5) /* a HIP runtime call failed                       */
 #define PA_ERR_NOT_FOUND   (-6) /* a K/V pointer is not the base of a live pool    */
 

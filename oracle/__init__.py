@@ -41,7 +41,7 @@ Modules:
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than
 itself (values printed on the pages, closed forms, a library routine, brute
-force on tiny inputs, invariants).  the design doc lists each pin.
+force on tiny inputs, invariants).
 """
 
 from . import quant, encode, attention, pool_model, alloc_model  # noqa: F401

@@ -4,7 +4,7 @@ infrastructure only).
 lucebox#555, Summary, names the allocator's properties: exact fixed-size
 blocks, transactional allocation, stale-handle detection, immediate release.
 TensorFold#1156, Design / Host, takes K/V pages from the bottom of its arena.
-This model makes each property concrete, in the readings the design doc lists:
+This model makes each property concrete, with these readings:
 
 * exact: ``n_free + n_used == n_blocks`` at all times; a request for more
   blocks than are free fails and changes nothing;

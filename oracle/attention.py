@@ -9,7 +9,7 @@ exact (llama.cpp-PR2, log-sum-exp output commit: attending parts separately
 and merging the normalised results reproduces the whole), so the oracle is
 one softmax per query row over all its visible keys.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * query head h reads KV head h // (Hq/Hkv): consecutive query heads share a
   KV head;

@@ -4,7 +4,7 @@ The pages describe K and V as pools of fixed-size pages, each logical page of a
 sequence mapped to a pool page through an int32 block table, one row per
 position (llama.cpp-PR2, page-table commit: K/V are a pool of pages;
 KV-streaming commit: per-layer page tables are one I32 input).  The pages do
-not fix how rows are laid out inside a pool page.  This build's reading:
+not fix how rows are laid out inside a pool page.  The reading taken here:
 
 * K and V are separate pools (``pa_decode`` takes ``k_pool`` and ``v_pool``);
 * a pool is ``[n_blocks][n_kv_heads][page_size][row_bytes]`` bytes
