@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp / prefill")
     ap.add_argument("--ctx", type=int, default=16384, help="context for --workload prefill")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
+    ap.add_argument("--plan", default="host", choices=["host", "device"],
+                    help="host: the call also passes a host copy of seq_lens (pa_decode_ext.seq_lens_host), so the "
+                         "split-K plan is computed on the host and travels with the launch; device: the kernels "
+                         "compute it from the device seq_lens.  The other route is timed too and reported")
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -215,10 +219,11 @@ def main():
                         for kp, vp in pools]
         append = {"rows": n_seq, "src": "f32", "keep": (dst_block, dst_slot, xk, xv)}
 
-    def make_call(kp, vp, bt, nb, pool=None):
+    def make_call(kp, vp, bt, nb, pool=None, plan=args.plan):
         """A step with every pointer and the ext struct prepared up front, so
         that the timed loop is one ctypes call per step (two with an append)."""
-        ext = pb.make_ext(bt_stride, nb, w["scale"], None, ws, ws.numel() * 4)
+        ext = pb.make_ext(bt_stride, nb, w["scale"], None, ws, ws.numel() * 4,
+                          seq_lens_host=w["seq_lens"] if plan == "host" else None)
         ext_ref = ctypes.byref(ext)
         a = (dq.data_ptr(), kp.data_ptr(), vp.data_ptr(), bt.data_ptr() if bt is not None else None,
              dlens.data_ptr(), n_seq, T, kv, P, out.data_ptr(), stream)
@@ -241,11 +246,16 @@ def main():
         f.keep = (ext, kp, vp, bt, pool)
         return f
 
-    def paged_call(r, with_append=True):
+    def paged_call(r, with_append=True, plan=args.plan):
         return make_call(pools[r][0], pools[r][1], bts[r], nblocks,
-                         append_pools[r] if (serving and with_append) else None)
+                         append_pools[r] if (serving and with_append) else None, plan)
 
+    other = "device" if args.plan == "host" else "host"
+    o_ms, o_k, _ = timed([paged_call(r, plan=other) for r in range(reps)], args.steps, args.warmup)
+    res_other = out.clone()
     cold_ms, cold_k, cold_k_med = timed([paged_call(r) for r in range(reps)], args.steps, args.warmup)
+    other_plan = {"plan": other, "ms_per_step": round(o_ms, 4), "split_kernel_ms": round(o_k, 4),
+                  "bitwise_equal": bool(torch.equal(out.view(torch.int32), res_other.view(torch.int32)))}
     hot_ms, hot_k, _ = timed([paged_call(0)], args.steps, args.warmup)
     decode_only_ms = None
     if serving:
@@ -321,6 +331,8 @@ def main():
         "hot": {"ms_per_step": round(hot_ms, 4), "split_kernel_ms": round(hot_k, 4),
                 "gbps": round(kv_bytes / (hot_ms * 1e-3) / 1e9, 2)},
         "replicas": reps,
+        "plan": args.plan,
+        "other_plan": other_plan,
         "roofline": roofline,
         "split_tflops": round(tflops, 2),
         "cpu_baseline": None,

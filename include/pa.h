@@ -257,7 +257,19 @@ typedef struct pa_decode_ext {
     size_t   workspace_bytes;
     void    *split_events[2];/* optional hipEvent_t pair, recorded on `stream` just
                                 before and after the split kernel (profiling)           */
+    const int32_t *seq_lens_host; /* optional HOST copy of seq_lens ([n_seq] int32), or
+                                NULL.  With it (and n_seq <= PA_HOST_PLAN_MAX_SEQS) the
+                                split-K plan -- chunk length and each sequence's first
+                                work item -- is computed on the host, with the same
+                                integer arithmetic as the device plan, and travels with
+                                the launch: the kernels then never read the device
+                                seq_lens, and the caller guarantees that it holds the
+                                same values.  Results are bitwise identical to the
+                                device-planned call.  Larger batches ignore it.        */
 } pa_decode_ext;
+
+/* Largest batch whose plan pa_decode_ext.seq_lens_host can carry. */
+#define PA_HOST_PLAN_MAX_SEQS 256
 
 /* One decode step (lucebox pull 555, Summary; achyudh/llama.cpp pull 2,
  * split-K decode and page-table commits).

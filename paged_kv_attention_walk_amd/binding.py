@@ -69,7 +69,8 @@ class PoolInfo(ctypes.Structure):
 class DecodeExt(ctypes.Structure):
     _fields_ = [("bt_stride", ctypes.c_int32), ("n_pool_blocks", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("flags", ctypes.c_uint32), ("lse_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("split_events", ctypes.c_void_p * 2)]
+                ("workspace_bytes", ctypes.c_size_t), ("split_events", ctypes.c_void_p * 2),
+                ("seq_lens_host", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -241,7 +242,7 @@ class Pool:
 
 
 def make_ext(bt_stride, n_pool_blocks=0, scale=0.0, lse_out=None, workspace=None, workspace_bytes=None,
-             split_events=None, flags=0) -> DecodeExt:
+             split_events=None, flags=0, seq_lens_host=None) -> DecodeExt:
     e = DecodeExt(bt_stride=int(bt_stride), n_pool_blocks=int(n_pool_blocks), scale=float(scale), flags=int(flags),
                   lse_out=_ptr(lse_out), workspace=_ptr(workspace),
                   workspace_bytes=int(workspace_bytes if workspace_bytes is not None else
@@ -249,6 +250,12 @@ def make_ext(bt_stride, n_pool_blocks=0, scale=0.0, lse_out=None, workspace=None
     if split_events is not None:
         e.split_events[0] = split_events[0]
         e.split_events[1] = split_events[1]
+    if seq_lens_host is not None:
+        # host int32 copy of seq_lens: the plan is computed on the host; the
+        # array is kept alive with the struct
+        lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+        e._seq_lens_host = lens
+        e.seq_lens_host = lens.ctypes.data
     return e
 
 

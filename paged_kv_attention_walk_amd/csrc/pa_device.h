@@ -422,6 +422,33 @@ __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, in
   return r;
 }
 
+// The plan as plan_wg gives it, taken from the launch arguments when the
+// host computed it (no load, no barrier), else computed from seq_lens.
+__device__ inline PlanWG plan_of(const DecodeParams& p, int cap, int j, int s_pref, long long* sh, int* shi) {
+  if (p.hp.on) {
+    PlanWG r{p.hp.chunk, -1, 0, 0};
+    if (j >= 0 && j < p.hp.first[p.n_seq]) {
+      // the last s with first[s] <= j (first[] increases: every sequence has a pair)
+      int s = 0, hi = p.n_seq - 1;
+      while (s < hi) {
+        const int mid = (s + hi + 1) >> 1;
+        if (p.hp.first[mid] <= j) s = mid;
+        else hi = mid - 1;
+      }
+      r.s = s;
+      r.c = j - p.hp.first[s];
+    }
+    if (s_pref >= 0) r.prefix = p.hp.first[s_pref];
+    return r;
+  }
+  return plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, j, s_pref, sh, shi);
+}
+
+// seq_lens[s], from the launch arguments with a host plan.
+__device__ inline int seq_len_of(const DecodeParams& p, int s) {
+  return p.hp.on ? p.hp.len[s] : __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
+}
+
 __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
   const int row_id = blockIdx.x;
@@ -433,7 +460,10 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cap = p.bt_stride * p.page_size;
   int chunk, first;
-  if (p.n_seq <= kHdrSeqs) {                             // the split kernel left the plan in the header
+  if (p.hp.on) {                                         // the host's plan, in the launch arguments
+    chunk = p.hp.chunk;
+    first = p.hp.first[s];
+  } else if (p.n_seq <= kHdrSeqs) {                      // the split kernel left the plan in the header
     const int32_t* hdr = reinterpret_cast<const int32_t*>(p.err);
     chunk = hdr[1];
     first = hdr[2 + s];
@@ -442,7 +472,7 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
     chunk = pl.chunk;
     first = pl.prefix;
   }
-  const int nc = n_chunks_of(p.seq_lens[s], cap, chunk);
+  const int nc = n_chunks_of(p.hp.on ? p.hp.len[s] : p.seq_lens[s], cap, chunk);
   if (nc <= 1) return;                                   // written by the split kernel
   const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(first) * kKvHeads + h;
   const size_t prows = static_cast<size_t>(p.part_rows);

@@ -127,6 +127,50 @@ void free_pool_resources(pa_pool* p) {
 
 }  // namespace
 
+namespace pa {
+
+static_assert(PA_HOST_PLAN_MAX_SEQS == kHostPlanSeqs, "host plan limit of the ABI");
+static_assert(sizeof(DecodeParams) <= 4096, "launch arguments stay within 4 KB");
+
+// The device plan (plan_wg / plan_chunk) in host arithmetic.
+void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, HostPlan& hp) {
+  auto n_chunks = [cap](int L, int chunk) { return (L <= 0 || L > cap) ? 1 : (L + chunk - 1) / chunk; };
+  auto granule = [](long long c) {
+    c = (c + kChunkGranule - 1) / kChunkGranule * kChunkGranule;
+    if (c < kChunkGranule) c = kChunkGranule;
+    return c > (1ll << 30) ? (1ll << 30) : c;
+  };
+  long long total = 0;
+  for (int i = 0; i < n_seq; ++i)
+    if (lens[i] > 0 && lens[i] <= cap) total += lens[i];
+  long long chunk = granule((total * kKvHeads + target - 1) / target);
+  if (budget > 0 && total > 0) {
+    const long long c0 = granule((total * kKvHeads + budget - 1) / budget);
+    if (c0 < chunk) {
+      long long pick = chunk;
+      for (int k = kPlanCand - 1; k >= 0; --k) {
+        const long long ck = c0 + static_cast<long long>(kChunkGranule) * k;
+        long long cnt = 0;
+        for (int i = 0; i < n_seq; ++i) cnt += n_chunks(lens[i], static_cast<int>(ck));
+        if (ck < chunk && kKvHeads * cnt <= budget) pick = ck;
+      }
+      chunk = pick;
+    }
+  }
+  hp.on = 1;
+  hp.chunk = static_cast<int32_t>(chunk);
+  hp.any_multi = 0;
+  hp.first[0] = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int nc = n_chunks(lens[i], hp.chunk);
+    hp.first[i + 1] = hp.first[i] + nc;
+    hp.len[i] = lens[i];
+    if (nc > 1) hp.any_multi = 1;
+  }
+}
+
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_status_string(pa_status s) {
@@ -424,6 +468,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   void* ws = nullptr;
   size_t ws_bytes = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const int32_t* lens_host = nullptr;
   int engine = 0;
   if (ext) {
     engine = (ext->flags & PA_DECODE_VECTOR_REFERENCE) ? 1 : 0;
@@ -439,6 +484,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
     ws_bytes = ext->workspace_bytes;
     ev0 = static_cast<hipEvent_t>(ext->split_events[0]);
     ev1 = static_cast<hipEvent_t>(ext->split_events[1]);
+    lens_host = ext->seq_lens_host;
     // Without a usable device the launch below reports the HIP error; the
     // remaining host checks still run first.
     if (hipGetDevice(&device) != hipSuccess) device = 0;
@@ -518,6 +564,9 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.engine = engine;
   const float sc = (scale == 0.f) ? 1.0f / 16.0f : scale;
   prm.scale_log2 = sc * 1.4426950408889634f;
+  prm.hp.on = 0;
+  if (lens_host && n_seq <= pa::kHostPlanSeqs)
+    pa::host_plan(lens_host, n_seq, bt_stride * page_size, prm.target_items, prm.plan_budget, prm.hp);
   return hip_status(pa::launch_decode(prm, stream, ev0, ev1));
 }
 

@@ -34,6 +34,19 @@ inline int row_bytes_of(int t) {
   }
 }
 
+// The chunk plan computed on the host from a host copy of seq_lens (up to
+// kHostPlanSeqs sequences), carried in the launch arguments: the kernels then
+// locate their work item without reading seq_lens.  Same integer arithmetic
+// as the device plan (plan_wg), so both give the same chunks.
+constexpr int kHostPlanSeqs = 256;
+struct HostPlan {
+  int32_t on;                       // 1: the fields below hold the plan
+  int32_t chunk;                    // chunk length in positions
+  int32_t any_multi;                // some sequence has more than one chunk (the merge has work)
+  int32_t first[kHostPlanSeqs + 1]; // plan index of sequence s's first chunk; first[n_seq] = all pairs
+  int32_t len[kHostPlanSeqs];       // seq_lens
+};
+
 // Everything one decode launch needs.  Device pointers unless noted.
 struct DecodeParams {
   const float* q;          // [n_seq][n_qtok][24][256]
@@ -62,6 +75,7 @@ struct DecodeParams {
   int32_t k_type, v_type;
   int32_t engine;          // 0: matrix-core path, 1: fp32 vector reference path
   float scale_log2;        // softmax scale * log2(e)
+  HostPlan hp;             // hp.on == 0: the kernels compute the plan from seq_lens
 };
 
 // Upper bound on work items for n_seq sequences (see the plan in the kernels).
@@ -81,6 +95,16 @@ inline int64_t plan_target(int64_t n_seq, int64_t slots, int64_t cap) {
   if (t < 1) t = 1;
   return t < cap ? t : cap;
 }
+
+// Work items the split grid covers (per token group): the plan's exact count
+// with a host plan, else the bound max_items.
+inline int32_t grid_items(const DecodeParams& p) {
+  return p.hp.on ? kKvHeads * p.hp.first[p.n_seq] : p.max_items;
+}
+
+// Fills `hp` from host seq_lens (n_seq <= kHostPlanSeqs) with the device
+// plan's arithmetic for the given target and budget.
+void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, HostPlan& hp);
 
 // Resident workgroups per compute unit of the split kernel a call selects
 // (from the runtime's occupancy query; at least 1).

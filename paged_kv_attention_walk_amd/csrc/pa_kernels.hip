@@ -151,6 +151,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t e
   if (e != hipSuccess) return e;
   if (ev_end) e = hipEventRecord(ev_end, stream);
   if (e != hipSuccess) return e;
+  if (p.hp.on && !p.hp.any_multi) return hipSuccess;   // every sequence wrote its rows directly
   return launch_merge(p, stream);
 }
 

@@ -976,17 +976,17 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   const int item_id = blockIdx.x / p.n_groups;
   const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
   const int jj = item_id / kKvHeads, h = item_id % kKvHeads;
-  const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, jj, -1, sh_sum, sh_loc);
+  const PlanWG pl = plan_of(p, cap, jj, -1, sh_sum, sh_loc);
   // every value that places loads is wave-uniform (scalar registers)
   const int chunk = __builtin_amdgcn_readfirstlane(pl.chunk);
   const int s = __builtin_amdgcn_readfirstlane(pl.s), c = __builtin_amdgcn_readfirstlane(pl.c);
   if (s < 0) return;
-  if (tid == 0 && c == 0 && h == 0 && tok0 == 0) {      // the plan, for the merge kernel
+  if (!p.hp.on && tid == 0 && c == 0 && h == 0 && tok0 == 0) {   // the plan, for the merge kernel
     int32_t* hdr = reinterpret_cast<int32_t*>(p.err);
     if (s < kHdrSeqs) hdr[2 + s] = jj;
     if (s == 0) hdr[1] = chunk;
   }
-  const int L = __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
+  const int L = seq_len_of(p, s);
   const int nc = n_chunks_of(L, cap, chunk);
   // this chunk's partial rows in the workspace
   const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
@@ -1222,7 +1222,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 
 template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.max_items) * static_cast<unsigned>(p.n_groups));
+  const dim3 grid(static_cast<unsigned>(grid_items(p)) * static_cast<unsigned>(p.n_groups));
   hipLaunchKernelGGL((split_mfma_kernel<KT, VT, PA_T>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
   const int item_id = blockIdx.x / p.n_groups;
   const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
   const int j = item_id / kKvHeads, h = item_id % kKvHeads;
-  const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, j, -1, sh_sum, sh_loc);
+  const PlanWG pl = plan_of(p, cap, j, -1, sh_sum, sh_loc);
   const int chunk = pl.chunk, s = pl.s, c = pl.c;
   if (s < 0) return;
   if (tid == 0 && c == 0 && h == 0 && tok0 == 0) {      // the plan, for the merge kernel
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
     if (s < kHdrSeqs) hdr[2 + s] = j;
     if (s == 0) hdr[1] = chunk;
   }
-  const int L = p.seq_lens[s];
+  const int L = seq_len_of(p, s);
   const int nc = n_chunks_of(L, cap, chunk);
   const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
   const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of the group's token 0
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
 
 template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.max_items) * static_cast<unsigned>(p.n_groups));
+  const dim3 grid(static_cast<unsigned>(grid_items(p)) * static_cast<unsigned>(p.n_groups));
   hipLaunchKernelGGL((split_valu_kernel<KT, VT, PA_T>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

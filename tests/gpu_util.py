@@ -36,9 +36,11 @@ ENGINES = {"mfma": 0, "valu": pb.DECODE_VECTOR_REFERENCE}
 
 
 def run(w, *, contiguous=False, kc=None, vc=None, scale=None, lse=False, ws=None, dq=None, dk=None, dv=None,
-        dbt=None, dlens=None, out=None, events=None, stream=None, engine="mfma"):
+        dbt=None, dlens=None, out=None, events=None, stream=None, engine="mfma", host_plan=False):
     """Decode workload ``w`` (synth.Workload) through pa_decode with an ext.
-    Returns (out np.float32, lse np.float32 or None, error word)."""
+    With ``host_plan`` the ext carries a host copy of seq_lens (the plan is
+    computed on the host).  Returns (out np.float32, lse np.float32 or None,
+    error word)."""
     n_seq = len(w["seq_lens"])
     T = w["n_qtok"]
     P = w["page_size"]
@@ -61,7 +63,8 @@ def run(w, *, contiguous=False, kc=None, vc=None, scale=None, lse=False, ws=None
     lse_t = torch.empty((n_seq, T, 24), dtype=torch.float32, device="cuda") if lse else None
     ws = workspace(n_seq, T) if ws is None else ws
     ext = pb.make_ext(bt_stride, nblocks, w["scale"] if scale is None else scale, lse_t, ws, ws.numel() * 4,
-                      split_events=events, flags=ENGINES[engine])
+                      split_events=events, flags=ENGINES[engine],
+                      seq_lens_host=w["seq_lens"] if host_plan else None)
     pb.decode(dq, dk, dv, bt, dlens, T, kv, P, out, ext=ext, stream=stream)
     err = pb.device_error(ws, stream=stream)
     torch.cuda.synchronize()

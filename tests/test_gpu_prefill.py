@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 ENGINES = {"mfma": 0, "valu": pb.DECODE_VECTOR_REFERENCE}
 
 
-def run_prefill(w, *, engine="mfma", contiguous=False, kc=None, vc=None, dbt=None, lse=False, scale=None):
+def run_prefill(w, *, engine="mfma", contiguous=False, kc=None, vc=None, dbt=None, lse=False, scale=None,
+                host_plan=False):
     n_seq, T, P = len(w["seq_lens"]), w["n_qtok"], w["page_size"]
     kv = pb.kv_type(w["k_kind"], w["v_kind"])
     dq = dev(w["q"])
@@ -33,7 +34,7 @@ def run_prefill(w, *, engine="mfma", contiguous=False, kc=None, vc=None, dbt=Non
     n = pb.prefill_workspace_size(n_seq, T, torch.cuda.current_device())
     ws = torch.zeros(n // 4 + 64, dtype=torch.int32, device="cuda")
     ext = pb.make_ext(bt_stride, nb, w["scale"] if scale is None else scale, lse_t, ws, ws.numel() * 4,
-                      flags=ENGINES[engine])
+                      flags=ENGINES[engine], seq_lens_host=w["seq_lens"] if host_plan else None)
     st = pb.prefill_status(dq, dk, dv, bt, dlens, n_seq, T, kv, P, out, ext=ext)
     assert st == pb.OK, st
     err = pb.device_error(ws)
