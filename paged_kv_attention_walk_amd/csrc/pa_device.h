@@ -457,7 +457,7 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int tg = r / 6, grp = tg / 8;                    // token, and its group of 8
   const int lr = r - 48 * grp;                           // row within the group's partial rows
   const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cap = p.bt_stride * p.page_size;
   int chunk, first;
   if (p.hp.on) {                                         // the host's plan, in the launch arguments
@@ -472,12 +472,16 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
     chunk = pl.chunk;
     first = pl.prefix;
   }
-  const int nc = n_chunks_of(p.hp.on ? p.hp.len[s] : p.seq_lens[s], cap, chunk);
+  const int nc = n_chunks_of(seq_len_of(p, s), cap, chunk);
   if (nc <= 1) return;                                   // written by the split kernel
   const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(first) * kKvHeads + h;
   const size_t prows = static_cast<size_t>(p.part_rows);
-  const float* base_o = p.part_o + (item0 * prows + lr) * kHeadDim + 4 * lane;   // chunk c at item0 + 4c
-  const float* base_l = p.part_lse + item0 * prows + lr;
+  // chunk c's row is at item0 + 4c; its address is wave-uniform (scalar
+  // registers) plus this lane's 16-byte offset, and its log-sum-exp a scalar
+  // load (the workspace is read-only here)
+  const float* row_o = p.part_o + (item0 * prows + lr) * kHeadDim;
+  typedef __attribute__((address_space(4))) const float cfloat;
+  cfloat* row_l = reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(p.part_lse + item0 * prows + lr));
   const size_t cstride = static_cast<size_t>(kKvHeads) * prows;                 // rows between chunks
   // each batch: all its chunk outputs and log-sum-exps in flight at once,
   // then this wave's base m, weights 2^(x - m) and sums
@@ -490,10 +494,13 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
       const int c = c0 + 4 * u;
-      const bool in = c < nc;
-      o[u] = in ? *reinterpret_cast<const float4*>(base_o + static_cast<size_t>(c) * cstride * kHeadDim)
-                : make_float4(0.f, 0.f, 0.f, 0.f);
-      x[u] = in ? base_l[static_cast<size_t>(c) * cstride] : kNegInf;
+      if (c < nc) {
+        o[u] = reinterpret_cast<const float4*>(row_o + static_cast<size_t>(c) * cstride * kHeadDim)[lane];
+        x[u] = row_l[static_cast<size_t>(c) * cstride];
+      } else {
+        o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        x[u] = kNegInf;
+      }
     }
     float mb = m;
 #pragma unroll
@@ -502,12 +509,12 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
       mb = fmaxf(mb, x[u]);                              // fmaxf ignores a NaN operand
     }
     if (mb == kNegInf) continue;                         // no visible key in any chunk so far
-    const float a = (m == kNegInf) ? 0.f : exp2f(m - mb);
+    const float a = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m - mb);
     acc.x *= a; acc.y *= a; acc.z *= a; acc.w *= a;
     l *= a;
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const float b = (x[u] == kNegInf || x[u] != x[u]) ? 0.f : exp2f(x[u] - mb);
+      const float b = (x[u] == kNegInf || x[u] != x[u]) ? 0.f : __builtin_amdgcn_exp2f(x[u] - mb);
       acc.x += b * o[u].x; acc.y += b * o[u].y; acc.z += b * o[u].z; acc.w += b * o[u].w;
       l += b;
     }
