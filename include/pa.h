@@ -271,6 +271,27 @@ typedef struct pa_decode_ext {
 /* Largest batch whose plan pa_decode_ext.seq_lens_host can carry. */
 #define PA_HOST_PLAN_MAX_SEQS 256
 
+/* The split-K partition of a one-token decode call (occupancy-aware,
+ * ragged-length-aware context parallelism: lucebox pull 555, Summary;
+ * achyudh/llama.cpp pull 2, split-K decode commit), computed on the host with
+ * the same integer arithmetic pa_decode uses; for inspection and tests, no
+ * device needed.
+ *
+ * seq_lens_host  host int32 [n_seq] (0 <= n_seq <= PA_HOST_PLAN_MAX_SEQS);
+ *                a length < 0 or > cap counts as one empty chunk.
+ * cap            rows per sequence (bt_stride * page_size).
+ * n_cu, wgs_per_cu  compute units and resident split workgroups per compute
+ *                unit (pa_decode takes both from the device: 256 and 2 for a
+ *                one-token Q4_0 call on MI355X).
+ * Writes *chunk (positions per chunk, a multiple of 128), *n_items (work
+ * items = chunks x 4 KV heads) and, if first != NULL, first[s] = index of
+ * sequence s's first chunk for s = 0..n_seq (first[n_seq] = all chunks).
+ * Errors: PA_ERR_INVALID (null chunk / n_items, or seq_lens_host with
+ * n_seq > 0; n_seq, cap, n_cu or wgs_per_cu out of range); nothing is
+ * written then. */
+pa_status pa_split_plan(const int32_t *seq_lens_host, int32_t n_seq, int32_t cap, int32_t n_cu,
+                        int32_t wgs_per_cu, int32_t *chunk, int32_t *n_items, int32_t *first);
+
 /* One decode step (lucebox pull 555, Summary; achyudh/llama.cpp pull 2,
  * split-K decode and page-table commits).
  *

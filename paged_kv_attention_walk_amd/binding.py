@@ -34,7 +34,7 @@ EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "
            "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_append_kv_device",
            "pa_decode",
            "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather", "pa_prefill",
-           "pa_prefill_workspace_size")
+           "pa_prefill_workspace_size", "pa_split_plan")
 
 
 def kv_type(k, v=0) -> int:
@@ -101,6 +101,7 @@ def _lib():
             "pa_prefill_workspace_size": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
             "pa_get_device_error": (I32, [P, VP, VP, I32, ctypes.POINTER(I32)]),
             "pa_debug_gather": (I32, [VP, I32, VP, I32, I32, I32, I32, I32, VP, VP, VP]),
+            "pa_split_plan": (I32, [VP, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), VP]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -273,6 +274,18 @@ def prefill_status(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv, 
     return _lib().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
                              int(n_seq), int(n_qtok), kv if isinstance(kv, int) else kv_type(kv), int(page_size),
                              _ptr(out), _stream(stream), ctypes.byref(ext) if ext is not None else None)
+
+
+def split_plan(seq_lens, cap, n_cu=256, wgs_per_cu=2):
+    """pa_split_plan: (chunk, n_items, first[n_seq + 1]) of a one-token decode
+    call, computed on the host."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    n = int(lens.shape[0])
+    chunk, items = ctypes.c_int32(), ctypes.c_int32()
+    first = np.zeros(n + 1, dtype=np.int32)
+    _check(_lib().pa_split_plan(lens.ctypes.data if n else None, n, int(cap), int(n_cu), int(wgs_per_cu),
+                                ctypes.byref(chunk), ctypes.byref(items), first.ctypes.data), "pa_split_plan")
+    return chunk.value, items.value, first
 
 
 def prefill_workspace_size(n_seq, n_qtok, device=0) -> int:

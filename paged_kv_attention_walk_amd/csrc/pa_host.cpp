@@ -443,6 +443,22 @@ int64_t workspace_items(int64_t n_seq, int n_qtok, bool prefill, int device) {
 
 int workspace_rows_tokens(int n_qtok, bool prefill) { return prefill ? kGroupTokens : n_qtok; }
 
+// Item target, grid bound and one-round budget of the chunk plan for
+// `slots` resident split workgroups, with `cap_target` the target the
+// workspace was sized for.
+struct PlanParams {
+  int64_t target, max_items, budget;
+};
+PlanParams plan_params(int64_t n_seq, int64_t slots, int64_t cap_target) {
+  PlanParams r;
+  r.target = pa::plan_target(n_seq, slots, cap_target);
+  r.max_items = pa::max_work_items(n_seq, r.target);
+  // when every item fits one round, the plan may shorten the chunk as long
+  // as the items stay within the grid (max_items)
+  r.budget = (2 * static_cast<int64_t>(pa::kKvHeads) * n_seq <= slots) ? r.max_items : 0;
+  return r;
+}
+
 // Decode and prefill: one implementation, the prefill taking its query
 // tokens in groups of 8 (one token group per workgroup).
 pa_status attend(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
@@ -548,12 +564,10 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   const int cu = cu_count(device);
   const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, kernel_tok, engine);
   const int64_t per_group_slots = slots / groups > 0 ? slots / groups : 1;
-  const int64_t plan = pa::plan_target(n_seq, per_group_slots, target);
-  prm.target_items = static_cast<int32_t>(plan);
-  prm.max_items = static_cast<int32_t>(pa::max_work_items(n_seq, plan));
-  // when every item fits one round, the plan may shorten the chunk as long
-  // as the items stay within the grid (max_items)
-  prm.plan_budget = (2 * static_cast<int64_t>(pa::kKvHeads) * n_seq <= per_group_slots) ? prm.max_items : 0;
+  const PlanParams pp = plan_params(n_seq, per_group_slots, target);
+  prm.target_items = static_cast<int32_t>(pp.target);
+  prm.max_items = static_cast<int32_t>(pp.max_items);
+  prm.plan_budget = static_cast<int32_t>(pp.budget);
   prm.tok_total = n_qtok;
   prm.tok0 = 0;
   prm.n_groups = 1;
@@ -584,6 +598,28 @@ pa_status pa_prefill(const float* q, const void* k_pool, const void* v_pool, con
                      float* out, hipStream_t stream, const pa_decode_ext* ext) {
   return attend(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv_type, page_size, out, stream, ext,
                 true);
+}
+
+pa_status pa_split_plan(const int32_t* seq_lens_host, int32_t n_seq, int32_t cap, int32_t n_cu, int32_t wgs_per_cu,
+                        int32_t* chunk, int32_t* n_items, int32_t* first) {
+  if (!chunk || !n_items || n_seq < 0 || n_seq > PA_HOST_PLAN_MAX_SEQS || cap < 1 || n_cu < 1 || wgs_per_cu < 1 ||
+      (n_seq > 0 && !seq_lens_host))
+    return PA_ERR_INVALID;
+  if (n_seq == 0) {
+    *chunk = 0;
+    *n_items = 0;
+    if (first) first[0] = 0;
+    return PA_OK;
+  }
+  const PlanParams pp = plan_params(n_seq, static_cast<int64_t>(n_cu) * wgs_per_cu,
+                                    static_cast<int64_t>(n_cu) * kTargetPerCu);
+  pa::HostPlan hp;
+  pa::host_plan(seq_lens_host, n_seq, cap, static_cast<int>(pp.target), static_cast<int>(pp.budget), hp);
+  *chunk = hp.chunk;
+  *n_items = pa::kKvHeads * hp.first[n_seq];
+  if (first)
+    for (int i = 0; i <= n_seq; ++i) first[i] = hp.first[i];
+  return PA_OK;
 }
 
 pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
