@@ -115,3 +115,28 @@ def test_host_plan_prefill(engine):
     _same(od, oh, "prefill out")
     _same(ld, lh, "prefill lse")
     parity(oh, _oracle(w)[0], what="host plan prefill")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_device_plan_equals_host_plan(seed):
+    # the device-planned split kernel leaves its chunk length and each
+    # sequence's first chunk in the workspace header (words 1 and 2 + s, up to
+    # 62 sequences); they must equal pa_split_plan's for this device's CU count
+    # and the kernel's two resident workgroups per CU (one-token Q4_0)
+    import torch
+    from paged_kv_attention_walk_amd import binding as pb
+    rng = np.random.default_rng(470 + seed)
+    n = int(rng.integers(2, 40))
+    lens = [int(x) for x in rng.integers(0, 6000, size=n)]
+    lens[0] = 20000
+    w = synth.make_workload(f"hp_dev_{seed}", lens, 1, "q4_0", "q4_0", 16, table="shuffled", seed=481 + seed)
+    log(f"[case] device plan header vs pa_split_plan, {n} sequences, seed {seed}")
+    from gpu_util import workspace
+    ws = workspace(n, 1)
+    _, _, err = run(w, ws=ws)
+    assert err == 0
+    hdr = ws[:2 + n].cpu().numpy()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    chunk, items, first = pb.split_plan(w["seq_lens"], w["block_table"].shape[1] * 16, n_cu, 2)
+    assert hdr[1] == chunk, (hdr[1], chunk)
+    assert list(hdr[2:2 + n]) == list(first[:n])
