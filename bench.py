@@ -77,6 +77,30 @@ def copy_ceiling(steps=20, nbytes=2 << 30):
             "read_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1), "read_plus_write_gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def read_ceiling(steps=20, nbytes=2 << 30):
+    """HBM read rate of pa_read_bandwidth_probe (16-byte loads, every byte of
+    `nbytes` read once) on this machine: the practical ceiling of the K/V stream,
+    reported beside the 8 TB/s nominal peak."""
+    import torch
+    from paged_kv_attention_walk_amd import binding as pb
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(32 * n_cu, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pb.read_bandwidth_probe(a, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        pb.read_bandwidth_probe(a, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del a, sink
+    return {"kernel": "pa_read_bandwidth_probe over 2 GiB (16-byte loads)", "bytes_read": nbytes, "ms": round(ms, 4),
+            "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("pa_mfma.hip", "pa_kernels.hip", "pa_device.h", "pa_internal.h"):
@@ -142,6 +166,7 @@ def main():
     if args.ceiling:
         print(json.dumps({"copy_ceiling": copy_ceiling()}), flush=True)
         return
+    ceiling = read_ceiling()
     t_gen = time.perf_counter()
     if args.workload == "ragged":
         w = synth.config3()
@@ -302,6 +327,7 @@ def main():
     roofline = {"kernel": SPLIT_KERNEL, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w["name"]),
                 "split_kernel_ms_mean": round(cold_k, 5), "split_kernel_ms_median": round(cold_k_med, 5)}
+    roofline["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
     tflops = flops / (cold_k * 1e-3) / 1e12
     if flops / kv_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):   # past the ridge point
         roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
@@ -339,6 +365,7 @@ def main():
         "plan": args.plan,
         "other_plan": other_plan,
         "roofline": roofline,
+        "read_ceiling": ceiling,
         "split_tflops": round(tflops, 2),
         "cpu_baseline": None,
     }

@@ -375,6 +375,20 @@ pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t devic
 pa_status pa_get_device_error(pa_pool *pool, void *workspace, hipStream_t stream,
                               int32_t clear, int32_t *err);
 
+/* Measurement helper: reads `bytes` (a multiple of 16) of device memory at
+ * `src` (16-byte aligned) once with 16-byte loads, 8 workgroups per compute
+ * unit in a grid-stride loop with four loads in flight per lane, and folds
+ * them into one word per wave written to `sink` (device, at least
+ * 32 x compute-unit-count words).  Time it to get the HBM read rate that a
+ * pure stream of 16-byte loads reaches on this device, the practical ceiling
+ * for the K/V stream of pa_decode (the bound the decode roofline refers to:
+ * lucebox pull 555 and achyudh/llama.cpp pull 2 report their decode
+ * throughput as a share of the card's bandwidth).  Enqueued on `stream`.
+ * Errors: PA_ERR_INVALID (null or misaligned pointers, bytes 0 or not a
+ * multiple of 16, sink too small), PA_ERR_HIP. */
+pa_status pa_read_bandwidth_probe(const void *src, size_t bytes, uint32_t *sink, size_t sink_words,
+                                  hipStream_t stream);
+
 /* Test hook: copies the logical rows [0, seq_len) of sequence `seq` of one
  * pool (K or V, row size row_bytes) through its block-table row into dst
  * (device, [4][seq_len][row_bytes]), using the same row-address helper as the

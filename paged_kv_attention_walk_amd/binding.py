@@ -34,7 +34,7 @@ EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "
            "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_append_kv_device",
            "pa_decode",
            "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather", "pa_prefill",
-           "pa_prefill_workspace_size", "pa_split_plan")
+           "pa_prefill_workspace_size", "pa_split_plan", "pa_read_bandwidth_probe")
 
 
 def kv_type(k, v=0) -> int:
@@ -102,6 +102,7 @@ def _lib():
             "pa_get_device_error": (I32, [P, VP, VP, I32, ctypes.POINTER(I32)]),
             "pa_debug_gather": (I32, [VP, I32, VP, I32, I32, I32, I32, I32, VP, VP, VP]),
             "pa_split_plan": (I32, [VP, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), VP]),
+            "pa_read_bandwidth_probe": (I32, [VP, SZ, VP, SZ, VP]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -286,6 +287,13 @@ def split_plan(seq_lens, cap, n_cu=256, wgs_per_cu=2):
     _check(_lib().pa_split_plan(lens.ctypes.data if n else None, n, int(cap), int(n_cu), int(wgs_per_cu),
                                 ctypes.byref(chunk), ctypes.byref(items), first.ctypes.data), "pa_split_plan")
     return chunk.value, items.value, first
+
+
+def read_bandwidth_probe(src, sink, stream=None):
+    """pa_read_bandwidth_probe over the whole of device tensor `src` (its size
+    a multiple of 16 bytes), folding into device int32/uint32 tensor `sink`."""
+    _check(_lib().pa_read_bandwidth_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
+                                          _stream(stream)), "pa_read_bandwidth_probe")
 
 
 def prefill_workspace_size(n_seq, n_qtok, device=0) -> int:

@@ -644,6 +644,17 @@ pa_status pa_get_device_error(pa_pool* pool, void* workspace, hipStream_t stream
   return PA_OK;
 }
 
+pa_status pa_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                                  hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || !aligned(src, 16) || !aligned(sink, 4)) return PA_ERR_INVALID;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) device = 0;
+  const int cu = cu_count(device);
+  const int64_t blocks = static_cast<int64_t>(cu > 0 ? cu : 256) * 8;
+  if (static_cast<int64_t>(sink_words) < blocks * 4) return PA_ERR_INVALID;
+  return hip_status(pa::launch_read_probe(src, bytes, sink, static_cast<int32_t>(blocks), stream));
+}
+
 pa_status pa_debug_gather(const void* pool, int32_t row_bytes, const int32_t* block_table, int32_t bt_stride,
                           int32_t n_pool_blocks, int32_t seq, int32_t seq_len, int32_t page_size, void* dst,
                           int32_t* err_word, hipStream_t stream) {

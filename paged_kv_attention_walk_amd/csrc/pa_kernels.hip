@@ -77,6 +77,30 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
   }
 }
 
+// ------------------------------------------------------- read ceiling
+//
+// Reads n16 16-byte words once each (grid-stride, four loads in flight per
+// lane) and folds them with xor; one word per wave goes to `sink` so that
+// nothing is optimised away.  The HBM read rate the decode kernels are
+// compared against.
+__global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint4* __restrict__ src, size_t n16,
+                                                              uint32_t* __restrict__ sink) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+  size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m, 64);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = acc;
+}
+
 // ------------------------------------------------------------- dispatch
 
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
@@ -160,6 +184,12 @@ hipError_t launch_scatter(const uint8_t* staging, int32_t n_rows, uint8_t* k_poo
   if (n_rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(scatter_kernel, dim3(n_rows), dim3(kThreads), 0, stream, staging, n_rows, k_pool, v_pool,
                      rb_k, rb_v, page_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<const uint4*>(src), bytes / 16, sink);
   return hipGetLastError();
 }
 

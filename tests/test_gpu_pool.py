@@ -167,3 +167,19 @@ def test_append_scatter_mixed_types_bitexact():
     assert np.array_equal(kp.cpu().numpy(), pool_model.scatter_rows(np.zeros((nb, 4, P, rbk), np.uint8), blocks, slots, krows))
     assert np.array_equal(vp.cpu().numpy(), pool_model.scatter_rows(np.zeros((nb, 4, P, rbv), np.uint8), blocks, slots, vrows))
     pool.destroy()
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 97, 1 << 20, (1 << 24) + 16 * 13])
+def test_read_bandwidth_probe_reads_every_word_once(nbytes):
+    # the probe folds what it reads with xor: the xor of its output words is the
+    # xor of every 32-bit word of the buffer exactly when each is read once
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(-2**31, 2**31 - 1, size=nbytes // 4, dtype=np.int64).astype(np.int32)
+    log(f"[case] read probe over {nbytes} bytes")
+    src = torch.from_numpy(host).cuda()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.full((32 * n_cu,), 0, dtype=torch.int32, device="cuda")
+    pb.read_bandwidth_probe(src, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy())
+    assert got == np.bitwise_xor.reduce(host)
