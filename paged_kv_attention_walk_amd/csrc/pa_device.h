@@ -1,5 +1,5 @@
 // Device helpers shared by the decode kernels: the row-address helper, the
-// chunk plan, wave reductions, row decoding and the fused merge.
+// chunk plan, wave reductions, row decoding and the merge of chunk partials.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -10,9 +10,11 @@
 //    live length and an occupancy target (a multiple of the compute-unit
 //    count), so a sequence gets chunks in proportion to its length and the
 //    item count stays near the target whatever the length mix;
-//  * the plan is a pure function of seq_lens, n_qtok and the target, computed
-//    by every workgroup from seq_lens on the device (no host round trip), and
-//    identical for paged and contiguous storage;
+//  * the plan is a pure function of seq_lens, n_qtok and the target, and
+//    identical for paged and contiguous storage.  Every workgroup computes it
+//    from seq_lens on the device (no host round trip), or, when the caller
+//    also passes the lengths on the host, the host computes it with the same
+//    arithmetic and it arrives with the launch arguments;
 //  * each chunk writes its normalised output and log-sum-exp; a sequence with
 //    one chunk writes the final output directly, the others are combined by
 //    the merge kernel.

@@ -1,6 +1,6 @@
 // Matrix-core split kernel of the paged decode (gfx950).
 //
-// Same work items, plan and fused merge as the vector path; the per-chunk
+// Same work items, plan and merge kernel as the vector path; the per-chunk
 // math runs on v_mfma_f32_16x16x32_{f16,bf16}.  One workgroup = one
 // (sequence, KV head, chunk); its 4 waves take 32-key tiles of the chunk in
 // turn, each wave with its own running max / sum / output.
@@ -9,9 +9,11 @@
 // table is read once per half -- llama.cpp pull 2, page-table commit, resolves
 // its table once per chunk of keys rather than per key):
 //  * QK^T as S^T = K Q^T: the A operand is 16 keys x 32 dims of one
-//    quantisation block, loaded straight from HBM into registers (a lane
-//    holds 8 dims of one key) and converted in-register to exact f16 values
-//    (codes for Q8_0 / Q4_0); the B operand is the 6*T query rows of the
+//    quantisation block, loaded from HBM straight into operand registers (a
+//    lane holds 8 dims of one key; Q4_0 rows instead arrive as contiguous
+//    16-byte pieces, are kept raw in LDS and read from there) and converted
+//    in-register to exact f16 values (codes for Q8_0 / Q4_0); the B operand
+//    is the 6*T query rows of the
 //    KV head (padded to 16 or 32), split as q = q_hi + q_lo in f16 (bf16 for
 //    BF16 K) so the products carry ~22 bits.  For Q8_0 / Q4_0 the block scale
 //    is applied per key to the fp32 result of each block's MFMA, so codes
@@ -23,8 +25,10 @@
 //    scales split apart), and the gfx950 LDS transpose reads
 //    (ds_read_b64_tr_b4 / _b8 / _b16) deliver the V^T operand -- 8 keys of one
 //    dim per lane -- in one read per block (Q4_0), per 16 dims (Q8_0) or two
-//    per 16 dims (F16 / BF16); the per-key V scale is folded into the
-//    probabilities, P' = p * d_v, split hi + lo like q.
+//    per 16 dims (F16 / BF16).  For Q8_0 / Q4_0 the operand is the code
+//    times the per-key block scale, split exactly into f16 hi + lo parts (a
+//    code times an fp16 scale has at most 19 significant bits), and the
+//    probabilities are split hi + lo like q.
 // Accumulation is fp32 throughout.
 //
 // This source is built once per query-token count T (-DPA_T=T, 1..8): the
