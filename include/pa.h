@@ -53,7 +53,10 @@ typedef int32_t pa_status;
 /* Static text for a status code. */
 const char *pa_status_string(pa_status s);
 
-/* Library version, "major.minor.patch". */
+/* Library version, "major.minor.patch".  The minor number changes when a
+ * struct of this header grows: 0.2 added pa_decode_ext.seq_lens_host,
+ * pa_split_plan and pa_read_bandwidth_probe. */
+#define PA_VERSION_STRING "0.2.0"
 const char *pa_version(void);
 
 /* ------------------------------------------------------------------ types */

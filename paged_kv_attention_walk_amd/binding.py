@@ -17,6 +17,7 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa_walk.so")
+ABI_VERSION = "0.2.0"      # the library version whose structs this binding mirrors
 
 F16, BF16, Q8_0, Q4_0 = 1, 2, 3, 4
 F32 = 5                                   # a source type of pa_append_kv_device only
@@ -108,6 +109,10 @@ def _lib():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        got = lib.pa_version().decode()
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} is version {got}, this binding mirrors {ABI_VERSION}: rebuild it with "
+                               "`python -m paged_kv_attention_walk_amd.build`")
         _LIB = lib
     return _LIB
 

@@ -186,7 +186,7 @@ const char* pa_status_string(pa_status s) {
   }
 }
 
-const char* pa_version(void) { return "0.1.0"; }
+const char* pa_version(void) { return PA_VERSION_STRING; }
 
 size_t pa_row_bytes(int32_t t) { return static_cast<size_t>(pa::row_bytes_of(t)); }
 

@@ -29,6 +29,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     assert set(pb.EXPORTS) == set(names)
     assert pb.version().count(".") == 2
+    assert pb.version() == pb.ABI_VERSION
 
 
 def test_row_bytes_and_status_strings():
