@@ -34,10 +34,23 @@ def _oracle_head(w, s, h, patch=None):
     return out
 
 
+def _bench_route(w, **kw):
+    """The decode as the benchmark launches it (split-K plan computed on the
+    host from a host copy of seq_lens), checked bitwise against the
+    device-planned call of the same inputs."""
+    out, lse, err = run(w, host_plan=True, **kw)
+    out_d, lse_d, err_d = run(w, **kw)
+    assert err == err_d
+    assert np.array_equal(out.view(np.int32), out_d.view(np.int32)), "host- and device-planned outputs differ"
+    if lse is not None:
+        assert np.array_equal(lse.view(np.int32), lse_d.view(np.int32))
+    return out, lse, err
+
+
 def test_uniform_8x4096_q4_0_whole():
     w = synth.config2()
     log("[case] uniform 8 x 4096 Q4_0, whole output")
-    out, _, err = run(w)
+    out, _, err = _bench_route(w)
     assert err == 0
     ref, _ = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q4_0", "q4_0", w["block_table"],
                                     w["seq_lens"], w["scale"])
@@ -48,7 +61,7 @@ def test_uniform_8x4096_q4_0_whole():
 def test_ragged_128k_7x8k_q4_0_sampled(engine):
     w = synth.config3()
     log(f"[case] ragged 131072 + 7 x 8192 Q4_0, sampled heads, {engine}")
-    out, _, err = run(w, engine=engine)
+    out, _, err = _bench_route(w, engine=engine)
     assert err == 0
     for s, h in [(0, 0), (0, 3), (1, 1), (7, 2)]:
         ref = _oracle_head(w, s, h)
@@ -59,7 +72,7 @@ def test_ragged_128k_7x8k_q4_0_sampled(engine):
 def test_mtp_q8_0_sampled(ctx, T):
     w = synth.config4(ctx=ctx, n_qtok=T)
     log(f"[case] Q8_0 single sequence ctx={ctx} T={T}, sampled heads")
-    out, _, err = run(w)
+    out, _, err = _bench_route(w)
     assert err == 0
     for h in (1, 2):
         parity(out[0][:, 6 * h:6 * h + 6][None], _oracle_head(w, 0, h)[None], what=f"mtp ctx={ctx} T={T} head {h}")
@@ -82,7 +95,7 @@ def test_serving_128_streams_append_then_decode_sampled():
     pool.append_kv_device(dev(blocks), dev(slots), dev(xk), dev(xv), "f32")
     torch.cuda.synchronize()
     assert pool.device_error() == 0
-    out, _, err = run(w, dk=kp, dv=vp)
+    out, _, err = _bench_route(w, dk=kp, dv=vp)
     assert err == 0
     rng = np.random.default_rng(12)
     picks = [int(x) for x in rng.choice(n_seq, size=6, replace=False)]
@@ -108,7 +121,7 @@ def test_many_sequences_with_long_ones(n_seq, engine):
     lens[0] = 0
     w = synth.make_workload(f"many_{n_seq}", lens, 2, "q4_0", "q8_0", 16, table="shuffled", seed=900 + n_seq)
     log(f"[case] {n_seq} sequences (4 long), {engine}")
-    out, lse, err = run(w, lse=True, engine=engine)
+    out, lse, err = _bench_route(w, lse=True, engine=engine)
     assert err == 0
     ref, rlse = attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], "q4_0", "q8_0", w["block_table"],
                                        w["seq_lens"], w["scale"])
