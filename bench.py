@@ -43,6 +43,11 @@ def parse():
                          "(encoded to BF16 into its page) followed by the decode; prefill: one --ctx-position "
                          "sequence, Q8_0 K and Q4_0 V, whose last --qtok positions are the new tokens (pa_prefill)")
     ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp / prefill")
+    ap.add_argument("--append", default="device", choices=["device", "host"],
+                    help="serving: the per-step append of one row per stream; device: pa_append_kv_device (float32 "
+                         "rows already on the GPU, encoded into the pool's BF16 on the way in); host: pa_append_kv "
+                         "(rows already BF16-encoded in host memory, one packed upload through pinned staging and a "
+                         "scatter kernel)")
     ap.add_argument("--ctx", type=int, default=16384, help="context for --workload prefill")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
     ap.add_argument("--plan", default="host", choices=["host", "device"],
@@ -242,7 +247,16 @@ def main():
         xv = torch.from_numpy(synth.normal((n_seq, 4, 256), seed=506)).cuda()
         append_pools = [pb.Pool(nblocks, P, kv, k_pool=kp, v_pool=vp, max_seqs=1, max_blocks_per_seq=bt_stride)
                         for kp, vp in pools]
-        append = {"rows": n_seq, "src": "f32", "keep": (dst_block, dst_slot, xk, xv)}
+        for ap_pool in append_pools:      # every page of the pool is in use (allocated through pa_alloc_blocks)
+            ap_pool.alloc(nblocks)
+        append = {"rows": n_seq, "src": "f32" if args.append == "device" else "bf16 rows in host memory",
+                  "entry": "pa_append_kv_device" if args.append == "device" else "pa_append_kv",
+                  "keep": (dst_block, dst_slot, xk, xv)}
+        # host route: the same rows, encoded to the pool's BF16 on the host
+        h_block = w["block_table"][np.arange(n_seq), last // P].astype(np.int32)
+        h_slot = (last % P).astype(np.int32)
+        h_k = synth.encode(xk.cpu().numpy(), w["k_kind"])
+        h_v = synth.encode(xv.cpu().numpy(), w["v_kind"])
 
     def make_call(kp, vp, bt, nb, pool=None, plan=args.plan):
         """A step with every pointer and the ext struct prepared up front, so
@@ -253,17 +267,20 @@ def main():
         a = (dq.data_ptr(), kp.data_ptr(), vp.data_ptr(), bt.data_ptr() if bt is not None else None,
              dlens.data_ptr(), n_seq, T, kv, P, out.data_ptr(), stream)
         ap = None
-        if pool is not None:
+        if pool is not None and args.append == "device":
             ap = (pool._h, n_seq, dst_block.data_ptr(), dst_slot.data_ptr(), xk.data_ptr(), xv.data_ptr(), pb.F32,
                   ws.data_ptr(), stream)
+        elif pool is not None:
+            ap = (pool._h, n_seq, h_block.ctypes.data, h_slot.ctypes.data, h_k.ctypes.data, h_v.ctypes.data, stream)
+        append_fn = lib.pa_append_kv_device if args.append == "device" else lib.pa_append_kv
 
         entry = lib.pa_prefill if prefill else lib.pa_decode
 
         def f(events):
             if ap is not None:
-                st = lib.pa_append_kv_device(*ap)
+                st = append_fn(*ap)
                 if st != pb.OK:
-                    raise pb.PaError(st, "pa_append_kv_device")
+                    raise pb.PaError(st, "pa_append_kv_device" if args.append == "device" else "pa_append_kv")
             ext.split_events[0], ext.split_events[1] = (events if events else (None, None))
             st = entry(*a, ext_ref)
             if st != pb.OK:
