@@ -28,7 +28,8 @@ struct Staging {
   void* host = nullptr;    // pinned
   void* dev = nullptr;
   size_t bytes = 0;
-  hipEvent_t done = nullptr;  // recorded after the slot's scatter kernel
+  hipEvent_t done = nullptr;    // recorded after the slot's scatter kernel
+  hipEvent_t copied = nullptr;  // recorded after the slot's host-to-device copy
   bool used = false;
 };
 
@@ -43,6 +44,7 @@ struct pa_pool {
   size_t workspace_bytes = 0;
   Staging staging[kStagingSlots];
   int next_slot = 0;
+  hipStream_t copy_stream = nullptr;   // the staging uploads (default priority)
   BlockAllocator alloc;
   std::mutex mu;
   explicit pa_pool(int32_t n) : alloc(n) {}
@@ -115,9 +117,18 @@ void free_pool_resources(pa_pool* p) {
       (void)hipEventSynchronize(s.done);
       (void)hipEventDestroy(s.done);
     }
+    if (s.copied) {
+      (void)hipEventSynchronize(s.copied);
+      (void)hipEventDestroy(s.copied);
+    }
     if (s.host) (void)hipHostFree(s.host);
     if (s.dev) (void)hipFree(s.dev);
     s = Staging{};
+  }
+  if (p->copy_stream) {
+    (void)hipStreamSynchronize(p->copy_stream);
+    (void)hipStreamDestroy(p->copy_stream);
+    p->copy_stream = nullptr;
   }
   if (p->workspace) (void)hipFree(p->workspace);
   p->workspace = nullptr;
@@ -254,7 +265,9 @@ pa_status pa_pool_create(const pa_pool_desc* d, pa_pool** out) {
     st = hip_status(hipHostMalloc(&s.host, sbytes, hipHostMallocDefault));
     if (st == PA_OK) st = hip_status(hipMalloc(&s.dev, sbytes));
     if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&s.done, hipEventDisableTiming));
+    if (st == PA_OK) st = hip_status(hipEventCreateWithFlags(&s.copied, hipEventDisableTiming));
   }
+  if (st == PA_OK) st = hip_status(hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking));
   if (st == PA_OK) {
     std::lock_guard<std::mutex> lk(g_registry_mu);
     if (g_registry.count(p->desc.k_pool)) st = PA_ERR_INVALID;
@@ -375,8 +388,14 @@ pa_status pa_append_kv(pa_pool* p, int32_t n_rows, const int32_t* dst_block, con
       std::memcpy(h + koff + r * krow, static_cast<const uint8_t*>(k_rows) + i * krow, krow);
       std::memcpy(h + voff + r * vrow, static_cast<const uint8_t*>(v_rows) + i * vrow, vrow);
     }
+    // The upload runs on the pool's own copy stream, so that it overlaps work
+    // already enqueued on `stream` (the previous decode); `stream` waits for
+    // it before the scatter.  The slot's previous scatter has finished (the
+    // wait above), so nothing still reads its device staging.
     const size_t bytes = pa::staging_bytes(n, p->rb_k, p->rb_v);
-    hipError_t e = hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, stream);
+    hipError_t e = hipMemcpyAsync(sl.dev, sl.host, bytes, hipMemcpyHostToDevice, p->copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(sl.copied, p->copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, sl.copied, 0);
     if (e == hipSuccess)
       e = pa::launch_scatter(static_cast<const uint8_t*>(sl.dev), n, static_cast<uint8_t*>(p->desc.k_pool),
                              static_cast<uint8_t*>(p->desc.v_pool), p->rb_k, p->rb_v, P, stream);
