@@ -185,9 +185,13 @@ pa_status pa_free_blocks(pa_pool *pool, int32_t n, const pa_block *handles);
  * puts them in place).  Row i goes to page dst_block[i], slot dst_slot[i], for
  * all 4 KV heads.  k_rows / v_rows (host) are [n_rows][4][row_bytes], already
  * encoded in the pool's K / V encodings.  dst_block / dst_slot are host
- * arrays.  The call copies indices and rows into pinned staging, enqueues one
- * host-to-device copy per staging batch (max_append_rows rows) and one
- * scatter kernel per batch on `stream`, and returns.  A caller appending
+ * arrays.  The call copies indices and rows into pinned staging and enqueues
+ * one host-to-device copy per staging batch (max_append_rows rows) on the
+ * pool's own copy stream, so that the transfer overlaps work already on
+ * `stream`.  It then makes `stream` wait for the copy, enqueues one scatter
+ * kernel per batch on `stream`, and returns.  The host waits only when a
+ * staging slot is still in use by an earlier batch.  It is not for graph
+ * capture: host copies and waits happen in the call.  A caller appending
  * position L of a sequence passes the page holding L and slot L % page_size:
  * the new row's position is the committed length (lucebox pull 555, Summary,
  * first-token bookkeeping fix).  Two rows with the same destination leave
