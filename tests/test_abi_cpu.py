@@ -207,3 +207,16 @@ def test_workspace_size_is_accepted_and_needed():
         for T in range(1, 9):
             st = pb.decode_status(a, a, a, a, a, n_seq, T, pb.kv_type("q4_0"), 16, a, 0, big)
             assert st != pb.ERR_INVALID, (n_seq, T)
+
+
+def test_read_bandwidth_probe_host_checks():
+    # argument errors come back before any HIP call (addresses are never touched)
+    lib = pb.lib()
+    a = 1 << 20                                          # a 16-byte aligned stand-in address
+    assert lib.pa_read_bandwidth_probe(None, 1024, a, 1 << 20, None) == pb.ERR_INVALID      # null source
+    assert lib.pa_read_bandwidth_probe(a, 1024, None, 1 << 20, None) == pb.ERR_INVALID      # null sink
+    assert lib.pa_read_bandwidth_probe(a, 0, a, 1 << 20, None) == pb.ERR_INVALID            # nothing to read
+    assert lib.pa_read_bandwidth_probe(a, 1000, a, 1 << 20, None) == pb.ERR_INVALID         # not a multiple of 16
+    assert lib.pa_read_bandwidth_probe(a + 4, 1024, a, 1 << 20, None) == pb.ERR_INVALID     # misaligned source
+    assert lib.pa_read_bandwidth_probe(a, 1024, a + 2, 1 << 20, None) == pb.ERR_INVALID     # misaligned sink
+    assert lib.pa_read_bandwidth_probe(a, 1024, a, 4, None) == pb.ERR_INVALID               # sink too small
