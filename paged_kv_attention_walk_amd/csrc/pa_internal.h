@@ -86,12 +86,15 @@ inline int64_t max_work_items(int64_t n_seq, int64_t target_items) {
 // Item target of the chunk plan for `slots` co-resident workgroups.  The plan
 // yields at most target + 4 n_seq items, so when the sequences leave room the
 // target fills exactly one round of resident workgroups (no second wave of
-// short-lived workgroups, each paying the set-up again); otherwise half a
-// round of chunks goes on top of the one-item-per-(sequence, head) minimum.
-// Never above `cap`, the target the workspace was sized for.
+// short-lived workgroups, each paying the set-up again).  Otherwise (many
+// sequences) the target is two rounds: chunks of half a slot's share, which
+// the hardware dispatcher spreads over the compute units as they free up, so
+// that the longest sequences of a ragged batch no longer set the time (a
+// target of half a round left every sequence in one chunk).  Never above
+// `cap`, the target the workspace was sized for.
 inline int64_t plan_target(int64_t n_seq, int64_t slots, int64_t cap) {
   const int64_t per = kKvHeads * n_seq;
-  int64_t t = (2 * per <= slots) ? slots - per : slots / 2;
+  int64_t t = (2 * per <= slots) ? slots - per : 2 * slots;
   if (t < 1) t = 1;
   return t < cap ? t : cap;
 }

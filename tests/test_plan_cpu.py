@@ -23,15 +23,15 @@ def _granule(c):
 
 def _model(lens, cap, n_cu, wgs):
     """The rule as stated: slots = CUs x resident workgroups; item target =
-    slots - 4 n_seq when 8 n_seq <= slots (one round) else slots / 2, capped at
-    4 per CU; chunk = ceil(4 sum(valid L) / target) rounded up to the granule;
+    slots - 4 n_seq when 8 n_seq <= slots (one round) else 2 slots (two
+    rounds), capped at 4 per CU; chunk = ceil(4 sum(valid L) / target) rounded up to the granule;
     in the one-round case the shortest of the four granule steps from
     ceil(4 sum L / budget) up whose items fit the budget (target + 4 n_seq),
     if shorter."""
     n = len(lens)
     slots = n_cu * wgs
     per = N_KV * n
-    target = slots - per if 2 * per <= slots else slots // 2
+    target = slots - per if 2 * per <= slots else 2 * slots
     target = max(1, min(target, n_cu * 4))
     total = sum(L for L in lens if 0 < L <= cap)
     chunk = _granule(-(-(total * N_KV) // target))
@@ -54,6 +54,17 @@ def _check_partition(lens, cap, chunk, items, first):
     for L, c in zip(lens, nc):                                  # chunks tile [0, L) exactly
         if 0 < L <= cap:
             assert (c - 1) * chunk < L <= c * chunk
+
+
+def test_many_stream_serving_workload_is_split():
+    # 128 streams of 513..8193 positions: chunks of about half a slot's share
+    # (2176 positions), 1280 items over two rounds of 512 resident workgroups,
+    # rather than one chunk per stream (the longest stream would set the time)
+    from paged_kv_attention_walk_amd import synth
+    w = synth.config5()
+    chunk, items, first = pb.split_plan(w["seq_lens"], w["block_table"].shape[1] * 64, 256, 2)
+    assert (chunk, items) == (2176, 1280)
+    assert int(np.max(np.diff(first))) > 1
 
 
 def test_headline_ragged_workload():
@@ -80,7 +91,7 @@ def test_random_batches_match_model_and_partition(n_cu, wgs):
         assert chunk == _model([int(x) for x in lens], cap, n_cu, wgs)
         _check_partition([int(x) for x in lens], cap, chunk, items, first)
         slots = n_cu * wgs
-        target = (slots - N_KV * n) if 2 * N_KV * n <= slots else slots // 2
+        target = (slots - N_KV * n) if 2 * N_KV * n <= slots else 2 * slots
         target = max(1, min(target, n_cu * 4))
         assert items <= target + N_KV * n                       # within the split grid
         if 2 * N_KV * n <= slots:
