@@ -49,6 +49,7 @@ def parse():
                          "(rows already BF16-encoded in host memory, one packed upload through pinned staging and a "
                          "scatter kernel)")
     ap.add_argument("--ctx", type=int, default=16384, help="context for --workload prefill")
+    ap.add_argument("--nseq", type=int, default=8, help="sequences of 4096 positions for --workload uniform")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
     ap.add_argument("--plan", default="host", choices=["host", "device"],
                     help="host: the call also passes a host copy of seq_lens (pa_decode_ext.seq_lens_host), so the "
@@ -178,7 +179,7 @@ def main():
     elif args.workload == "ragged_q8k_q4v":
         w = synth.ragged_mixed()
     elif args.workload == "uniform":
-        w = synth.config2()
+        w = synth.config2(n_seq=args.nseq)
     elif args.workload == "mtp":
         w = synth.config4(ctx=131072, n_qtok=args.qtok)
     elif args.workload == "serving":

@@ -86,6 +86,23 @@ __device__ inline void block_sum_vec(long long (&v)[kPlanCand], long long* sh) {
     v[k] = sh[k] + sh[kPlanCand + k] + sh[2 * kPlanCand + k] + sh[3 * kPlanCand + k];
 }
 
+// Block-wide maximum of a non-negative per-thread value (256 threads).  `sh`
+// holds 4 slots.
+__device__ inline long long block_max(long long v, long long* sh) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const long long o = __shfl_xor(v, d, 64);
+    v = o > v ? o : v;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long m = sh[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) m = sh[w] > m ? sh[w] : m;
+  return m;
+}
+
 __device__ inline long long round_granule(long long c) {
   c = (c + kChunkGranule - 1) / kChunkGranule * kChunkGranule;
   if (c < kChunkGranule) c = kChunkGranule;
@@ -101,13 +118,17 @@ __device__ inline long long round_granule(long long c) {
 // of them is shorter than the length from target.  Shorter chunks give each
 // wave fewer tiles.  `sh` holds kPlanShared slots.
 __device__ inline int plan_chunk(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
-                                 long long* sh) {
-  long long acc = 0;
+                                 int split, int slots, long long* sh) {
+  long long acc = 0, mx = 0;
   for (int i = threadIdx.x; i < n_seq; i += kThreads) {
     const int L = lens[i];
-    if (L > 0 && L <= cap) acc += L;
+    if (L > 0 && L <= cap) {
+      acc += L;
+      mx = L > mx ? L : mx;
+    }
   }
   const long long total = block_sum(acc, sh);
+  if (split > 0 && ragged_split(block_max(mx, sh), total, slots)) target = split;
   const long long c = round_granule((total * kKvHeads + target - 1) / target);
   if (budget <= 0 || total == 0) return static_cast<int>(c);
   const long long c0 = round_granule((total * kKvHeads + budget - 1) / budget);
@@ -359,10 +380,10 @@ __device__ inline int wave_sum_i(int v) {
 }
 
 __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
-                                 int j, int s_pref, long long* sh, int* shi) {
+                                 int split, int slots, int j, int s_pref, long long* sh, int* shi) {
   PlanWG r{0, -1, 0, 0};
   if (n_seq > 64) {
-    r.chunk = plan_chunk(lens, n_seq, cap, target, budget, sh);
+    r.chunk = plan_chunk(lens, n_seq, cap, target, budget, split, slots, sh);
     if (j >= 0) {
       plan_locate(lens, n_seq, cap, r.chunk, j, shi);
       r.s = shi[0];
@@ -376,6 +397,12 @@ __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, in
     const bool has = lane < n_seq;
     const int L = has ? lens[lane] : 0;
     const long long total = wave_sum_ll((has && L > 0 && L <= cap) ? L : 0);
+    if (split > 0) {
+      int mx = (has && L > 0 && L <= cap) ? L : 0;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d, 64));
+      if (ragged_split(mx, total, slots)) target = split;
+    }
     long long chunk = round_granule((total * kKvHeads + target - 1) / target);
     if (budget > 0 && total > 0) {
       const long long c0 = round_granule((total * kKvHeads + budget - 1) / budget);
@@ -441,7 +468,8 @@ __device__ inline PlanWG plan_of(const DecodeParams& p, int cap, int j, int s_pr
     if (s_pref >= 0) r.prefix = p.hp.first[s_pref];
     return r;
   }
-  return plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, j, s_pref, sh, shi);
+  return plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, p.split_target, p.plan_slots, j, s_pref,
+                 sh, shi);
 }
 
 // seq_lens[s], from the launch arguments with a host plan.
@@ -468,7 +496,8 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
     chunk = hdr[1];
     first = hdr[2 + s];
   } else {
-    const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, -1, s, sh.sum, sh.ints);
+    const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, p.split_target, p.plan_slots,
+                              -1, s, sh.sum, sh.ints);
     chunk = pl.chunk;
     first = pl.prefix;
   }

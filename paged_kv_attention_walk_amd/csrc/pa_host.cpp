@@ -144,16 +144,20 @@ static_assert(PA_HOST_PLAN_MAX_SEQS == kHostPlanSeqs, "host plan limit of the AB
 static_assert(sizeof(DecodeParams) <= 4096, "launch arguments stay within 4 KB");
 
 // The device plan (plan_wg / plan_chunk) in host arithmetic.
-void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, HostPlan& hp) {
+void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, int split, int slots, HostPlan& hp) {
   auto n_chunks = [cap](int L, int chunk) { return (L <= 0 || L > cap) ? 1 : (L + chunk - 1) / chunk; };
   auto granule = [](long long c) {
     c = (c + kChunkGranule - 1) / kChunkGranule * kChunkGranule;
     if (c < kChunkGranule) c = kChunkGranule;
     return c > (1ll << 30) ? (1ll << 30) : c;
   };
-  long long total = 0;
+  long long total = 0, mx = 0;
   for (int i = 0; i < n_seq; ++i)
-    if (lens[i] > 0 && lens[i] <= cap) total += lens[i];
+    if (lens[i] > 0 && lens[i] <= cap) {
+      total += lens[i];
+      mx = lens[i] > mx ? lens[i] : mx;
+    }
+  if (split > 0 && ragged_split(mx, total, slots)) target = split;
   long long chunk = granule((total * kKvHeads + target - 1) / target);
   if (budget > 0 && total > 0) {
     const long long c0 = granule((total * kKvHeads + budget - 1) / budget);
@@ -466,12 +470,15 @@ int workspace_rows_tokens(int n_qtok, bool prefill) { return prefill ? kGroupTok
 // `slots` resident split workgroups, with `cap_target` the target the
 // workspace was sized for.
 struct PlanParams {
-  int64_t target, max_items, budget;
+  int64_t target, max_items, budget, split, slots;
 };
 PlanParams plan_params(int64_t n_seq, int64_t slots, int64_t cap_target) {
   PlanParams r;
+  r.slots = slots;
   r.target = pa::plan_target(n_seq, slots, cap_target);
-  r.max_items = pa::max_work_items(n_seq, r.target);
+  r.split = pa::split_target(n_seq, slots, cap_target);
+  // the grid covers the items of either target
+  r.max_items = pa::max_work_items(n_seq, r.split > r.target ? r.split : r.target);
   // when every item fits one round, the plan may shorten the chunk as long
   // as the items stay within the grid (max_items)
   r.budget = (2 * static_cast<int64_t>(pa::kKvHeads) * n_seq <= slots) ? r.max_items : 0;
@@ -587,6 +594,8 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.target_items = static_cast<int32_t>(pp.target);
   prm.max_items = static_cast<int32_t>(pp.max_items);
   prm.plan_budget = static_cast<int32_t>(pp.budget);
+  prm.split_target = static_cast<int32_t>(pp.split);
+  prm.plan_slots = static_cast<int32_t>(pp.slots);
   prm.tok_total = n_qtok;
   prm.tok0 = 0;
   prm.n_groups = 1;
@@ -599,7 +608,8 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.scale_log2 = sc * 1.4426950408889634f;
   prm.hp.on = 0;
   if (lens_host && n_seq <= pa::kHostPlanSeqs)
-    pa::host_plan(lens_host, n_seq, bt_stride * page_size, prm.target_items, prm.plan_budget, prm.hp);
+    pa::host_plan(lens_host, n_seq, bt_stride * page_size, prm.target_items, prm.plan_budget, prm.split_target,
+                  prm.plan_slots, prm.hp);
   return hip_status(pa::launch_decode(prm, stream, ev0, ev1));
 }
 
@@ -633,7 +643,8 @@ pa_status pa_split_plan(const int32_t* seq_lens_host, int32_t n_seq, int32_t cap
   const PlanParams pp = plan_params(n_seq, static_cast<int64_t>(n_cu) * wgs_per_cu,
                                     static_cast<int64_t>(n_cu) * kTargetPerCu);
   pa::HostPlan hp;
-  pa::host_plan(seq_lens_host, n_seq, cap, static_cast<int>(pp.target), static_cast<int>(pp.budget), hp);
+  pa::host_plan(seq_lens_host, n_seq, cap, static_cast<int>(pp.target), static_cast<int>(pp.budget),
+                static_cast<int>(pp.split), static_cast<int>(pp.slots), hp);
   *chunk = hp.chunk;
   *n_items = pa::kKvHeads * hp.first[n_seq];
   if (first)

@@ -63,6 +63,8 @@ struct DecodeParams {
   int32_t page_shift;      // log2(page_size) when it is a power of two, else -1
   int32_t target_items;    // item target of the chunk plan (plan_target)
   int32_t plan_budget;     // > 0: the plan takes the shortest chunk whose items fit in it
+  int32_t split_target;    // > 0: the target of a ragged many-sequence batch (split_target)
+  int32_t plan_slots;      // co-resident split workgroups (for ragged_split)
   int32_t max_items;       // work items of the plan the grid covers (per token group)
   // Token groups: q / out / lse_out hold tok_total tokens per sequence; a
   // launch covers n_groups groups of the kernel's token count starting at
@@ -86,17 +88,32 @@ inline int64_t max_work_items(int64_t n_seq, int64_t target_items) {
 // Item target of the chunk plan for `slots` co-resident workgroups.  The plan
 // yields at most target + 4 n_seq items, so when the sequences leave room the
 // target fills exactly one round of resident workgroups (no second wave of
-// short-lived workgroups, each paying the set-up again).  Otherwise (many
-// sequences) the target is two rounds: chunks of half a slot's share, which
-// the hardware dispatcher spreads over the compute units as they free up, so
-// that the longest sequences of a ragged batch no longer set the time (a
-// target of half a round left every sequence in one chunk).  Never above
-// `cap`, the target the workspace was sized for.
+// short-lived workgroups, each paying the set-up again); otherwise half a
+// round of chunks goes on top of the one-item-per-(sequence, head) minimum.
+// Never above `cap`, the target the workspace was sized for.
 inline int64_t plan_target(int64_t n_seq, int64_t slots, int64_t cap) {
   const int64_t per = kKvHeads * n_seq;
-  int64_t t = (2 * per <= slots) ? slots - per : 2 * slots;
+  int64_t t = (2 * per <= slots) ? slots - per : slots / 2;
   if (t < 1) t = 1;
   return t < cap ? t : cap;
+}
+
+// The target a many-sequence batch switches to when it is ragged (0 when the
+// sequences leave room for one round): two rounds of chunks of half a slot's
+// share, which the hardware dispatcher spreads over the compute units as they
+// free up.  The plan takes it when the longest valid sequence exceeds 1.5
+// times a slot's share of the work, 4 sum(L) / slots (ragged_split); a batch
+// of even lengths keeps one chunk per (sequence, head), which already
+// balances.
+inline int64_t split_target(int64_t n_seq, int64_t slots, int64_t cap) {
+  const int64_t per = kKvHeads * n_seq;
+  if (2 * per <= slots) return 0;
+  const int64_t t = 2 * slots;
+  return t < cap ? t : cap;
+}
+
+PA_HD inline bool ragged_split(long long max_len, long long total, long long slots) {
+  return 2 * max_len * slots > 3 * static_cast<long long>(kKvHeads) * total;
 }
 
 // Work items the split grid covers (per token group): the plan's exact count
@@ -107,7 +124,7 @@ inline int32_t grid_items(const DecodeParams& p) {
 
 // Fills `hp` from host seq_lens (n_seq <= kHostPlanSeqs) with the device
 // plan's arithmetic for the given target and budget.
-void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, HostPlan& hp);
+void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, int split, int slots, HostPlan& hp);
 
 // Resident workgroups per compute unit of the split kernel a call selects
 // (from the runtime's occupancy query; at least 1).

@@ -23,19 +23,26 @@ def _granule(c):
 
 def _model(lens, cap, n_cu, wgs):
     """The rule as stated: slots = CUs x resident workgroups; item target =
-    slots - 4 n_seq when 8 n_seq <= slots (one round) else 2 slots (two
-    rounds), capped at 4 per CU; chunk = ceil(4 sum(valid L) / target) rounded up to the granule;
-    in the one-round case the shortest of the four granule steps from
+    slots - 4 n_seq when 8 n_seq <= slots (one round), else slots / 2, or 2
+    slots when the batch is ragged (the longest valid sequence above 1.5
+    times a slot's share 4 sum(L) / slots); capped at 4 per CU; chunk =
+    ceil(4 sum(valid L) / target) rounded up to the granule; in the
+    one-round case the shortest of the four granule steps from
     ceil(4 sum L / budget) up whose items fit the budget (target + 4 n_seq),
-    if shorter."""
+    if shorter.  Returns (chunk, target)."""
     n = len(lens)
     slots = n_cu * wgs
     per = N_KV * n
-    target = slots - per if 2 * per <= slots else 2 * slots
-    target = max(1, min(target, n_cu * 4))
-    total = sum(L for L in lens if 0 < L <= cap)
+    cap_t = n_cu * 4
+    valid = [L for L in lens if 0 < L <= cap]
+    total = sum(valid)
+    one_round = 2 * per <= slots
+    target = slots - per if one_round else slots // 2
+    target = max(1, min(target, cap_t))
+    if not one_round and valid and 2 * max(valid) * slots > 3 * N_KV * total:
+        target = min(2 * slots, cap_t)
     chunk = _granule(-(-(total * N_KV) // target))
-    if 2 * per <= slots and total > 0:
+    if one_round and total > 0:
         budget = target + per
         c0 = _granule(-(-(total * N_KV) // budget))
         for k in range(4):
@@ -43,7 +50,7 @@ def _model(lens, cap, n_cu, wgs):
             if ck < chunk and N_KV * sum(_n_chunks(L, cap, ck) for L in lens) <= budget:
                 chunk = ck
                 break
-    return chunk
+    return chunk, target
 
 
 def _check_partition(lens, cap, chunk, items, first):
@@ -67,6 +74,13 @@ def test_many_stream_serving_workload_is_split():
     assert int(np.max(np.diff(first))) > 1
 
 
+def test_even_many_sequence_batch_keeps_one_chunk_per_head():
+    # 200 x 4096: more (sequence, head) pairs than a round holds, but even
+    # lengths: one chunk each already balances, so the batch is not split
+    chunk, items, first = pb.split_plan([4096] * 200, 4096, 256, 2)
+    assert items == 800 and chunk >= 4096
+
+
 def test_headline_ragged_workload():
     # 131072 + 7 x 8192, 16-position pages: 1536-position chunks, 512 items
     # on 256 compute units x 2 workgroups (one round of resident workgroups)
@@ -88,11 +102,10 @@ def test_random_batches_match_model_and_partition(n_cu, wgs):
         if rng.random() < 0.3:
             lens[rng.integers(0, n)] = cap + 7
         chunk, items, first = pb.split_plan(lens, cap, n_cu, wgs)
-        assert chunk == _model([int(x) for x in lens], cap, n_cu, wgs)
+        m_chunk, target = _model([int(x) for x in lens], cap, n_cu, wgs)
+        assert chunk == m_chunk
         _check_partition([int(x) for x in lens], cap, chunk, items, first)
         slots = n_cu * wgs
-        target = (slots - N_KV * n) if 2 * N_KV * n <= slots else 2 * slots
-        target = max(1, min(target, n_cu * 4))
         assert items <= target + N_KV * n                       # within the split grid
         if 2 * N_KV * n <= slots:
             assert items <= slots                               # one round of resident workgroups
