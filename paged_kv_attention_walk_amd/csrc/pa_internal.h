@@ -142,10 +142,12 @@ PA_HD constexpr int rows_per_item(int n_qtok) { return 6 * n_qtok; }
 
 // The workspace header's int32 words: [0] the device error word, [1] the
 // call's chunk length and [2 + s] the plan index of sequence s's first chunk
-// for s < kHdrSeqs, written by the split kernel for the merge kernel.
-constexpr int kHdrSeqs = 62;
+// for s < kHdrSeqs, written by the split kernel for the merge kernel (larger
+// batches make the merge compute the plan again).
+constexpr int kHdrBytes = 4096;
+constexpr int kHdrSeqs = kHdrBytes / 4 - 2;
 
-// Workspace: [0, 256) header (error word at 0); chunk log-sum-exps
+// Workspace: [0, kHdrBytes) header (error word at 0); chunk log-sum-exps
 // [items][6 n_qtok]; chunk outputs [items][6 n_qtok][256].  The layout
 // depends on the call's n_qtok and the item capacity only, so a workspace
 // sized for n_qtok tokens also serves every call of fewer tokens (more items
@@ -154,7 +156,7 @@ inline WorkspaceLayout workspace_layout_items(int64_t items, int n_qtok) {
   const size_t rows = static_cast<size_t>(rows_per_item(n_qtok));
   WorkspaceLayout w;
   w.items = items;
-  w.lse_off = 256;
+  w.lse_off = kHdrBytes;
   w.o_off = align_up(w.lse_off + static_cast<size_t>(items) * rows * sizeof(float), 256);
   w.total = align_up(w.o_off + static_cast<size_t>(items) * rows * kHeadDim * sizeof(float), 256);
   return w;

@@ -109,11 +109,12 @@ def test_serving_128_streams_append_then_decode_sampled():
 
 
 @pytest.mark.parametrize("engine", ["mfma", "valu"])
-@pytest.mark.parametrize("n_seq", [62, 63, 64, 65, 130])
+@pytest.mark.parametrize("n_seq", [62, 63, 64, 65, 130, 1100])
 def test_many_sequences_with_long_ones(n_seq, engine):
     # mostly short sequences and a few long ones, so the long ones split into
-    # several chunks: the plan runs block-wide past 64 sequences and the merge
-    # plans for itself past 62
+    # several chunks: the plan runs block-wide past 64 sequences, the host plan
+    # stops at 256, and the merge plans for itself past the 1022 sequences its
+    # header holds
     rng = np.random.default_rng(n_seq)
     lens = [int(x) for x in rng.integers(0, 200, size=n_seq)]
     for i in rng.choice(n_seq, size=4, replace=False):
