@@ -35,8 +35,8 @@ Modules:
                      quantiser of a device-side append).
 * ``attention``   -- block-table gather, plain causal GQA softmax attention,
                      the log-sum-exp merge of chunk partials.
-* ``pool_model``  -- byte-level model of the paged pool (row addresses,
-                     append scatter, logical gather).
+* ``pool_model``  -- byte-level model of the paged pool (append scatter,
+                     logical gather).
 * ``alloc_model`` -- model of the exact transactional block allocator.
 
 Every function is pinned by ``tests/test_oracle_*.py`` to something other than

@@ -10,40 +10,25 @@ not fix how rows are laid out inside a pool page.  The reading taken here:
 * a pool is ``[n_blocks][n_kv_heads][page_size][row_bytes]`` bytes
   (head-major inside a page, so one KV head's rows of one page are
   contiguous);
-* contiguous (unpaged) storage is ``[n_seq][n_kv_heads][max_len][row_bytes]``;
-  a sequence's position ``pos`` lives in logical page ``pos // page_size`` at
-  slot ``pos % page_size``.
+* a sequence's position ``pos`` lives in logical page ``pos // page_size``
+  at slot ``pos % page_size``.
 
-TensorFold#1156 (Design / Kernels) routes every row address through one
-helper whose no-table case is the contiguous expression; this model has the
-same two cases, written independently of the HIP library.
+Two operations are modelled: the append scatter (rows into (page, slot)
+destinations) and the logical gather through a block-table row.  Both are
+written independently of the HIP library.
 """
 
 import numpy as np
-
-
-def pool_row_offset(block: int, head: int, slot: int, *, n_kv_heads: int,
-                    page_size: int, row_bytes: int) -> int:
-    """Byte offset of (pool page ``block``, KV head ``head``, slot ``slot``)."""
-    return ((block * n_kv_heads + head) * page_size + slot) * row_bytes
-
-
-def contiguous_row_offset(seq: int, head: int, pos: int, *, n_kv_heads: int,
-                          max_len: int, row_bytes: int) -> int:
-    """Byte offset of (sequence, KV head, position) in contiguous storage."""
-    return ((seq * n_kv_heads + head) * max_len + pos) * row_bytes
-
-
-def empty_pool(n_blocks: int, n_kv_heads: int, page_size: int, row_bytes: int) -> np.ndarray:
-    return np.zeros((n_blocks, n_kv_heads, page_size, row_bytes), dtype=np.uint8)
 
 
 def scatter_rows(pool: np.ndarray, blocks, slots, rows: np.ndarray) -> np.ndarray:
     """Append model (colibri#372, Summary: only the new rows are uploaded and a
     scatter puts them into pages).  ``rows`` is ``[n][n_kv_heads][row_bytes]``;
     row i goes to page ``blocks[i]``, slot ``slots[i]``, for every KV head.
-    Returns a new pool; the input pool is not modified.  Out-of-range
-    destinations raise ``IndexError``."""
+    Rows are written in order, so when two rows name the same destination the
+    later one is kept.  Returns a new pool; the input pool is not modified.
+    An out-of-range destination raises ``IndexError`` before anything is
+    written."""
     out = pool.copy()
     n_blocks, n_kv_heads, page_size, rb = out.shape
     rows = np.asarray(rows, dtype=np.uint8)
@@ -53,6 +38,8 @@ def scatter_rows(pool: np.ndarray, blocks, slots, rows: np.ndarray) -> np.ndarra
         b, s = int(blocks[i]), int(slots[i])
         if not (0 <= b < n_blocks and 0 <= s < page_size):
             raise IndexError(f"row {i}: destination (block {b}, slot {s}) out of range")
+    for i in range(rows.shape[0]):
+        b, s = int(blocks[i]), int(slots[i])
         for h in range(n_kv_heads):
             out[b, h, s, :] = rows[i, h, :]
     return out
@@ -77,16 +64,4 @@ def gather_rows(pool: np.ndarray, table_row, seq_len: int) -> np.ndarray:
         first = lp * page_size
         n = min(page_size, seq_len - first)
         out[:, first:first + n, :] = pool[b, :, 0:n, :]
-    return out
-
-
-def contiguous_from_paged(pool: np.ndarray, block_table, seq_lens, max_len: int) -> np.ndarray:
-    """Contiguous storage ``[n_seq][n_kv_heads][max_len][row_bytes]`` holding the
-    same logical rows as the paged pool (unused positions are zero)."""
-    n_blocks, n_kv_heads, page_size, rb = pool.shape
-    n_seq = len(seq_lens)
-    out = np.zeros((n_seq, n_kv_heads, max_len, rb), dtype=np.uint8)
-    for s in range(n_seq):
-        L = int(seq_lens[s])
-        out[s, :, :L, :] = gather_rows(pool, block_table[s], L)
     return out

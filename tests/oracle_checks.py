@@ -335,3 +335,49 @@ def check_encode_two_byte_rounding(enc):
 
 ENCODE_CHECKS = (check_encode_closed_forms, check_encode_clip_and_zero, check_encode_rounding,
                  check_encode_scale_rounding, check_encode_two_byte_rounding)
+
+
+# ------------------------------------------------------------ append scatter
+
+def check_scatter(scatter, gather, P=16, rb=144, seed=0):
+    """scatter(pool, blocks, slots, rows) against the logical positions that
+    the (separately pinned) gather reads back.  Three sequences own every page
+    of the pool through a shuffled table, so gathering all of them reads every
+    byte.  Rows are appended at logical positions (s, pos): destination
+    (table[s][pos // P], pos % P).  After the scatter, gathered row pos of
+    sequence s is the appended row for each KV head; two rows aimed at one
+    position leave the later; every other gathered row keeps its bytes."""
+    rng = np.random.default_rng(seed)
+    n_pages = [3, 5, 2]
+    nb = sum(n_pages)
+    perm = rng.permutation(nb)
+    tables, k = [], 0
+    for n in n_pages:
+        tables.append(perm[k:k + n])
+        k += n
+    pool = rng.integers(0, 256, size=(nb, HKV, P, rb), dtype=np.uint8)
+    before = [gather(pool, tables[s], n_pages[s] * P) for s in range(3)]
+    # logical destinations: page boundaries, slot 0 and P - 1, and one repeat
+    dests = [(0, 0), (0, P - 1), (0, P), (1, 2 * P + 7), (1, 5 * P - 1), (2, P + 3), (1, 2 * P + 7)]
+    rows = rng.integers(0, 256, size=(len(dests), HKV, rb), dtype=np.uint8)
+    blocks = np.array([tables[s][pos // P] for s, pos in dests], np.int32)
+    slots = np.array([pos % P for s, pos in dests], np.int32)
+    pool_copy = pool.copy()
+    after = scatter(pool, blocks, slots, rows)
+    assert np.array_equal(pool, pool_copy), "the input pool is left unmodified"
+    expect = [b.copy() for b in before]
+    for i, (s, pos) in enumerate(dests):
+        expect[s][:, pos, :] = rows[i]                    # in order: the later row of a repeat wins
+    for s in range(3):
+        got = gather(after, tables[s], n_pages[s] * P)
+        for h in range(HKV):
+            for pos in range(n_pages[s] * P):
+                assert np.array_equal(got[h, pos], expect[s][h, pos]), f"sequence {s}, KV head {h}, position {pos}"
+    # out-of-range destinations raise and write nothing
+    for b, sl in ((nb, 0), (-1, 0), (0, P), (0, -1)):
+        try:
+            scatter(pool, np.array([0, b], np.int32), np.array([1, sl], np.int32), rows[:2])
+        except IndexError:
+            pass
+        else:
+            raise AssertionError(f"destination (block {b}, slot {sl}) accepted")
