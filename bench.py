@@ -31,9 +31,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=400,
-                    help="untimed steps before each timed run; the GPU reaches its steady clock only after "
-                         "some milliseconds of work, so the default covers that")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before each timed run (after --settle)")
     ap.add_argument("--workload", default="ragged",
                     choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16", "serving", "prefill"],
                     help="ragged: 131072 + 7 x 8192 Q4_0 (the headline); ragged_q8k_q4v: same with Q8_0 K and Q4_0 V; "
@@ -58,6 +56,9 @@ def parse():
     ap.add_argument("--no-contiguous", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of back-to-back untimed steps before every timed run (on top of --warmup): "
+                         "the clocks reach their steady state only after some milliseconds of continuous work")
     ap.add_argument("--ceiling", action="store_true",
                     help="only time a plain 2 GiB device-to-device copy (read-bandwidth ceiling; also the "
                          "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -130,31 +131,62 @@ def synth_row_bytes(kind):
     return {"f16": 512, "bf16": 512, "q8_0": 272, "q4_0": 144}[kind]
 
 
+def host_info():
+    """CPU model, logical CPUs and ROCm version of the machine the bench runs on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rocm = None
+    for f in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            rocm = open(f).read().strip()
+            break
+        except OSError:
+            continue
+    import torch
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "rocm": rocm, "torch": torch.__version__,
+            "torch_hip": getattr(torch.version, "hip", None)}
+
+
 def cpu_baseline(w, seconds):
-    """The float64 oracle, as it stands, on a bounded sample of the workload:
-    one 8192-position sequence of it (all 24 query heads), repeated for about
-    `seconds`.  Reported in K/V GB/s like the GPU value."""
-    import numpy as np
+    """The float64 oracle, as it stands, on the whole workload (every
+    sequence, all 24 query heads), repeated until `seconds` have passed (at
+    least once).  Reported in K/V GB/s like the GPU value."""
     from threadpoolctl import threadpool_info
     from oracle import attention
-    s = 1 if len(w["seq_lens"]) > 1 else 0
-    L = int(w["seq_lens"][s])
-    bt = w["block_table"][s:s + 1]
-    lens = w["seq_lens"][s:s + 1]
-    q = w["q"][s:s + 1]
-    per = L * 4 * (synth_row_bytes(w["k_kind"]) + synth_row_bytes(w["v_kind"]))
     t0 = time.perf_counter()
     n = 0
     while True:
-        attention.paged_decode(q, w["k_pool"], w["v_pool"], w["k_kind"], w["v_kind"], bt, lens, w["scale"])
+        attention.paged_decode(w["q"], w["k_pool"], w["v_pool"], w["k_kind"], w["v_kind"], w["block_table"],
+                               w["seq_lens"], w["scale"])
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(per * n / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"sequence {s} of the workload ({L} positions, 24 query heads, 1 token), {n} runs in "
-                      f"{dt:.1f} s on the host; host has {os.cpu_count()} logical CPUs"}
+    return {"value": round(w.kv_bytes * n / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole workload ({len(w['seq_lens'])} sequences, {int(sum(w['seq_lens']))} positions, "
+                      f"24 query heads, {w['n_qtok']} token(s)), {n} pass(es) in {dt:.1f} s on the host; "
+                      f"{os.cpu_count()} logical CPUs",
+            "seconds_per_step": round(dt / n, 3)}
+
+
+def load_profile(workload_name):
+    """Split-kernel duration from the committed rocprofv3 kernel trace of the
+    default bench command, if the kernel sources are unchanged since it was
+    taken (else None): a cross-check of the live event timing."""
+    p = os.path.join(ROOT, "profiles", f"trace_{workload_name}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d
 
 
 def main():
@@ -207,17 +239,31 @@ def main():
     bt_stride = w["block_table"].shape[1]
     nblocks = w["k_pool"].shape[0]
 
+    def settle(calls, seconds):
+        """Back-to-back steps for `seconds` of wall time before a timed run:
+        the GPU's clocks reach their steady state only after some milliseconds
+        of continuous work, whatever the untimed warm-up count."""
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(64):
+                calls[i % len(calls)](None)
+                i += 1
+            torch.cuda.synchronize()
+        return i
+
     def timed(calls, steps, warmup):
-        """calls: list of callables taking an event pair or None.  Times `steps`
-        steps with no events (wall clock, ms/step), then the same steps again
-        with HIP events recorded on the launch stream just before and after
-        each split kernel.  Returns (ms/step, split-kernel ms mean, median).
-        An event pair costs several microseconds of step time, so the step
-        time comes from the pass without them."""
+        """calls: list of callables taking an event pair or None.  After the
+        settle phase and `warmup` untimed steps, times `steps` steps with no
+        events (wall clock between two synchronisations, ms/step), then the
+        same steps again with the split kernel's timing events attached to its
+        dispatch (the kernel's execution time).  Returns (ms/step,
+        split-kernel ms mean, median)."""
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in evs:          # create the events on this stream
             a.record()
             b.record()
+        settle(calls, args.settle)
         for i in range(warmup):
             calls[i % len(calls)](None)
         torch.cuda.synchronize()
@@ -344,8 +390,15 @@ def main():
     flops = 4.0 * 256 * 24 * vis
     roofline = {"kernel": SPLIT_KERNEL, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w["name"]),
-                "split_kernel_ms_mean": round(cold_k, 5), "split_kernel_ms_median": round(cold_k_med, 5)}
+                "split_kernel_ms_mean": round(cold_k, 5), "split_kernel_ms_median": round(cold_k_med, 5),
+                "timing": "timing events attached to the split kernel's dispatch (its execution), mean over the "
+                          "cold steps"}
     roofline["frac_of_read_ceiling"] = round(achieved / ceiling["gbps"], 4)
+    prof = load_profile(w["name"])
+    if prof is not None:      # the committed rocprofv3 trace of this command, same kernel sources
+        pk = prof["split_kernel_avg_ns"] * 1e-6
+        roofline["profile"] = {"file": f"profiles/trace_{w['name']}.json", "split_kernel_ms": round(pk, 5),
+                               "frac": round(kv_bytes / (pk * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     tflops = flops / (cold_k * 1e-3) / 1e12
     if flops / kv_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):   # past the ridge point
         roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
@@ -358,6 +411,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle,
         "ms_per_step": round(cold_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -386,6 +440,7 @@ def main():
         "read_ceiling": ceiling,
         "split_tflops": round(tflops, 2),
         "cpu_baseline": None,
+        "host": host_info(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

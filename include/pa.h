@@ -262,8 +262,11 @@ typedef struct pa_decode_ext {
                                 workspace.  Its first 4 bytes are the device error
                                 word: zero them before the first use (e.g. hipMemset) */
     size_t   workspace_bytes;
-    void    *split_events[2];/* optional hipEvent_t pair, recorded on `stream` just
-                                before and after the split kernel (profiling)           */
+    void    *split_events[2];/* optional hipEvent_t pair (created with timing) attached
+                                to the split kernel's dispatch on `stream`: [0] records
+                                when it starts executing, [1] when it has completed, so
+                                hipEventElapsedTime gives the kernel's run time
+                                (profiling).  Either may be NULL.                       */
     const int32_t *seq_lens_host; /* optional HOST copy of seq_lens ([n_seq] int32), or
                                 NULL.  With it (and n_seq <= PA_HOST_PLAN_MAX_SEQS) the
                                 split-K plan -- chunk length and each sequence's first

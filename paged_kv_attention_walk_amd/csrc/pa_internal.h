@@ -177,16 +177,26 @@ inline WorkspaceLayout workspace_layout_for_bytes(size_t bytes, int n_qtok) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin,
                          hipEvent_t ev_end);
 
+// Where a split kernel is launched: the stream, and optional timing events
+// that the runtime attaches to the dispatch itself (start: the kernel begins
+// executing; stop: it has completed), so their interval is the kernel's run
+// time, not the time between two marker packets around it.
+struct SplitLaunch {
+  hipStream_t stream;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
 // Split kernels for n_qtok = T: each T is its own translation unit (the
 // matrix-core and vector sources are built once per T with -DPA_T=T), so
 // the instantiations of all K x V encodings compile in parallel.
-template <int T> hipError_t launch_split_mfma_t(const DecodeParams& p, hipStream_t stream);
+template <int T> hipError_t launch_split_mfma_t(const DecodeParams& p, const SplitLaunch& l);
 template <int T> int split_mfma_wgs_t(int k_type, int v_type);
-template <int T> hipError_t launch_split_valu_t(const DecodeParams& p, hipStream_t stream);
-#define PA_DECLARE_SPLIT_T(T)                                                            \
-  template <> hipError_t launch_split_mfma_t<T>(const DecodeParams& p, hipStream_t stream); \
-  template <> int split_mfma_wgs_t<T>(int k_type, int v_type);                             \
-  template <> hipError_t launch_split_valu_t<T>(const DecodeParams& p, hipStream_t stream);
+template <int T> hipError_t launch_split_valu_t(const DecodeParams& p, const SplitLaunch& l);
+#define PA_DECLARE_SPLIT_T(T)                                                              \
+  template <> hipError_t launch_split_mfma_t<T>(const DecodeParams& p, const SplitLaunch& l); \
+  template <> int split_mfma_wgs_t<T>(int k_type, int v_type);                               \
+  template <> hipError_t launch_split_valu_t<T>(const DecodeParams& p, const SplitLaunch& l);
 PA_DECLARE_SPLIT_T(1)
 PA_DECLARE_SPLIT_T(2)
 PA_DECLARE_SPLIT_T(3)

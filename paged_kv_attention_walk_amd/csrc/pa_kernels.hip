@@ -116,17 +116,17 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_split(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_split(const DecodeParams& p, const SplitLaunch& l) {
   const bool valu = p.engine == 1;
   switch (p.n_qtok) {
-    case 1: return valu ? launch_split_valu_t<1>(p, stream) : launch_split_mfma_t<1>(p, stream);
-    case 2: return valu ? launch_split_valu_t<2>(p, stream) : launch_split_mfma_t<2>(p, stream);
-    case 3: return valu ? launch_split_valu_t<3>(p, stream) : launch_split_mfma_t<3>(p, stream);
-    case 4: return valu ? launch_split_valu_t<4>(p, stream) : launch_split_mfma_t<4>(p, stream);
-    case 5: return valu ? launch_split_valu_t<5>(p, stream) : launch_split_mfma_t<5>(p, stream);
-    case 6: return valu ? launch_split_valu_t<6>(p, stream) : launch_split_mfma_t<6>(p, stream);
-    case 7: return valu ? launch_split_valu_t<7>(p, stream) : launch_split_mfma_t<7>(p, stream);
-    case 8: return valu ? launch_split_valu_t<8>(p, stream) : launch_split_mfma_t<8>(p, stream);
+    case 1: return valu ? launch_split_valu_t<1>(p, l) : launch_split_mfma_t<1>(p, l);
+    case 2: return valu ? launch_split_valu_t<2>(p, l) : launch_split_mfma_t<2>(p, l);
+    case 3: return valu ? launch_split_valu_t<3>(p, l) : launch_split_mfma_t<3>(p, l);
+    case 4: return valu ? launch_split_valu_t<4>(p, l) : launch_split_mfma_t<4>(p, l);
+    case 5: return valu ? launch_split_valu_t<5>(p, l) : launch_split_mfma_t<5>(p, l);
+    case 6: return valu ? launch_split_valu_t<6>(p, l) : launch_split_mfma_t<6>(p, l);
+    case 7: return valu ? launch_split_valu_t<7>(p, l) : launch_split_mfma_t<7>(p, l);
+    case 8: return valu ? launch_split_valu_t<8>(p, l) : launch_split_mfma_t<8>(p, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -147,17 +147,18 @@ int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine) {
   }
 }
 
+// ev_begin / ev_end (optional) are attached to the split launches: begin to
+// the first, end to the last (the prefill takes two when its token count is
+// not a multiple of 8), so they time the split kernels' execution.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.n_seq <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
-  if (ev_begin) e = hipEventRecord(ev_begin, stream);
-  if (e != hipSuccess) return e;
   if (p.tok_total <= kMaxQtok) {
     DecodeParams a = p;
     a.n_qtok = p.tok_total;
     a.n_groups = 1;
     a.tok0 = 0;
-    e = launch_split(a, stream);
+    e = launch_split(a, SplitLaunch{stream, ev_begin, ev_end});
   } else {
     // prefill: full groups of kMaxQtok tokens in one launch, the rest in another
     const int full = p.tok_total / kMaxQtok, rest = p.tok_total % kMaxQtok;
@@ -165,17 +166,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t e
     a.n_qtok = kMaxQtok;
     a.n_groups = full;
     a.tok0 = 0;
-    e = launch_split(a, stream);
+    e = launch_split(a, SplitLaunch{stream, ev_begin, rest > 0 ? nullptr : ev_end});
     if (e == hipSuccess && rest > 0) {
       DecodeParams b = p;
       b.n_qtok = rest;
       b.n_groups = 1;
       b.tok0 = full * kMaxQtok;
-      e = launch_split(b, stream);
+      e = launch_split(b, SplitLaunch{stream, nullptr, ev_end});
     }
   }
-  if (e != hipSuccess) return e;
-  if (ev_end) e = hipEventRecord(ev_end, stream);
   if (e != hipSuccess) return e;
   if (p.hp.on && !p.hp.any_multi) return hipSuccess;   // every sequence wrote its rows directly
   return launch_merge(p, stream);

@@ -35,6 +35,7 @@
 // 6T query rows of a KV head take ceil(6T/16) B tiles of 16 columns (one
 // token packs hi and lo parts into one tile).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 
@@ -1225,19 +1226,20 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 }
 
 template <int KT, int VT>
-hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_kvt(const DecodeParams& p, const SplitLaunch& l) {
   const dim3 grid(static_cast<unsigned>(grid_items(p)) * static_cast<unsigned>(p.n_groups));
-  hipLaunchKernelGGL((split_mfma_kernel<KT, VT, PA_T>), grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  void* args[] = {const_cast<DecodeParams*>(&p)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&split_mfma_kernel<KT, VT, PA_T>), grid, dim3(kThreads), args, 0,
+                            l.stream, l.start, l.stop, 0);
 }
 
 template <int KT>
-hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_kt(const DecodeParams& p, const SplitLaunch& l) {
   switch (p.v_type) {
-    case kF16: return launch_kvt<KT, kF16>(p, stream);
-    case kBF16: return launch_kvt<KT, kBF16>(p, stream);
-    case kQ8_0: return launch_kvt<KT, kQ8_0>(p, stream);
-    case kQ4_0: return launch_kvt<KT, kQ4_0>(p, stream);
+    case kF16: return launch_kvt<KT, kF16>(p, l);
+    case kBF16: return launch_kvt<KT, kBF16>(p, l);
+    case kQ8_0: return launch_kvt<KT, kQ8_0>(p, l);
+    case kQ4_0: return launch_kvt<KT, kQ4_0>(p, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1277,12 +1279,12 @@ int split_mfma_wgs_t<PA_T>(int k_type, int v_type) {
 }
 
 template <>
-hipError_t launch_split_mfma_t<PA_T>(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_split_mfma_t<PA_T>(const DecodeParams& p, const SplitLaunch& l) {
   switch (p.k_type) {
-    case kF16: return launch_kt<kF16>(p, stream);
-    case kBF16: return launch_kt<kBF16>(p, stream);
-    case kQ8_0: return launch_kt<kQ8_0>(p, stream);
-    case kQ4_0: return launch_kt<kQ4_0>(p, stream);
+    case kF16: return launch_kt<kF16>(p, l);
+    case kBF16: return launch_kt<kBF16>(p, l);
+    case kQ8_0: return launch_kt<kQ8_0>(p, l);
+    case kQ4_0: return launch_kt<kQ4_0>(p, l);
     default: return hipErrorInvalidValue;
   }
 }

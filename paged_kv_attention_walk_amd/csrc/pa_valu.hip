@@ -8,6 +8,7 @@
 // KV head, context chunk) serves the 6 query heads x T tokens reading that
 // KV head.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 
@@ -203,19 +204,20 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
 }
 
 template <int KT, int VT>
-hipError_t launch_kvt(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_kvt(const DecodeParams& p, const SplitLaunch& l) {
   const dim3 grid(static_cast<unsigned>(grid_items(p)) * static_cast<unsigned>(p.n_groups));
-  hipLaunchKernelGGL((split_valu_kernel<KT, VT, PA_T>), grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  void* args[] = {const_cast<DecodeParams*>(&p)};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&split_valu_kernel<KT, VT, PA_T>), grid, dim3(kThreads), args, 0,
+                            l.stream, l.start, l.stop, 0);
 }
 
 template <int KT>
-hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_kt(const DecodeParams& p, const SplitLaunch& l) {
   switch (p.v_type) {
-    case kF16: return launch_kvt<KT, kF16>(p, stream);
-    case kBF16: return launch_kvt<KT, kBF16>(p, stream);
-    case kQ8_0: return launch_kvt<KT, kQ8_0>(p, stream);
-    case kQ4_0: return launch_kvt<KT, kQ4_0>(p, stream);
+    case kF16: return launch_kvt<KT, kF16>(p, l);
+    case kBF16: return launch_kvt<KT, kBF16>(p, l);
+    case kQ8_0: return launch_kvt<KT, kQ8_0>(p, l);
+    case kQ4_0: return launch_kvt<KT, kQ4_0>(p, l);
     default: return hipErrorInvalidValue;
   }
 }
@@ -223,12 +225,12 @@ hipError_t launch_kt(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 template <>
-hipError_t launch_split_valu_t<PA_T>(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_split_valu_t<PA_T>(const DecodeParams& p, const SplitLaunch& l) {
   switch (p.k_type) {
-    case kF16: return launch_kt<kF16>(p, stream);
-    case kBF16: return launch_kt<kBF16>(p, stream);
-    case kQ8_0: return launch_kt<kQ8_0>(p, stream);
-    case kQ4_0: return launch_kt<kQ4_0>(p, stream);
+    case kF16: return launch_kt<kF16>(p, l);
+    case kBF16: return launch_kt<kBF16>(p, l);
+    case kQ8_0: return launch_kt<kQ8_0>(p, l);
+    case kQ4_0: return launch_kt<kQ4_0>(p, l);
     default: return hipErrorInvalidValue;
   }
 }
