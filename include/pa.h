@@ -54,9 +54,11 @@ typedef int32_t pa_status;
 const char *pa_status_string(pa_status s);
 
 /* Library version, "major.minor.patch".  The minor number changes when a
- * struct of this header grows: 0.2 added pa_decode_ext.seq_lens_host,
- * pa_split_plan and pa_read_bandwidth_probe. */
-#define PA_VERSION_STRING "0.2.0"
+ * struct of this header grows or calls are added: 0.2 added
+ * pa_decode_ext.seq_lens_host, pa_split_plan and pa_read_bandwidth_probe;
+ * 0.3 added pa_split_workgroups_per_cu and attaches pa_decode_ext.split_events
+ * to the split kernel's dispatch. */
+#define PA_VERSION_STRING "0.3.0"
 const char *pa_version(void);
 
 /* ------------------------------------------------------------------ types */
@@ -291,8 +293,9 @@ typedef struct pa_decode_ext {
  *                a length < 0 or > cap counts as one empty chunk.
  * cap            rows per sequence (bt_stride * page_size).
  * n_cu, wgs_per_cu  compute units and resident split workgroups per compute
- *                unit (pa_decode takes both from the device: 256 and 2 for a
- *                one-token Q4_0 call on MI355X).
+ *                unit (pa_decode takes both from the device; the second is what
+ *                pa_split_workgroups_per_cu reports: 256 and 2 for a one-token
+ *                Q4_0 call on MI355X).
  * Writes *chunk (positions per chunk, a multiple of 128), *n_items (work
  * items = chunks x 4 KV heads) and, if first != NULL, first[s] = index of
  * sequence s's first chunk for s = 0..n_seq (first[n_seq] = all chunks).
@@ -301,6 +304,15 @@ typedef struct pa_decode_ext {
  * written then. */
 pa_status pa_split_plan(const int32_t *seq_lens_host, int32_t n_seq, int32_t cap, int32_t n_cu,
                         int32_t wgs_per_cu, int32_t *chunk, int32_t *n_items, int32_t *first);
+
+/* Resident split workgroups per compute unit that pa_decode / pa_prefill
+ * plan with for `kv_type`, `n_qtok` query tokens (1..PA_MAX_QTOK; prefill
+ * uses 8 per group) and `flags` (pa_decode_ext.flags) on the current device:
+ * the runtime's occupancy query for the kernel the call launches.  Pass it
+ * to pa_split_plan to reproduce a call's partition.
+ * Errors: PA_ERR_INVALID (null wgs, a bad kv_type, n_qtok or flags);
+ * PA_ERR_HIP (no usable device). */
+pa_status pa_split_workgroups_per_cu(int32_t kv_type, int32_t n_qtok, uint32_t flags, int32_t *wgs);
 
 /* One decode step (lucebox pull 555, Summary; achyudh/llama.cpp pull 2,
  * split-K decode and page-table commits).

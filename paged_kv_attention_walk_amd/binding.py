@@ -17,7 +17,7 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa_walk.so")
-ABI_VERSION = "0.2.0"      # the library version whose structs this binding mirrors
+ABI_VERSION = "0.3.0"      # the library version whose structs this binding mirrors
 
 F16, BF16, Q8_0, Q4_0 = 1, 2, 3, 4
 F32 = 5                                   # a source type of pa_append_kv_device only
@@ -35,7 +35,7 @@ EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "
            "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_append_kv_device",
            "pa_decode",
            "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather", "pa_prefill",
-           "pa_prefill_workspace_size", "pa_split_plan", "pa_read_bandwidth_probe")
+           "pa_prefill_workspace_size", "pa_split_plan", "pa_read_bandwidth_probe", "pa_split_workgroups_per_cu")
 
 
 def kv_type(k, v=0) -> int:
@@ -104,6 +104,7 @@ def _lib():
             "pa_debug_gather": (I32, [VP, I32, VP, I32, I32, I32, I32, I32, VP, VP, VP]),
             "pa_split_plan": (I32, [VP, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), VP]),
             "pa_read_bandwidth_probe": (I32, [VP, SZ, VP, SZ, VP]),
+            "pa_split_workgroups_per_cu": (I32, [I32, I32, ctypes.c_uint32, ctypes.POINTER(I32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -280,6 +281,14 @@ def prefill_status(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv, 
     return _lib().pa_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
                              int(n_seq), int(n_qtok), kv if isinstance(kv, int) else kv_type(kv), int(page_size),
                              _ptr(out), _stream(stream), ctypes.byref(ext) if ext is not None else None)
+
+
+def split_workgroups_per_cu(kv, n_qtok=1, flags=0) -> int:
+    """pa_split_workgroups_per_cu on the current device."""
+    w = ctypes.c_int32()
+    _check(_lib().pa_split_workgroups_per_cu(kv if isinstance(kv, int) else kv_type(kv), int(n_qtok), int(flags),
+                                             ctypes.byref(w)), "pa_split_workgroups_per_cu")
+    return w.value
 
 
 def split_plan(seq_lens, cap, n_cu=256, wgs_per_cu=2):

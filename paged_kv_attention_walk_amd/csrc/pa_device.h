@@ -59,18 +59,24 @@ __device__ inline int wave_incl_scan(int x) {
   return x;
 }
 
-// Block-wide sum of a per-thread value (256 threads).  `sh` holds 4 slots.
+// Waves of the calling workgroup (a multiple of 64 threads, at most
+// kMaxWaves waves); the block-wide helpers below work for any such size.
+__device__ inline int block_waves() { return static_cast<int>(blockDim.x) >> 6; }
+
+// Block-wide sum of a per-thread value.  `sh` holds kMaxWaves slots.
 __device__ inline long long block_sum(long long v, long long* sh) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  return sh[0] + sh[1] + sh[2] + sh[3];
+  long long t = 0;
+  for (int w = 0; w < block_waves(); ++w) t += sh[w];
+  return t;
 }
 
-// Block-wide sums of kPlanCand per-thread values (256 threads); `sh` holds
-// kPlanShared slots.
+// Block-wide sums of kPlanCand per-thread values; `sh` holds kPlanShared
+// slots.
 __device__ inline void block_sum_vec(long long (&v)[kPlanCand], long long* sh) {
 #pragma unroll
   for (int k = 0; k < kPlanCand; ++k)
@@ -82,12 +88,15 @@ __device__ inline void block_sum_vec(long long (&v)[kPlanCand], long long* sh) {
     for (int k = 0; k < kPlanCand; ++k) sh[(threadIdx.x >> 6) * kPlanCand + k] = v[k];
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kPlanCand; ++k)
-    v[k] = sh[k] + sh[kPlanCand + k] + sh[2 * kPlanCand + k] + sh[3 * kPlanCand + k];
+  for (int k = 0; k < kPlanCand; ++k) {
+    long long t = 0;
+    for (int w = 0; w < block_waves(); ++w) t += sh[w * kPlanCand + k];
+    v[k] = t;
+  }
 }
 
-// Block-wide maximum of a non-negative per-thread value (256 threads).  `sh`
-// holds 4 slots.
+// Block-wide maximum of a non-negative per-thread value.  `sh` holds
+// kMaxWaves slots.
 __device__ inline long long block_max(long long v, long long* sh) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -98,8 +107,7 @@ __device__ inline long long block_max(long long v, long long* sh) {
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
   long long m = sh[0];
-#pragma unroll
-  for (int w = 1; w < 4; ++w) m = sh[w] > m ? sh[w] : m;
+  for (int w = 1; w < block_waves(); ++w) m = sh[w] > m ? sh[w] : m;
   return m;
 }
 
@@ -120,7 +128,7 @@ __device__ inline long long round_granule(long long c) {
 __device__ inline int plan_chunk(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
                                  int split, int slots, long long* sh) {
   long long acc = 0, mx = 0;
-  for (int i = threadIdx.x; i < n_seq; i += kThreads) {
+  for (int i = threadIdx.x; i < n_seq; i += blockDim.x) {
     const int L = lens[i];
     if (L > 0 && L <= cap) {
       acc += L;
@@ -136,7 +144,7 @@ __device__ inline int plan_chunk(const int32_t* __restrict__ lens, int n_seq, in
   long long cnt[kPlanCand];
 #pragma unroll
   for (int k = 0; k < kPlanCand; ++k) cnt[k] = 0;
-  for (int i = threadIdx.x; i < n_seq; i += kThreads) {
+  for (int i = threadIdx.x; i < n_seq; i += blockDim.x) {
     const int L = lens[i];
 #pragma unroll
     for (int k = 0; k < kPlanCand; ++k) cnt[k] += n_chunks_of(L, cap, static_cast<int>(c0) + kChunkGranule * k);
@@ -352,7 +360,7 @@ struct MergeShared {
 // Number of (sequence, chunk) pairs before sequence s.
 __device__ inline int plan_prefix(const int32_t* __restrict__ lens, int s, int cap, int chunk, long long* sh) {
   long long acc = 0;
-  for (int i = threadIdx.x; i < s; i += kThreads) acc += n_chunks_of(lens[i], cap, chunk);
+  for (int i = threadIdx.x; i < s; i += blockDim.x) acc += n_chunks_of(lens[i], cap, chunk);
   return static_cast<int>(block_sum(acc, sh));
 }
 

@@ -652,6 +652,17 @@ pa_status pa_split_plan(const int32_t* seq_lens_host, int32_t n_seq, int32_t cap
   return PA_OK;
 }
 
+pa_status pa_split_workgroups_per_cu(int32_t kv_type, int32_t n_qtok, uint32_t flags, int32_t* wgs) {
+  if (!wgs || n_qtok < 1 || n_qtok > PA_MAX_QTOK || (flags & ~PA_DECODE_VECTOR_REFERENCE)) return PA_ERR_INVALID;
+  int kt = 0, vt = 0;
+  const pa_status ts = parse_kv_type(kv_type, &kt, &vt);
+  if (ts != PA_OK) return ts;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return PA_ERR_HIP;
+  *wgs = pa::split_wgs_per_cu(kt, vt, n_qtok, (flags & PA_DECODE_VECTOR_REFERENCE) ? 1 : 0);
+  return PA_OK;
+}
+
 pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device, size_t* bytes) {
   if (!bytes || n_seq < 0 || n_qtok < 1 || n_qtok > PA_MAX_PREFILL_TOKENS) return PA_ERR_INVALID;
   *bytes = pa::workspace_layout_items(workspace_items(n_seq, n_qtok, true, device), kGroupTokens).total;

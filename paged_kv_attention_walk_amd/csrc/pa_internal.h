@@ -17,7 +17,8 @@ constexpr int kGroup = kQHeads / kKvHeads;  // query heads per KV head
 constexpr int kMaxQtok = 8;
 constexpr int kChunkGranule = 128;          // chunk lengths are multiples of this (32 keys x 4 waves)
 constexpr int kPlanCand = 4;                // chunk lengths the plan tries at once
-constexpr int kPlanShared = 4 * kPlanCand;  // long long slots of the plan's shared scratch
+constexpr int kMaxWaves = 8;                // waves of the largest workgroup
+constexpr int kPlanShared = kMaxWaves * kPlanCand;  // long long slots of the plan's shared scratch
 
 enum KvType { kF16 = 1, kBF16 = 2, kQ8_0 = 3, kQ4_0 = 4 };
 

@@ -2,6 +2,7 @@
 its allocator matches the allocator model bit for bit, and host-side argument
 checks fail before anything reaches the device.  No compute call is made."""
 
+import ctypes
 import os
 import re
 
@@ -220,3 +221,15 @@ def test_read_bandwidth_probe_host_checks():
     assert lib.pa_read_bandwidth_probe(a + 4, 1024, a, 1 << 20, None) == pb.ERR_INVALID     # misaligned source
     assert lib.pa_read_bandwidth_probe(a, 1024, a + 2, 1 << 20, None) == pb.ERR_INVALID     # misaligned sink
     assert lib.pa_read_bandwidth_probe(a, 1024, a, 4, None) == pb.ERR_INVALID               # sink too small
+
+
+def test_split_workgroups_per_cu_rejects_bad_arguments():
+    # argument checks come before any device call
+    lib = pb.lib()
+    w = ctypes.c_int32(-7)
+    q4 = pb.kv_type("q4_0")
+    assert lib.pa_split_workgroups_per_cu(q4, 1, 0, None) == pb.ERR_INVALID
+    for kv, t, flags in ((q4, 0, 0), (q4, pb.MAX_QTOK + 1, 0), (0, 1, 0), (9, 1, 0), (q4 | (9 << 8), 1, 0),
+                         (q4, 1, 2)):
+        assert lib.pa_split_workgroups_per_cu(kv, t, flags, ctypes.byref(w)) == pb.ERR_INVALID
+    assert w.value == -7

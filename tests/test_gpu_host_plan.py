@@ -121,8 +121,9 @@ def test_host_plan_prefill(engine):
 def test_device_plan_equals_host_plan(seed):
     # the device-planned split kernel leaves its chunk length and each
     # sequence's first chunk in the workspace header (words 1 and 2 + s, up to
-    # 62 sequences); they must equal pa_split_plan's for this device's CU count
-    # and the kernel's two resident workgroups per CU (one-token Q4_0)
+    # 1022 sequences); they must equal pa_split_plan's for this device's CU
+    # count and the resident split workgroups per CU the library reports for
+    # a one-token Q4_0 call
     import torch
     from paged_kv_attention_walk_amd import binding as pb
     rng = np.random.default_rng(470 + seed)
@@ -137,6 +138,8 @@ def test_device_plan_equals_host_plan(seed):
     assert err == 0
     hdr = ws[:2 + n].cpu().numpy()
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
-    chunk, items, first = pb.split_plan(w["seq_lens"], w["block_table"].shape[1] * 16, n_cu, 2)
+    wgs = pb.split_workgroups_per_cu("q4_0", 1)
+    assert wgs >= 1
+    chunk, items, first = pb.split_plan(w["seq_lens"], w["block_table"].shape[1] * 16, n_cu, wgs)
     assert hdr[1] == chunk, (hdr[1], chunk)
     assert list(hdr[2:2 + n]) == list(first[:n])

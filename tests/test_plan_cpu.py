@@ -82,9 +82,13 @@ def test_even_many_sequence_batch_keeps_one_chunk_per_head():
 
 
 def test_headline_ragged_workload():
-    # 131072 + 7 x 8192, 16-position pages: 1536-position chunks, 512 items
-    # on 256 compute units x 2 workgroups (one round of resident workgroups)
+    # 131072 + 7 x 8192, 16-position pages: one round of resident workgroups,
+    # 512 items of 1536 positions on 256 compute units x 2 workgroups (one
+    # workgroup per compute unit would give 256 items of 3072)
     lens = [131072] + [8192] * 7
+    chunk, items, first = pb.split_plan(lens, 131072, 256, 1)
+    assert (chunk, items) == (3072, 256)
+    assert list(first) == [0, 43, 46, 49, 52, 55, 58, 61, 64]
     chunk, items, first = pb.split_plan(lens, 131072, 256, 2)
     assert (chunk, items) == (1536, 512)
     assert list(first) == [0, 86, 92, 98, 104, 110, 116, 122, 128]
