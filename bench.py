@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of back-to-back untimed steps before every timed run (on top of --warmup): "
                          "the clocks reach their steady state only after some milliseconds of continuous work")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="only sweep pa_read_bandwidth_probe_ex over its configurations (the measured read ceiling)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only time a plain 2 GiB device-to-device copy (read-bandwidth ceiling; also the "
                          "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -87,7 +89,8 @@ def copy_ceiling(steps=20, nbytes=2 << 30):
 def read_ceiling(steps=20, nbytes=2 << 30):
     """HBM read rate of pa_read_bandwidth_probe (16-byte loads, every byte of
     `nbytes` read once) on this machine: the practical ceiling of the K/V stream,
-    reported beside the 8 TB/s nominal peak."""
+    reported beside the 8 TB/s nominal peak (bench.py --ceiling-sweep times
+    the probe's other configurations)."""
     import torch
     from paged_kv_attention_walk_amd import binding as pb
     a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
@@ -104,8 +107,48 @@ def read_ceiling(steps=20, nbytes=2 << 30):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     del a, sink
-    return {"kernel": "pa_read_bandwidth_probe over 2 GiB (16-byte loads)", "bytes_read": nbytes, "ms": round(ms, 4),
-            "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return {"kernel": "pa_read_bandwidth_probe over 2 GiB (16-byte loads, 8 workgroups per CU, one load in flight "
+                      "per lane: the fastest configuration of the sweep in profiles/read_ceiling_sweep.md)",
+            "bytes_read": nbytes, "ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def ceiling_sweep(steps=10):
+    """pa_read_bandwidth_probe_ex over workgroups per CU x loads in flight x
+    access (grid-stride or per-workgroup slice) x load kind (registers or
+    direct to LDS) on a 4 GiB buffer, then the best configurations on 2 and
+    8 GiB.  Returns {"runs": [...], "best": {...}}."""
+    import torch
+    from paged_kv_attention_walk_amd import binding as pb
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(4 * 32 * n_cu, dtype=torch.int32, device="cuda")
+    bufs = {gib: torch.ones((gib << 30) // 4, dtype=torch.int32, device="cuda") for gib in (2, 4, 8)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(buf, wgs, u, flags):
+        for _ in range(2):
+            pb.read_bandwidth_probe_ex(buf, sink, wgs, u, flags)
+        e0.record()
+        for _ in range(steps):
+            pb.read_bandwidth_probe_ex(buf, sink, wgs, u, flags)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        return round(buf.numel() * 4 / (ms * 1e-3) / 1e9, 1)
+
+    runs = []
+    for flags in (0, pb.PROBE_SLICE, pb.PROBE_LDS, pb.PROBE_SLICE | pb.PROBE_LDS):
+        for wgs in (1, 2, 4, 8, 16, 32):
+            for u in (1, 2, 4, 8, 16):
+                runs.append({"gib": 4, "wgs_per_cu": wgs, "loads_in_flight": u,
+                             "slice": bool(flags & pb.PROBE_SLICE), "lds": bool(flags & pb.PROBE_LDS),
+                             "gbps": rate(bufs[4], wgs, u, flags)})
+    top = sorted(runs, key=lambda r: -r["gbps"])[:4]
+    for r in top:
+        flags = (pb.PROBE_SLICE if r["slice"] else 0) | (pb.PROBE_LDS if r["lds"] else 0)
+        for gib in (2, 8):
+            runs.append(dict(r, gib=gib, gbps=rate(bufs[gib], r["wgs_per_cu"], r["loads_in_flight"], flags)))
+    del bufs
+    return {"runs": runs, "best": max(runs, key=lambda r: r["gbps"])}
 
 
 def kernel_source_hash():
@@ -203,6 +246,9 @@ def main():
     torch.cuda.set_device(0)
     if args.ceiling:
         print(json.dumps({"copy_ceiling": copy_ceiling()}), flush=True)
+        return
+    if args.ceiling_sweep:
+        print(json.dumps({"read_ceiling_sweep": ceiling_sweep()}), flush=True)
         return
     ceiling = read_ceiling()
     t_gen = time.perf_counter()

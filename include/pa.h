@@ -56,8 +56,8 @@ const char *pa_status_string(pa_status s);
 /* Library version, "major.minor.patch".  The minor number changes when a
  * struct of this header grows or calls are added: 0.2 added
  * pa_decode_ext.seq_lens_host, pa_split_plan and pa_read_bandwidth_probe;
- * 0.3 added pa_split_workgroups_per_cu and attaches pa_decode_ext.split_events
- * to the split kernel's dispatch. */
+ * 0.3 added pa_split_workgroups_per_cu and pa_read_bandwidth_probe_ex and
+ * attaches pa_decode_ext.split_events to the split kernel's dispatch. */
 #define PA_VERSION_STRING "0.3.0"
 const char *pa_version(void);
 
@@ -398,16 +398,33 @@ pa_status pa_get_device_error(pa_pool *pool, void *workspace, hipStream_t stream
                               int32_t clear, int32_t *err);
 
 /* Measurement helper: reads `bytes` (a multiple of 16) of device memory at
- * `src` (16-byte aligned) once with 16-byte loads, 8 workgroups per compute
- * unit in a grid-stride loop with four loads in flight per lane, and folds
- * them into one word per wave written to `sink` (device, at least
- * 32 x compute-unit-count words).  Time it to get the HBM read rate that a
- * pure stream of 16-byte loads reaches on this device, the practical ceiling
- * for the K/V stream of pa_decode (the bound the decode roofline refers to:
- * lucebox pull 555 and achyudh/llama.cpp pull 2 report their decode
- * throughput as a share of the card's bandwidth).  Enqueued on `stream`.
+ * `src` (16-byte aligned) once with 16-byte loads and folds them into one
+ * word per wave written to `sink` (device, at least
+ * 4 x wgs_per_cu x compute-unit-count words).  Time it to get the HBM read
+ * rate that a pure stream of 16-byte loads reaches on this device, the
+ * practical ceiling for the K/V stream of pa_decode (the bound the decode
+ * roofline refers to: lucebox pull 555 and achyudh/llama.cpp pull 2 report
+ * their decode throughput as a share of the card's bandwidth).  Enqueued on
+ * `stream`.
+ * wgs_per_cu      256-thread workgroups per compute unit (1..32).
+ * loads_in_flight 16-byte loads issued back to back per lane (1, 2, 4, 8, 16).
+ * flags           PA_PROBE_SLICE: each workgroup streams one contiguous share
+ *                 of the buffer (as a split-K work item streams its chunk)
+ *                 instead of a grid-stride loop over the whole of it;
+ *                 PA_PROBE_LDS: the loads write LDS directly
+ *                 (global_load_lds_dwordx4) instead of registers.
+ * pa_read_bandwidth_probe is this call with the configuration that measured
+ * fastest on MI355X (PA_PROBE_DEFAULT_*).
  * Errors: PA_ERR_INVALID (null or misaligned pointers, bytes 0 or not a
- * multiple of 16, sink too small), PA_ERR_HIP. */
+ * multiple of 16, sink too small, a parameter out of range), PA_ERR_HIP. */
+#define PA_PROBE_SLICE 1u
+#define PA_PROBE_LDS   2u
+#define PA_PROBE_DEFAULT_WGS    8
+#define PA_PROBE_DEFAULT_LOADS  1
+#define PA_PROBE_DEFAULT_FLAGS  0u
+pa_status pa_read_bandwidth_probe_ex(const void *src, size_t bytes, uint32_t *sink, size_t sink_words,
+                                     int32_t wgs_per_cu, int32_t loads_in_flight, uint32_t flags,
+                                     hipStream_t stream);
 pa_status pa_read_bandwidth_probe(const void *src, size_t bytes, uint32_t *sink, size_t sink_words,
                                   hipStream_t stream);
 

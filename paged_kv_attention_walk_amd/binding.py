@@ -35,7 +35,8 @@ EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "
            "pa_pool_get_info", "pa_alloc_blocks", "pa_free_blocks", "pa_append_kv", "pa_append_kv_device",
            "pa_decode",
            "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather", "pa_prefill",
-           "pa_prefill_workspace_size", "pa_split_plan", "pa_read_bandwidth_probe", "pa_split_workgroups_per_cu")
+           "pa_prefill_workspace_size", "pa_split_plan", "pa_read_bandwidth_probe", "pa_split_workgroups_per_cu",
+           "pa_read_bandwidth_probe_ex")
 
 
 def kv_type(k, v=0) -> int:
@@ -104,6 +105,7 @@ def _lib():
             "pa_debug_gather": (I32, [VP, I32, VP, I32, I32, I32, I32, I32, VP, VP, VP]),
             "pa_split_plan": (I32, [VP, I32, I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), VP]),
             "pa_read_bandwidth_probe": (I32, [VP, SZ, VP, SZ, VP]),
+            "pa_read_bandwidth_probe_ex": (I32, [VP, SZ, VP, SZ, I32, I32, ctypes.c_uint32, VP]),
             "pa_split_workgroups_per_cu": (I32, [I32, I32, ctypes.c_uint32, ctypes.POINTER(I32)]),
         }
         for name, (res, args) in sig.items():
@@ -308,6 +310,16 @@ def read_bandwidth_probe(src, sink, stream=None):
     a multiple of 16 bytes), folding into device int32/uint32 tensor `sink`."""
     _check(_lib().pa_read_bandwidth_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
                                           _stream(stream)), "pa_read_bandwidth_probe")
+
+
+PROBE_SLICE, PROBE_LDS = 1, 2
+
+
+def read_bandwidth_probe_ex(src, sink, wgs_per_cu, loads_in_flight, flags=0, stream=None):
+    """pa_read_bandwidth_probe_ex: the probe with an explicit configuration."""
+    _check(_lib().pa_read_bandwidth_probe_ex(_ptr(src), src.numel() * src.element_size(), _ptr(sink), sink.numel(),
+                                             int(wgs_per_cu), int(loads_in_flight), int(flags), _stream(stream)),
+           "pa_read_bandwidth_probe_ex")
 
 
 def prefill_workspace_size(n_seq, n_qtok, device=0) -> int:

@@ -685,15 +685,26 @@ pa_status pa_get_device_error(pa_pool* pool, void* workspace, hipStream_t stream
   return PA_OK;
 }
 
-pa_status pa_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
-                                  hipStream_t stream) {
+pa_status pa_read_bandwidth_probe_ex(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                                     int32_t wgs_per_cu, int32_t loads_in_flight, uint32_t flags,
+                                     hipStream_t stream) {
   if (!src || !sink || bytes == 0 || bytes % 16 || !aligned(src, 16) || !aligned(sink, 4)) return PA_ERR_INVALID;
+  if (wgs_per_cu < 1 || wgs_per_cu > 32 || (flags & ~(PA_PROBE_SLICE | PA_PROBE_LDS))) return PA_ERR_INVALID;
+  const int u = loads_in_flight;
+  if (u != 1 && u != 2 && u != 4 && u != 8 && u != 16) return PA_ERR_INVALID;
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) device = 0;
   const int cu = cu_count(device);
-  const int64_t blocks = static_cast<int64_t>(cu > 0 ? cu : 256) * 8;
+  const int64_t blocks = static_cast<int64_t>(cu > 0 ? cu : 256) * wgs_per_cu;
   if (static_cast<int64_t>(sink_words) < blocks * 4) return PA_ERR_INVALID;
-  return hip_status(pa::launch_read_probe(src, bytes, sink, static_cast<int32_t>(blocks), stream));
+  return hip_status(pa::launch_read_probe(src, bytes, sink, static_cast<int32_t>(blocks), u,
+                                          (flags & PA_PROBE_LDS) != 0, (flags & PA_PROBE_SLICE) != 0, stream));
+}
+
+pa_status pa_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                                  hipStream_t stream) {
+  return pa_read_bandwidth_probe_ex(src, bytes, sink, sink_words, PA_PROBE_DEFAULT_WGS, PA_PROBE_DEFAULT_LOADS,
+                                    PA_PROBE_DEFAULT_FLAGS, stream);
 }
 
 pa_status pa_debug_gather(const void* pool, int32_t row_bytes, const int32_t* block_table, int32_t bt_stride,

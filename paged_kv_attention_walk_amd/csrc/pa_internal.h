@@ -238,8 +238,11 @@ struct AppendLaunch {
 hipError_t launch_append_encode(const AppendLaunch& l, hipStream_t stream);
 
 // Read-bandwidth probe: `blocks` workgroups read `bytes` (a multiple of 16)
-// once; sink receives blocks * 4 words.
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, hipStream_t stream);
+// once with `unroll` (1, 2, 4, 8 or 16) 16-byte loads in flight per lane,
+// into registers or straight to LDS, grid-stride or one contiguous slice per
+// workgroup; sink receives blocks * 4 words.
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll,
+                             bool to_lds, bool slice, hipStream_t stream);
 
 hipError_t launch_gather(const uint8_t* pool, int32_t row_bytes, const int32_t* bt, int32_t bt_stride,
                          int32_t n_pool_blocks, int32_t seq, int32_t seq_len, int32_t page_size,

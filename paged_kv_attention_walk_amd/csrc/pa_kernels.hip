@@ -81,22 +81,54 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const uint8_t* __restr
 
 // ------------------------------------------------------- read ceiling
 //
-// Reads n16 16-byte words once each (grid-stride, four loads in flight per
-// lane) and folds them with xor; one word per wave goes to `sink` so that
-// nothing is optimised away.  The HBM read rate the decode kernels are
-// compared against.
+// Reads n16 16-byte words once each and folds them with xor; one word per
+// wave goes to `sink` so that nothing is optimised away.  The HBM read rate
+// the decode kernels are compared against.  U loads are in flight per lane.
+// Access: grid-stride (consecutive lanes, then waves, then workgroups read
+// adjacent words; a step of the loop covers the whole grid), or per-slice
+// (each workgroup streams one contiguous share of the buffer in 4 KB
+// steps, as a split-K work item streams its chunk).  Loads land in registers,
+// or with kLds go straight to LDS (global_load_lds_dwordx4): the data is not
+// used there, every load of a wave overwrites the wave's one 1 KB slot.
+template <int U, bool kLds, bool kSlice>
 __global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint4* __restrict__ src, size_t n16,
                                                               uint32_t* __restrict__ sink) {
-  const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
-  size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-  uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= (a.x ^ a.y ^ a.z ^ a.w) ^ (b.x ^ b.y ^ b.z ^ b.w) ^ (c.x ^ c.y ^ c.z ^ c.w) ^ (d.x ^ d.y ^ d.z ^ d.w);
+  __shared__ __attribute__((aligned(16))) uint32_t slot[kLds ? kThreads * 4 : 4];
+  size_t i, end, stride;
+  if constexpr (kSlice) {
+    const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const size_t first = static_cast<size_t>(blockIdx.x) * per;
+    end = first + per < n16 ? first + per : n16;
+    i = first + threadIdx.x;
+    stride = kThreads;
+  } else {
+    end = n16;
+    i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    stride = static_cast<size_t>(gridDim.x) * kThreads;
   }
-  for (; i < n16; i += stride) {
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < end; i += U * stride) {
+    if constexpr (kLds) {
+      typedef __attribute__((address_space(3))) void lds_void;
+      lds_void* dst = reinterpret_cast<lds_void*>(reinterpret_cast<uintptr_t>(slot) + (threadIdx.x >> 6) * 1024);
+#pragma unroll
+      for (int u = 0; u < U; ++u) __builtin_amdgcn_global_load_lds(src + i + u * stride, dst, 16, 0, 0);
+    } else {
+      uint4 a[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = src[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+    }
+  }
+  for (; i < end; i += stride) {
     const uint4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if constexpr (kLds) {
+    __builtin_amdgcn_s_waitcnt(0);      // every direct-to-LDS load has landed
+    __syncthreads();
+    acc ^= slot[threadIdx.x];
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m, 64);
@@ -188,10 +220,28 @@ hipError_t launch_scatter(const uint8_t* staging, int32_t n_rows, uint8_t* k_poo
   return hipGetLastError();
 }
 
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(src), bytes / 16, sink);
+template <bool kLds, bool kSlice>
+hipError_t launch_read_probe_u(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll,
+                               hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  const uint4* s = static_cast<const uint4*>(src);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL((read_probe_kernel<1, kLds, kSlice>), grid, block, 0, stream, s, bytes / 16, sink); break;
+    case 2: hipLaunchKernelGGL((read_probe_kernel<2, kLds, kSlice>), grid, block, 0, stream, s, bytes / 16, sink); break;
+    case 4: hipLaunchKernelGGL((read_probe_kernel<4, kLds, kSlice>), grid, block, 0, stream, s, bytes / 16, sink); break;
+    case 8: hipLaunchKernelGGL((read_probe_kernel<8, kLds, kSlice>), grid, block, 0, stream, s, bytes / 16, sink); break;
+    case 16: hipLaunchKernelGGL((read_probe_kernel<16, kLds, kSlice>), grid, block, 0, stream, s, bytes / 16, sink); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll,
+                             bool to_lds, bool slice, hipStream_t stream) {
+  if (to_lds) return slice ? launch_read_probe_u<true, true>(src, bytes, sink, blocks, unroll, stream)
+                           : launch_read_probe_u<true, false>(src, bytes, sink, blocks, unroll, stream);
+  return slice ? launch_read_probe_u<false, true>(src, bytes, sink, blocks, unroll, stream)
+               : launch_read_probe_u<false, false>(src, bytes, sink, blocks, unroll, stream);
 }
 
 hipError_t launch_gather(const uint8_t* pool, int32_t row_bytes, const int32_t* bt, int32_t bt_stride,

@@ -221,6 +221,12 @@ def test_read_bandwidth_probe_host_checks():
     assert lib.pa_read_bandwidth_probe(a + 4, 1024, a, 1 << 20, None) == pb.ERR_INVALID     # misaligned source
     assert lib.pa_read_bandwidth_probe(a, 1024, a + 2, 1 << 20, None) == pb.ERR_INVALID     # misaligned sink
     assert lib.pa_read_bandwidth_probe(a, 1024, a, 4, None) == pb.ERR_INVALID               # sink too small
+    ex = lib.pa_read_bandwidth_probe_ex
+    for wgs, u, flags in ((0, 4, 0), (33, 4, 0), (8, 0, 0), (8, 3, 0), (8, 32, 0), (8, 4, 4)):
+        assert ex(a, 1024, a, 1 << 20, wgs, u, flags, None) == pb.ERR_INVALID, (wgs, u, flags)
+    assert ex(a, 1024, a, 4 * 16 * 256 - 1, 16, 4, 0, None) == pb.ERR_INVALID                  # short of 4 x wgs x 256 CUs
+    assert ex(None, 1024, a, 1 << 20, 8, 4, 0, None) == pb.ERR_INVALID
+    assert ex(a, 1000, a, 1 << 20, 8, 4, 0, None) == pb.ERR_INVALID
 
 
 def test_split_workgroups_per_cu_rejects_bad_arguments():

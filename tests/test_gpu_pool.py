@@ -183,3 +183,31 @@ def test_read_bandwidth_probe_reads_every_word_once(nbytes):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy())
     assert got == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("wgs,u,slice_", [(1, 1, False), (4, 16, False), (32, 2, False), (2, 8, True), (16, 4, True),
+                                          (8, 16, True)])
+def test_read_bandwidth_probe_ex_reads_every_word_once(wgs, u, slice_):
+    # every register-load configuration of the probe reads each word once
+    nbytes = (1 << 22) + 16 * 77
+    rng = np.random.default_rng(wgs * 100 + u)
+    host = rng.integers(-2**31, 2**31 - 1, size=nbytes // 4, dtype=np.int64).astype(np.int32)
+    log(f"[case] read probe ex wgs={wgs} loads={u} slice={slice_}")
+    src = torch.from_numpy(host).cuda()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros((4 * wgs * n_cu,), dtype=torch.int32, device="cuda")
+    pb.read_bandwidth_probe_ex(src, sink, wgs, u, pb.PROBE_SLICE if slice_ else 0)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy()) == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("slice_", [False, True])
+def test_read_bandwidth_probe_ex_direct_to_lds_runs(slice_):
+    # the direct-to-LDS loads discard the data (each wave overwrites one LDS
+    # slot), so only completion is checked
+    src = torch.ones((1 << 20) // 4 + 4 * 13, dtype=torch.int32, device="cuda")
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros((4 * 8 * n_cu,), dtype=torch.int32, device="cuda")
+    log(f"[case] read probe ex direct to LDS slice={slice_}")
+    pb.read_bandwidth_probe_ex(src, sink, 8, 8, pb.PROBE_LDS | (pb.PROBE_SLICE if slice_ else 0))
+    torch.cuda.synchronize()
