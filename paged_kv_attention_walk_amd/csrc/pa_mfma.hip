@@ -124,6 +124,26 @@ __device__ inline void split8(const float (&x)[8], u4& hi, u4& lo, bool bf) {
   }
 }
 
+__device__ inline uint32_t pkrtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// 8 floats as f16 hi + lo parts with round-toward-zero conversions: hi =
+// rtz(x) and lo = rtz(x - hi), where x - hi is exact in f32 (hi keeps the
+// leading 11 bits of x), so hi + lo holds x to about 22 bits.  With `m` = 0
+// a lane gets hi in `lo` as well, with m = -1 the remainder: the one-token
+// packing takes its part with no select (lanes n < 8 hi, n >= 8 lo).
+__device__ inline void split8_rtz(const float (&x)[8], u4& hi, u4& lo, float m) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t h = pkrtz(x[2 * k], x[2 * k + 1]);
+    hi[k] = h;
+    const h2 hv = __builtin_bit_cast(h2, h);
+    lo[k] = pkrtz(__builtin_fmaf(static_cast<float>(hv[0]), m, x[2 * k]),
+                  __builtin_fmaf(static_cast<float>(hv[1]), m, x[2 * k + 1]));
+  }
+}
+
 // (x & mask) | (0x64006400 & ~mask): one bit-field insert.
 __device__ inline uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) {
   uint32_t r;
@@ -252,23 +272,27 @@ struct Half {
   bool live;    // inside the chunk, with a valid table entry
 };
 
-// Where the chunk's block-table entries are read: an LDS copy of entries
-// [lp0, lp0 + kTblCap) once staged, else the table itself through the
-// constant address space (scalar loads).  Both give wave-uniform values and
-// are waited on with the scalar / LDS counter, never behind tile loads.
+// Where a group's rows are found.  Rows in LDS: entry j is the first pool
+// row of the 16-position group at k0 + 16 j for this workgroup's KV head
+// (the row-address arithmetic done once per group before the loop), or -1
+// when its block-table entry lies outside the pool; entries past the chunk
+// end are 0 (in bounds, masked).  A tile reads both of its entries with one
+// 8-byte LDS read, issued a tile ahead.  Otherwise (contiguous storage, the
+// chunk's first tile, or chunks of more than kGrpCap groups) the row comes
+// from the block table through the constant address space (scalar loads).
+// Either way the values are wave-uniform and never wait behind tile loads.
 typedef __attribute__((address_space(3))) const int lds_int;
-constexpr int kTblCap = 1024;
+constexpr int kGrpCap = 1024;
 
 struct Pages {
-  lds_int* tbl;
-  int lp0;
+  lds_int* grp;
   bool in_lds;
 };
 
-// Locates the 16-position group at pos0 (all arguments wave-uniform).  `bad`
-// is set for a group inside the chunk whose table entry is outside the pool.
-__device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int h, int pos0, int k0, int k1,
-                              bool& bad) {
+// Locates the 16-position group at pos0 (all arguments wave-uniform) from the
+// block table.  `bad` is set for a group inside the chunk whose table entry
+// is outside the pool.
+__device__ inline Half locate(const DecodeParams& p, int s, int h, int pos0, int k0, int k1, bool& bad) {
   const bool in = pos0 < k1;
   const int pos = in ? pos0 : k0;
   Half r;
@@ -278,19 +302,30 @@ __device__ inline Half locate(const DecodeParams& p, const Pages& pg, int s, int
     r.live = in;
     return r;
   }
-  // page and slot of pos (a shift for power-of-two pages: this runs twice per tile)
-  const int lp = (p.page_shift >= 0) ? (pos >> p.page_shift) : pos / p.page_size;
+  const int lp = pos / p.page_size;
   const int slot = pos - lp * p.page_size;
-  int phys;
-  if (pg.in_lds) {
-    phys = __builtin_amdgcn_readfirstlane(pg.tbl[lp - pg.lp0]);
-  } else {
-    phys = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
-        reinterpret_cast<uintptr_t>(p.bt))[static_cast<size_t>(s) * p.bt_stride + lp];
-  }
+  const int phys = reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      reinterpret_cast<uintptr_t>(p.bt))[static_cast<size_t>(s) * p.bt_stride + lp];
   const bool ok = static_cast<unsigned>(phys) < static_cast<unsigned>(p.n_pool_blocks);
   if (in && !ok) bad = true;
   r.row = ok ? (static_cast<size_t>(phys) * kKvHeads + h) * p.page_size + slot : 0;
+  r.live = in && ok;
+  return r;
+}
+
+// The LDS row entries of tile ti's two groups (read early; used by the next
+// load of that tile).
+__device__ inline i2 read_rows(const Pages& pg, int ti) {
+  return pg.in_lds ? *reinterpret_cast<const __attribute__((address_space(3))) i2*>(pg.grp + 2 * ti) : i2{0, 0};
+}
+
+// The group at pos0 from its LDS entry e (wave-uniform after readfirstlane).
+__device__ inline Half from_entry(int e, int pos0, int k1, bool& bad) {
+  const bool in = pos0 < k1;
+  const bool ok = e >= 0;
+  if (in && !ok) bad = true;
+  Half r;
+  r.row = ok ? static_cast<size_t>(e) : 0;
   r.live = in && ok;
   return r;
 }
@@ -337,8 +372,8 @@ __device__ inline u4a ld128(const uint8_t* base, uint32_t off) { return *reinter
 // Issues the loads of the tile at tb.  Only loads: no instruction here reads
 // a loaded register.
 template <int KT, int VT>
-__device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, int h, int tb, int k0, int k1,
-                                 Tile<KT, VT>& t, bool& bad) {
+__device__ inline void load_tile(const DecodeParams& p, const Pages& pg, i2 rows, int s, int h, int tb, int k0,
+                                 int k1, Tile<KT, VT>& t, bool& bad) {
   using F = Fmt<KT>;
   using FV = Fmt<VT>;
   const int lane = threadIdx.x & 63;
@@ -347,7 +382,8 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, int s, 
   const uint8_t* rk_half[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const Half hv = locate(p, pg, s, h, tb + 16 * hf, k0, k1, bad);
+    const Half hv = pg.in_lds ? from_entry(__builtin_amdgcn_readfirstlane(rows[hf]), tb + 16 * hf, k1, bad)
+                              : locate(p, s, h, tb + 16 * hf, k0, k1, bad);
     t.live[hf] = hv.live;
     const uint8_t* rk = p.k + hv.row * F::kRow;
     const uint8_t* rv = p.v + hv.row * FV::kRow;
@@ -718,10 +754,19 @@ __device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = p[e];
     }
-    split8(x, bh[nt], bl[nt], Fmt<VT>::kQuant ? false : Fmt<VT>::kBf);
-    if constexpr (C::kPack) {
+    if constexpr (Fmt<VT>::kBf) {
+      split8(x, bh[nt], bl[nt], true);
+      if constexpr (C::kPack) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) bh[nt][k] = lo_lane ? bl[nt][k] : bh[nt][k];
+        for (int k = 0; k < 4; ++k) bh[nt][k] = lo_lane ? bl[nt][k] : bh[nt][k];
+      }
+    } else if constexpr (C::kPack) {
+      u4 h, l;
+      split8_rtz(x, h, l, -1.f);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bh[nt][k] = lo_lane ? l[k] : h[k];   // this lane's part
+    } else {
+      split8_rtz(x, bh[nt], bl[nt], -1.f);
     }
   }
   return __ballot(any) != 0;
@@ -925,18 +970,11 @@ __device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wa
   }
 }
 
-// Issue priority from the share of this wave's tiles still to do.  Two
-// workgroups share each compute unit and the hardware favours the older
-// wave of a SIMD; a wave that falls behind its SIMD partner (which has the
-// same share of work) gets ahead in issue instead of finishing alone at the
-// end.  Results do not depend on it.
-__device__ inline void set_prio_remaining(int rem, int total) {
-  const int q = total > 0 ? (4 * rem - 1) / total : 0;
-  if (q >= 3) __builtin_amdgcn_s_setprio(3);
-  else if (q == 2) __builtin_amdgcn_s_setprio(2);
-  else if (q == 1) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
+// Issue priority (set per tile in the double-buffered loop) follows the
+// share of this wave's tiles still to do.  Two workgroups share each compute
+// unit and the hardware favours the older wave of a SIMD; a wave that falls
+// behind its SIMD partner (which has the same share of work) gets ahead in
+// issue instead of finishing alone at the end.  Results do not depend on it.
 
 // Register double-buffering of the next tile pays for the compact quant rows;
 // the 16-bit rows use a single buffer (their loads are large enough that the
@@ -964,7 +1002,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
-  __shared__ int tbl_lds[kTblCap];
+  __shared__ __attribute__((aligned(16))) int grp_lds[kGrpCap];
   __shared__ float ml_lds[4][R][2];
   __shared__ float row_stat[2][R];                   // per row: 1 / sum of weights, log2-sum-exp
   __shared__ long long sh_sum[kPlanShared];
@@ -1037,34 +1075,43 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   bool bad = false;
   const int n_tiles = (k1 > k0) ? (k1 - k0 + 31) / 32 : 0;
 
-  // The chunk's table entries go to LDS (read there once the barrier below
-  // has passed); the first tile, loaded before it, reads the table itself.
-  Pages pg{(lds_int*)(tbl_lds), 0, false};
-  bool tbl_fits = false;
-  // The entries are loaded into registers here and written to LDS once q and
-  // the first tile are in flight as well (loads return in order, so the
-  // writes wait for the table alone).
-  constexpr int kTblPer = kTblCap / kThreads;
-  int tbl_v[kTblPer];
-  int n_tbl = 0;
-  if (p.bt != nullptr && k1 > k0) {
-    pg.lp0 = k0 / p.page_size;
-    n_tbl = (k1 - 1) / p.page_size - pg.lp0 + 1;
-    tbl_fits = n_tbl <= kTblCap;
-    if (tbl_fits) {
+  // The rows of the chunk's 16-position groups go to LDS (read there once the
+  // barrier below has passed); the first tile, loaded before it, reads the
+  // table itself.  The table entries are loaded here and turned into rows
+  // and written to LDS once q and the first tile are in flight as well
+  // (loads return in order, so the writes wait for the table alone).  Row
+  // indices are int32: pools of fewer than 2^31 rows per KV-head set.
+  Pages pg{(lds_int*)(grp_lds), false};
+  const int n_grp = 2 * n_tiles;                        // the tiles' groups (the last may lie past k1)
+  const bool grp_fits = p.bt != nullptr && n_grp <= kGrpCap &&
+                        static_cast<long long>(p.n_pool_blocks) * kKvHeads * p.page_size < (1ll << 31);
+  constexpr int kGrpPer = kGrpCap / kThreads;
+  int grp_v[kGrpPer];
+  auto page_of = [&](int pos) { return (p.page_shift >= 0) ? (pos >> p.page_shift) : pos / p.page_size; };
+  if (grp_fits) {
 #pragma unroll
-      for (int k = 0; k < kTblPer; ++k) {
-        const int i = tid + kThreads * k;
-        if (i < n_tbl) tbl_v[k] = p.bt[static_cast<size_t>(s) * p.bt_stride + pg.lp0 + i];
-      }
+    for (int k = 0; k < kGrpPer; ++k) {
+      const int j = tid + kThreads * k;
+      const int pos = k0 + 16 * j;
+      if (j < n_grp && pos < k1) grp_v[k] = p.bt[static_cast<size_t>(s) * p.bt_stride + page_of(pos)];
     }
   }
-  auto stage_table = [&]() {
-    if (tbl_fits) {
+  auto stage_rows = [&]() {
+    if (grp_fits) {
 #pragma unroll
-      for (int k = 0; k < kTblPer; ++k) {
-        const int i = tid + kThreads * k;
-        if (i < n_tbl) tbl_lds[i] = tbl_v[k];
+      for (int k = 0; k < kGrpPer; ++k) {
+        const int j = tid + kThreads * k;
+        const int pos = k0 + 16 * j;
+        if (j < n_grp) {
+          int row = 0;                                    // past the chunk: in bounds, masked
+          if (pos < k1) {
+            const int e = grp_v[k], lp = page_of(pos);
+            row = (static_cast<unsigned>(e) < static_cast<unsigned>(p.n_pool_blocks))
+                      ? (e * kKvHeads + h) * p.page_size + (pos - lp * p.page_size)
+                      : -1;
+          }
+          grp_lds[j] = row;
+        }
       }
     }
   };
@@ -1077,14 +1124,27 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     uint8_t* wk = wl + 2 * FV::kVbuf;
     Tile<KT, VT> ta, tb2;
     int ti = wave;
+    // issue priority 3, 2, 1, 0 by the quarter of this wave's tiles still to
+    // do: it drops after own tile k = ((4 - j) total - 1) / 4, j = 3, 2, 1
     const int my_total = (n_tiles - wave + 3) / 4;
+    const int kq3 = (my_total - 1) >> 2, kq2 = (2 * my_total - 1) >> 2, kq1 = (3 * my_total - 1) >> 2;
+    auto set_prio = [&](int k) {                        // k: own index of the tile about to be staged
+      const int q = (k <= kq1) + (k <= kq2) + (k <= kq3);
+      if (q >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (q == 2) __builtin_amdgcn_s_setprio(2);
+      else if (q == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    };
+    int kown = 1;
     QLoad<T> ql;
+    i2 nrows = {0, 0};                    // LDS entries of this wave's next tile to load
     load_q<KT, T>(p, s, h, tok0, wave, ql);
-    if (ti < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * ti, k0, k1, ta, bad);
-    stage_table();
+    if (ti < n_tiles) load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * ti, k0, k1, ta, bad);
+    stage_rows();
     build_q<KT, T>(p, ql, wave, q_lds);
     __syncthreads();
-    pg.in_lds = tbl_fits;
+    pg.in_lds = grp_fits;
+    if (ti + 4 < n_tiles) nrows = read_rows(pg, ti + 4);
     if (ti < n_tiles) {
       u4 bh[NT], bl[NT];                  // PV operands of the previous tile
       float alpha[NT];
@@ -1093,17 +1153,23 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       // first tile: no PV behind it yet
       stage_tile<KT, VT>(wl, wk, ta, k0 + 32 * ti, k1);
       wave_lds_sync();
-      if (ti + 4 < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+      if (ti + 4 < n_tiles) {
+        load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+        if (ti + 8 < n_tiles) nrows = read_rows(pg, ti + 8);
+      }
       qk_tile<KT, VT, T>(ta, wk, qs, sacc);
       softmax_tile<KT, VT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl);
       wave_lds_sync();
       ti += 4;
       vb = 1;
       while (ti < n_tiles) {
-        set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
+        set_prio(kown++);
         stage_tile<KT, VT>(wl + vb * FV::kVbuf, wk, tb2, k0 + 32 * ti, k1);
         wave_lds_sync();
-        if (ti + 4 < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
+        if (ti + 4 < n_tiles) {
+          load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * (ti + 4), k0, k1, ta, bad);
+          if (ti + 8 < n_tiles) nrows = read_rows(pg, ti + 8);
+        }
         qk_with_pv<KT, VT, T>(tb2, wk, qs, sacc, wl + (vb ^ 1) * FV::kVbuf, bh, bl, o);
         if (softmax_tile<KT, VT, T>(sacc, tb2, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
           rescale<T>(o, alpha);
@@ -1111,10 +1177,13 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
         ti += 4;
         vb ^= 1;
         if (ti >= n_tiles) break;
-        set_prio_remaining((n_tiles - ti + 3) / 4, my_total);
+        set_prio(kown++);
         stage_tile<KT, VT>(wl + vb * FV::kVbuf, wk, ta, k0 + 32 * ti, k1);
         wave_lds_sync();
-        if (ti + 4 < n_tiles) load_tile<KT, VT>(p, pg, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+        if (ti + 4 < n_tiles) {
+          load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * (ti + 4), k0, k1, tb2, bad);
+          if (ti + 8 < n_tiles) nrows = read_rows(pg, ti + 8);
+        }
         qk_with_pv<KT, VT, T>(ta, wk, qs, sacc, wl + (vb ^ 1) * FV::kVbuf, bh, bl, o);
         if (softmax_tile<KT, VT, T>(sacc, ta, k0 + 32 * ti, k1, lim, lim_min, m_run, l_run, alpha, bh, bl))
           rescale<T>(o, alpha);
@@ -1129,14 +1198,16 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     {
       QLoad<T> ql;
       load_q<KT, T>(p, s, h, tok0, wave, ql);
-      stage_table();
+      stage_rows();
       build_q<KT, T>(p, ql, wave, q_lds);
     }
     __syncthreads();
-    pg.in_lds = tbl_fits;
+    pg.in_lds = grp_fits;
+    i2 nrows = (wave < n_tiles) ? read_rows(pg, wave) : i2{0, 0};
     for (int ti = wave; ti < n_tiles; ti += 4) {
       Tile<KT, VT> tt;
-      load_tile<KT, VT>(p, pg, s, h, k0 + 32 * ti, k0, k1, tt, bad);
+      load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * ti, k0, k1, tt, bad);
+      if (ti + 4 < n_tiles) nrows = read_rows(pg, ti + 4);
       stage_tile<KT, VT>(wl, wk, tt, k0 + 32 * ti, k1);
       wave_lds_sync();
       compute_tile<KT, VT, T>(tt, wl, wk, k0 + 32 * ti, k1, lim, lim_min, qs, o, m_run, l_run);
