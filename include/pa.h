@@ -56,8 +56,9 @@ const char *pa_status_string(pa_status s);
 /* Library version, "major.minor.patch".  The minor number changes when a
  * struct of this header grows or calls are added: 0.2 added
  * pa_decode_ext.seq_lens_host, pa_split_plan and pa_read_bandwidth_probe;
- * 0.3 added pa_split_workgroups_per_cu and pa_read_bandwidth_probe_ex and
- * attaches pa_decode_ext.split_events to the split kernel's dispatch. */
+ * 0.3 added pa_split_workgroups_per_cu, pa_read_bandwidth_probe_ex and
+ * pa_decode_scratch and attaches pa_decode_ext.split_events to the split
+ * kernel's dispatch. */
 #define PA_VERSION_STRING "0.3.0"
 const char *pa_version(void);
 
@@ -357,6 +358,28 @@ pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
                     int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
                     float *out, hipStream_t stream, const pa_decode_ext *ext);
 
+/* pa_decode for callers that cannot allocate device memory or pass a
+ * workspace (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same call, with the chunk partials and plan header
+ * in a static device buffer of PA_SCRATCH_BYTES that the library holds on each
+ * device it runs on until the process ends.  It allocates nothing.
+ * ext           required (bt_stride, n_pool_blocks, scale, lse_out, flags,
+ *               split_events, seq_lens_host as for pa_decode); ext->workspace
+ *               must be NULL and ext->workspace_bytes 0.
+ * Every call on a device shares that device's buffer: calls that overlap on
+ * one device (on different streams, or from different threads) race.  The
+ * buffer's error word is cleared at the start of each call, on `stream`;
+ * read it with pa_get_device_error(NULL, NULL, stream, ...).
+ * Errors: as pa_decode; PA_ERR_INVALID without ext or with a workspace in
+ * it; PA_ERR_UNSUPPORTED when pa_decode_workspace_size(n_seq, n_qtok) on the
+ * device exceeds PA_SCRATCH_BYTES (on 256 compute units: up to 2400
+ * sequences of one token, 424 of four, 84 of eight). */
+#define PA_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_scratch(const float *q, const void *k_pool, const void *v_pool,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
+                            float *out, hipStream_t stream, const pa_decode_ext *ext);
+
 /* Bytes of decode workspace for n_seq sequences of n_qtok (1..8) tokens on
  * `device` (reserved up front, as llama.cpp pull 2 does for its split
  * partials in the commit that moved them out of run-time pool allocations).
@@ -393,7 +416,9 @@ pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t devic
 
 /* Reads the error word of a workspace after the work on `stream` finishes
  * (this call waits for the stream) and, if clear != 0, zeroes it (enqueued on
- * `stream`).  Pass NULL to read the pool's own workspace through `pool`. */
+ * `stream`).  Pass NULL to read the pool's own workspace through `pool`;
+ * pool and workspace both NULL read the buffer of pa_decode_scratch on the
+ * current device. */
 pa_status pa_get_device_error(pa_pool *pool, void *workspace, hipStream_t stream,
                               int32_t clear, int32_t *err);
 

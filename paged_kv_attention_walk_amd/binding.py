@@ -29,6 +29,7 @@ HEAD_DIM, N_Q_HEADS, N_KV_HEADS, MAX_QTOK = 256, 24, 4, 8
 OK, ERR_INVALID, ERR_NOMEM, ERR_STALE, ERR_UNSUPPORTED, ERR_HIP, ERR_NOT_FOUND = 0, -1, -2, -3, -4, -5, -6
 DEVERR_TABLE, DEVERR_LENGTH, DEVERR_APPEND = 1, 2, 4
 DECODE_VECTOR_REFERENCE = 1
+SCRATCH_BYTES = 64 << 20      # PA_SCRATCH_BYTES
 POOL_HOST_ONLY = 1
 
 EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "pa_pool_destroy",
@@ -36,7 +37,7 @@ EXPORTS = ("pa_status_string", "pa_version", "pa_row_bytes", "pa_pool_create", "
            "pa_decode",
            "pa_decode_workspace_size", "pa_get_device_error", "pa_debug_gather", "pa_prefill",
            "pa_prefill_workspace_size", "pa_split_plan", "pa_read_bandwidth_probe", "pa_split_workgroups_per_cu",
-           "pa_read_bandwidth_probe_ex")
+           "pa_read_bandwidth_probe_ex", "pa_decode_scratch")
 
 
 def kv_type(k, v=0) -> int:
@@ -99,6 +100,7 @@ def _lib():
             "pa_append_kv_device": (I32, [P, I32, VP, VP, VP, VP, I32, VP, VP]),
             "pa_decode": (I32, [VP, VP, VP, VP, VP, I32, I32, I32, I32, VP, VP, ctypes.POINTER(DecodeExt)]),
             "pa_decode_workspace_size": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
+            "pa_decode_scratch": (I32, [VP, VP, VP, VP, VP, I32, I32, I32, I32, VP, VP, ctypes.POINTER(DecodeExt)]),
             "pa_prefill": (I32, [VP, VP, VP, VP, VP, I32, I32, I32, I32, VP, VP, ctypes.POINTER(DecodeExt)]),
             "pa_prefill_workspace_size": (I32, [I32, I32, I32, ctypes.POINTER(SZ)]),
             "pa_get_device_error": (I32, [P, VP, VP, I32, ctypes.POINTER(I32)]),
@@ -335,6 +337,24 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, n_qtok, kv, page_size, out,
     _check(decode_status(q, k_pool, v_pool, block_table, seq_lens, n, n_qtok, kv, page_size, out, stream, ext),
            "pa_decode")
     return out
+
+
+def decode_scratch_status(q, k_pool, v_pool, block_table, seq_lens, n_seq, n_qtok, kv, page_size, out, stream,
+                          ext: DecodeExt) -> int:
+    """pa_decode_scratch (the workspace is the library's static device
+    buffer; ext is required and carries no workspace); returns the status."""
+    return _lib().pa_decode_scratch(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens),
+                                    int(n_seq), int(n_qtok), kv if isinstance(kv, int) else kv_type(kv),
+                                    int(page_size), _ptr(out), _stream(stream),
+                                    ctypes.byref(ext) if ext is not None else None)
+
+
+def scratch_device_error(stream=None, clear=True) -> int:
+    """The error word of pa_decode_scratch's buffer on the current device."""
+    e = ctypes.c_int32()
+    _check(_lib().pa_get_device_error(None, None, _stream(stream), int(clear), ctypes.byref(e)),
+           "pa_get_device_error")
+    return e.value
 
 
 def device_error(workspace, stream=None, clear=True) -> int:

@@ -59,7 +59,7 @@ def build(verbose: bool = True) -> str:
     # are built once per query-token count (each instantiates every K x V
     # encoding pair for its count)
     cmds = []
-    for name in ("pa_kernels", "pa_append"):
+    for name in ("pa_kernels", "pa_append", "pa_scratch"):
         o = os.path.join(BUILD_DIR, name + ".o")
         cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)

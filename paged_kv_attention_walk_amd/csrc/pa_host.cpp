@@ -672,8 +672,13 @@ pa_status pa_prefill_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t devic
 pa_status pa_get_device_error(pa_pool* pool, void* workspace, hipStream_t stream, int32_t clear, int32_t* err) {
   if (!err) return PA_ERR_INVALID;
   void* ws = workspace;
+  if (!ws && !pool) {                       // pa_decode_scratch's buffer on the current device
+    pa_status st = PA_OK;
+    ws = pa::scratch_buffer(&st);
+    if (st != PA_OK) return st;
+  }
   if (!ws) {
-    if (!pool || !pool->workspace) return PA_ERR_INVALID;
+    if (!pool->workspace) return PA_ERR_INVALID;
     ws = pool->workspace;
   }
   int32_t v = 0;

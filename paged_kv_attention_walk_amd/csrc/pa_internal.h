@@ -244,6 +244,10 @@ hipError_t launch_append_encode(const AppendLaunch& l, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, int32_t unroll,
                              bool to_lds, bool slice, hipStream_t stream);
 
+// The device address of pa_decode_scratch's buffer on the current device
+// (taken once per device), or nullptr with *st set.
+void* scratch_buffer(int32_t* st);
+
 hipError_t launch_gather(const uint8_t* pool, int32_t row_bytes, const int32_t* bt, int32_t bt_stride,
                          int32_t n_pool_blocks, int32_t seq, int32_t seq_len, int32_t page_size,
                          uint8_t* dst, int32_t* err_word, hipStream_t stream);

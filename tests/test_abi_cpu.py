@@ -239,3 +239,15 @@ def test_split_workgroups_per_cu_rejects_bad_arguments():
                          (q4, 1, 2)):
         assert lib.pa_split_workgroups_per_cu(kv, t, flags, ctypes.byref(w)) == pb.ERR_INVALID
     assert w.value == -7
+
+
+def test_decode_scratch_rejects_bad_arguments():
+    # checks before any device call: ext is required and carries no workspace
+    a = 1 << 20
+    ext = pb.make_ext(8, 64, 0.0)
+    assert pb.decode_scratch_status(a, a, a, a, a, 2, 1, pb.kv_type("q4_0"), 16, a, 0, None) == pb.ERR_INVALID
+    with_ws = pb.make_ext(8, 64, 0.0, None, 1 << 30, 1 << 20)
+    assert pb.decode_scratch_status(a, a, a, a, a, 2, 1, pb.kv_type("q4_0"), 16, a, 0, with_ws) == pb.ERR_INVALID
+    for T in (0, pb.MAX_QTOK + 1):
+        assert pb.decode_scratch_status(a, a, a, a, a, 2, T, pb.kv_type("q4_0"), 16, a, 0, ext) == pb.ERR_INVALID
+    assert pb.decode_scratch_status(a, a, a, a, a, -1, 1, pb.kv_type("q4_0"), 16, a, 0, ext) == pb.ERR_INVALID
