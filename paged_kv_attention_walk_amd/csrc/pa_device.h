@@ -338,17 +338,21 @@ __device__ inline void v_dims4(const uint8_t* __restrict__ row, int lane, float 
 
 // ------------------------------------------------------------------ merge
 //
-// Chunks of one (sequence, KV head) are combined by a second kernel, one
-// workgroup per (sequence, KV head, query row).  M = max lse; all -inf gives
-// 0 with lse -inf (llama.cpp pull 2, pd_combine fix: an all-masked row is 0,
-// not 0/0); a NaN partial (corrupt table) gives NaN; otherwise
-// out = sum_c w_c o_c / sum_c w_c with w_c = 2^(lse_c - M) (lse in base 2).
-// Wave w takes chunks c = w, w+4, ... (lane = 4 dims, float4 loads), up to
-// kMergeBatch at once: their log-sum-exps give the batch's base, then the
-// weighted outputs are summed in chunk order (a running base across
-// batches); the 4 waves' states are combined in wave order, so the result is
-// bitwise repeatable.
-constexpr int kMergeBatch = 24;     // chunk outputs per lane in flight
+// Chunks of one (sequence, KV head) are combined by a second kernel.  For a
+// query row: M = max lse; all -inf gives 0 with lse -inf (llama.cpp pull 2,
+// pd_combine fix: an all-masked row is 0, not 0/0); a NaN partial (corrupt
+// table) gives NaN; otherwise out = sum_c w_c o_c / sum_c w_c with
+// w_c = 2^(lse_c - M) (lse in base 2).  A lane holds 4 dims (float4 loads).
+// A row of at most kMergeBatch chunks is merged by one wave: every chunk in
+// flight at once, summed in chunk order.  A longer row takes a whole
+// workgroup: wave w takes chunks c = w, w+4, ..., up to kMergeBatch at once
+// (a running base across batches), and the 4 waves' states are combined in
+// wave order.  Which of the two a row takes depends only on its chunk count,
+// so the result is bitwise the same whatever the grid, and repeatable.  With
+// the host's plan the grid is compact: a sequence of one-wave rows takes
+// 4 rows per workgroup, a sequence of longer rows one row per workgroup, and
+// sequences of one chunk none (hp.mfirst, the prefix of these counts);
+// otherwise one workgroup per row.
 
 struct MergeShared {
   float4 part[4][64];
@@ -485,32 +489,36 @@ __device__ inline int seq_len_of(const DecodeParams& p, int s) {
   return p.hp.on ? p.hp.len[s] : __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
 }
 
-__device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
-  const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
-  const int row_id = blockIdx.x;
-  const int r = row_id % R;
-  const int sh_id = row_id / R;
+// Writes one merged row from the state (m, l, acc) of all its chunks.
+__device__ inline void merge_write(const DecodeParams& p, int s, int h, int r, bool any_nan, float M, float lt,
+                                   float4 t, int lane) {
+  float4 val;
+  float lse2;
+  if (any_nan) {
+    val = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+    lse2 = __builtin_nanf("");
+  } else if (M == kNegInf) {
+    val = make_float4(0.f, 0.f, 0.f, 0.f);
+    lse2 = kNegInf;
+  } else {
+    const float inv = 1.f / lt;
+    val = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    lse2 = M + __log2f(lt);
+  }
+  const int tg = r / 6, g = r % 6;
+  const size_t orow = static_cast<size_t>(s) * p.tok_total + tg;
+  *reinterpret_cast<float4*>(p.out + (orow * kQHeads + h * kGroup + g) * kHeadDim + 4 * lane) = val;
+  if (p.lse_out && lane == 0) p.lse_out[orow * kQHeads + h * kGroup + g] = lse2 * kLn2;
+}
+
+// Merges query row r of (sequence s, KV head h): nc chunks whose partial
+// rows start at plan index `first`.  one_wave: this wave alone (nc <=
+// kMergeBatch); else the 4 waves of the workgroup together.
+__device__ inline void merge_one_row(const DecodeParams& p, int s, int h, int r, int nc, int first, bool one_wave,
+                                     MergeShared& sh) {
   const int tg = r / 6, grp = tg / 8;                    // token, and its group of 8
   const int lr = r - 48 * grp;                           // row within the group's partial rows
-  const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cap = p.bt_stride * p.page_size;
-  int chunk, first;
-  if (p.hp.on) {                                         // the host's plan, in the launch arguments
-    chunk = p.hp.chunk;
-    first = p.hp.first[s];
-  } else if (p.n_seq <= kHdrSeqs) {                      // the split kernel left the plan in the header
-    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.err);
-    chunk = hdr[1];
-    first = hdr[2 + s];
-  } else {
-    const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, p.split_target, p.plan_slots,
-                              -1, s, sh.sum, sh.ints);
-    chunk = pl.chunk;
-    first = pl.prefix;
-  }
-  const int nc = n_chunks_of(seq_len_of(p, s), cap, chunk);
-  if (nc <= 1) return;                                   // written by the split kernel
   const size_t item0 = static_cast<size_t>(grp) * p.part_items + static_cast<size_t>(first) * kKvHeads + h;
   const size_t prows = static_cast<size_t>(p.part_rows);
   // chunk c's row is at item0 + 4c; its address is wave-uniform (scalar
@@ -520,17 +528,18 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   typedef __attribute__((address_space(4))) const float cfloat;
   cfloat* row_l = reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(p.part_lse + item0 * prows + lr));
   const size_t cstride = static_cast<size_t>(kKvHeads) * prows;                 // rows between chunks
+  const int c_first = one_wave ? 0 : wave, c_step = one_wave ? 1 : 4;
   // each batch: all its chunk outputs and log-sum-exps in flight at once,
   // then this wave's base m, weights 2^(x - m) and sums
   float m = kNegInf, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   bool nan = false;
-  for (int c0 = wave; c0 < nc; c0 += 4 * kMergeBatch) {
+  for (int c0 = c_first; c0 < nc; c0 += c_step * kMergeBatch) {
     float4 o[kMergeBatch];
     float x[kMergeBatch];
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      const int c = c0 + 4 * u;
+      const int c = c0 + c_step * u;
       if (c < nc) {
         o[u] = reinterpret_cast<const float4*>(row_o + static_cast<size_t>(c) * cstride * kHeadDim)[lane];
         x[u] = row_l[static_cast<size_t>(c) * cstride];
@@ -557,6 +566,10 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
     }
     m = mb;
   }
+  if (one_wave) {
+    merge_write(p, s, h, r, __ballot(nan) != 0, m, l, acc, lane);
+    return;
+  }
   const bool any_nan = __syncthreads_or(nan);
   sh.part[wave][lane] = acc;
   if (lane == 0) {
@@ -578,24 +591,52 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
       t.x += f * u.x; t.y += f * u.y; t.z += f * u.z; t.w += f * u.w;
       lt += f * sh.ml[w][1];
     }
-    float4 val;
-    float lse2;
-    if (any_nan) {
-      val = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
-      lse2 = __builtin_nanf("");
-    } else if (M == kNegInf) {
-      val = make_float4(0.f, 0.f, 0.f, 0.f);
-      lse2 = kNegInf;
-    } else {
-      const float inv = 1.f / lt;
-      val = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-      lse2 = M + __log2f(lt);
-    }
-    const int g = r % 6;
-    const size_t orow = static_cast<size_t>(s) * p.tok_total + tg;
-    *reinterpret_cast<float4*>(p.out + (orow * kQHeads + h * kGroup + g) * kHeadDim + 4 * lane) = val;
-    if (p.lse_out && lane == 0) p.lse_out[orow * kQHeads + h * kGroup + g] = lse2 * kLn2;
+    merge_write(p, s, h, r, any_nan, M, lt, t, lane);
   }
+}
+
+__device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
+  const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
+  const int rows = kKvHeads * R;                         // query rows of a sequence
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int cap = p.bt_stride * p.page_size;
+  if (p.hp.on) {                                         // the host's plan, in the launch arguments
+    const int j = blockIdx.x;
+    // the last s with mfirst[s] <= j (it owns workgroup j)
+    int s = 0, hi = p.n_seq - 1;
+    while (s < hi) {
+      const int mid = (s + hi + 1) >> 1;
+      if (p.hp.mfirst[mid] <= j) s = mid;
+      else hi = mid - 1;
+    }
+    const int nc = n_chunks_of(p.hp.len[s], cap, p.hp.chunk);
+    const int local = j - p.hp.mfirst[s];
+    const bool one_wave = nc <= kMergeBatch;
+    const int row = one_wave ? 4 * local + wave : local;
+    if (row >= rows) return;
+    merge_one_row(p, s, row / R, row % R, nc, p.hp.first[s], one_wave, sh);
+    return;
+  }
+  const int row_id = blockIdx.x;                         // one workgroup per row
+  const int r = row_id % R;
+  const int sh_id = row_id / R;
+  const int s = sh_id / kKvHeads, h = sh_id % kKvHeads;
+  int chunk, first;
+  if (p.n_seq <= kHdrSeqs) {                             // the split kernel left the plan in the header
+    const int32_t* hdr = reinterpret_cast<const int32_t*>(p.err);
+    chunk = hdr[1];
+    first = hdr[2 + s];
+  } else {
+    const PlanWG pl = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, p.split_target, p.plan_slots,
+                              -1, s, sh.sum, sh.ints);
+    chunk = pl.chunk;
+    first = pl.prefix;
+  }
+  const int nc = n_chunks_of(seq_len_of(p, s), cap, chunk);
+  if (nc <= 1) return;                                   // written by the split kernel
+  const bool one_wave = nc <= kMergeBatch;
+  if (one_wave && wave != 0) return;
+  merge_one_row(p, s, h, r, nc, first, one_wave, sh);
 }
 
 }  // namespace dev

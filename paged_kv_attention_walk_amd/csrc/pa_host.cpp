@@ -144,7 +144,8 @@ static_assert(PA_HOST_PLAN_MAX_SEQS == kHostPlanSeqs, "host plan limit of the AB
 static_assert(sizeof(DecodeParams) <= 4096, "launch arguments stay within 4 KB");
 
 // The device plan (plan_wg / plan_chunk) in host arithmetic.
-void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, int split, int slots, HostPlan& hp) {
+void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, int split, int slots, int tok_total,
+               HostPlan& hp) {
   auto n_chunks = [cap](int L, int chunk) { return (L <= 0 || L > cap) ? 1 : (L + chunk - 1) / chunk; };
   auto granule = [](long long c) {
     c = (c + kChunkGranule - 1) / kChunkGranule * kChunkGranule;
@@ -176,9 +177,12 @@ void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, 
   hp.chunk = static_cast<int32_t>(chunk);
   hp.any_multi = 0;
   hp.first[0] = 0;
+  hp.mfirst[0] = 0;
+  const int rows = kKvHeads * 6 * tok_total;              // query rows of a sequence
   for (int i = 0; i < n_seq; ++i) {
     const int nc = n_chunks(lens[i], hp.chunk);
     hp.first[i + 1] = hp.first[i] + nc;
+    hp.mfirst[i + 1] = hp.mfirst[i] + merge_wgs(nc, rows);
     hp.len[i] = lens[i];
     if (nc > 1) hp.any_multi = 1;
   }
@@ -561,8 +565,6 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   const pa::WorkspaceLayout wl = pa::workspace_layout_for_bytes(ws_bytes, workspace_rows_tokens(n_qtok, prefill));
   const int64_t items = workspace_items(n_seq, n_qtok, prefill, device);
   if (wl.items < items) return PA_ERR_INVALID;
-  if (items > (1ll << 31) - 1 || static_cast<int64_t>(n_seq) * PA_N_Q_HEADS * n_qtok > (1ll << 31) - 1)   // merge grid
-    return PA_ERR_UNSUPPORTED;
 
   pa::DecodeParams prm{};
   prm.q = q;
@@ -591,6 +593,12 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, kernel_tok, engine);
   const int64_t per_group_slots = slots / groups > 0 ? slots / groups : 1;
   const PlanParams pp = plan_params(n_seq, per_group_slots, target);
+  // A dispatch holds at most 2^32 - 1 work items: both grids (split: the
+  // plan's items per token group times the groups; merge: one workgroup per
+  // query row at most) must fit before anything is enqueued.
+  const int64_t max_wgs = ((1ll << 32) - 1) / 256;
+  if (pp.max_items * groups > max_wgs || static_cast<int64_t>(n_seq) * PA_N_Q_HEADS * n_qtok > max_wgs)
+    return PA_ERR_UNSUPPORTED;
   prm.target_items = static_cast<int32_t>(pp.target);
   prm.max_items = static_cast<int32_t>(pp.max_items);
   prm.plan_budget = static_cast<int32_t>(pp.budget);
@@ -609,7 +617,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.hp.on = 0;
   if (lens_host && n_seq <= pa::kHostPlanSeqs)
     pa::host_plan(lens_host, n_seq, bt_stride * page_size, prm.target_items, prm.plan_budget, prm.split_target,
-                  prm.plan_slots, prm.hp);
+                  prm.plan_slots, n_qtok, prm.hp);
   return hip_status(pa::launch_decode(prm, stream, ev0, ev1));
 }
 
@@ -644,7 +652,7 @@ pa_status pa_split_plan(const int32_t* seq_lens_host, int32_t n_seq, int32_t cap
                                     static_cast<int64_t>(n_cu) * kTargetPerCu);
   pa::HostPlan hp;
   pa::host_plan(seq_lens_host, n_seq, cap, static_cast<int>(pp.target), static_cast<int>(pp.budget),
-                static_cast<int>(pp.split), static_cast<int>(pp.slots), hp);
+                static_cast<int>(pp.split), static_cast<int>(pp.slots), 1, hp);
   *chunk = hp.chunk;
   *n_items = pa::kKvHeads * hp.first[n_seq];
   if (first)

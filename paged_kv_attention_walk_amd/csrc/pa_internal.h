@@ -35,6 +35,16 @@ inline int row_bytes_of(int t) {
   }
 }
 
+// Merge of chunk partials: chunk outputs per lane in flight, and the
+// workgroups the compact merge grid gives a sequence of nc chunks and `rows`
+// query rows (a row of up to kMergeBatch chunks is merged by one wave, four
+// rows per workgroup; a longer row by a workgroup; one chunk needs none).
+constexpr int kMergeBatch = 24;
+PA_HD inline int merge_wgs(int nc, int rows) {
+  if (nc <= 1) return 0;
+  return nc > kMergeBatch ? rows : (rows + 3) / 4;
+}
+
 // The chunk plan computed on the host from a host copy of seq_lens (up to
 // kHostPlanSeqs sequences), carried in the launch arguments: the kernels then
 // locate their work item without reading seq_lens.  Same integer arithmetic
@@ -46,6 +56,7 @@ struct HostPlan {
   int32_t any_multi;                // some sequence has more than one chunk (the merge has work)
   int32_t first[kHostPlanSeqs + 1]; // plan index of sequence s's first chunk; first[n_seq] = all pairs
   int32_t len[kHostPlanSeqs];       // seq_lens
+  int32_t mfirst[kHostPlanSeqs + 1];// first merge workgroup of sequence s; mfirst[n_seq] = the merge grid
 };
 
 // Everything one decode launch needs.  Device pointers unless noted.
@@ -124,8 +135,10 @@ inline int32_t grid_items(const DecodeParams& p) {
 }
 
 // Fills `hp` from host seq_lens (n_seq <= kHostPlanSeqs) with the device
-// plan's arithmetic for the given target and budget.
-void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, int split, int slots, HostPlan& hp);
+// plan's arithmetic for the given target and budget; the merge grid is laid
+// out for tok_total query tokens per sequence.
+void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, int split, int slots, int tok_total,
+               HostPlan& hp);
 
 // Resident workgroups per compute unit of the split kernel a call selects
 // (from the runtime's occupancy query; at least 1).

@@ -143,7 +143,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
 }
 
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(p.n_seq) * kKvHeads * 6 * static_cast<unsigned>(p.tok_total)), block(kThreads);
+  // the host's plan: the compact grid; else one workgroup per query row
+  const unsigned wgs = p.hp.on ? static_cast<unsigned>(p.hp.mfirst[p.n_seq])
+                               : static_cast<unsigned>(p.n_seq) * kKvHeads * 6 * static_cast<unsigned>(p.tok_total);
+  if (wgs == 0) return hipSuccess;
+  const dim3 grid(wgs), block(kThreads);
   hipLaunchKernelGGL(merge_kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }

@@ -566,11 +566,14 @@ __device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT, VT>& t
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       d[i] = half_bits(*reinterpret_cast<const uint16_t*>(kr + (16 * hf + m0 + i) * F::kRow + 18 * b));
-    // zero for keys that are not visible (a select on live: t stays in registers)
-    const bool lv = hf ? t.live[1] : t.live[0];
+    // zero for keys that are not visible (a select on live: t stays in
+    // registers); a tile inside the chunk with both halves live skips it
+    if (!(t.live[0] && t.live[1] && tb + 32 <= k1)) {
+      const bool lv = hf ? t.live[1] : t.live[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (!lv || tb + 16 * hf + m0 + i >= k1) d[i] = 0.f;
+      for (int i = 0; i < 4; ++i)
+        if (!lv || tb + 16 * hf + m0 + i >= k1) d[i] = 0.f;
+    }
     *reinterpret_cast<f4*>(wk + F::kKScale + ((hf * 8 + b) * 16 + m0) * 4) = d;
   }
 }
@@ -991,11 +994,12 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int NT = C::NT;
   // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
   constexpr int kWaveBytes = (kDoubleBuffer<KT, VT, T> ? 2 : 1) * FV::kVbuf + F::kKarea;
-  // the combine, one B tile of rows at a time: [4 waves][kRT rows][256 + 1]
-  // floats (the pad puts the rows a column group writes in different banks;
-  // only a tile's live rows are kept, so one or two tokens leave room for a
-  // second workgroup per compute unit)
-  constexpr int kRedStride = kHeadDim + 1;
+  // the combine, one B tile of rows at a time: [4 waves][kRT rows][256 + 4]
+  // floats (the pad puts the rows a column group writes in different banks
+  // and keeps them 16-byte aligned for vector writes; only a tile's live rows
+  // are kept, so one or two tokens leave room for a second workgroup per
+  // compute unit)
+  constexpr int kRedStride = kHeadDim + 4;
   constexpr int kRT = (R < 16) ? R : 16;
   constexpr int kRed = 4 * kRT * kRedStride * 4;
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
@@ -1218,7 +1222,7 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[0][mt][i] += __shfl_xor(o[0][mt][i], 8, 64);
+      for (int i = 0; i < 4; ++i) o[0][mt][i] += lane_xor8(o[0][mt][i]);
   }
 
   __builtin_amdgcn_s_setprio(0);
@@ -1266,8 +1270,14 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
       float* dst = red + (wave * kRT + n) * kRedStride;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[out_dim<VT>(mt, g, i)] = o[nt][mt][i] * a;
+        const f4 v = o[nt][mt] * a;
+        if constexpr (VT == kQ4_0) {    // elements 0, 2 and 1, 3 hold adjacent dims
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          *reinterpret_cast<f2*>(dst + out_dim<VT>(mt, g, 0)) = f2{v[0], v[2]};
+          *reinterpret_cast<f2*>(dst + out_dim<VT>(mt, g, 1)) = f2{v[1], v[3]};
+        } else {                        // elements 0..3 hold dims 16 mt + 4 g ..
+          *reinterpret_cast<f4*>(dst + out_dim<VT>(mt, g, 0)) = v;
+        }
       }
     }
     __syncthreads();

@@ -185,6 +185,15 @@ def test_prefill_host_checks_and_workspace():
             assert pb.prefill_status(a, a, a, a, a, n_seq, T, kvq, 16, a, 0, ok) != pb.ERR_INVALID, (n_seq, T)
             small = pb.make_ext(8, 64, 0.0, None, 1 << 30, n - 48 * 257 * 4)
             assert pb.prefill_status(a, a, a, a, a, n_seq, T, kvq, 16, a, 0, small) == pb.ERR_INVALID, (n_seq, T)
+    # a dispatch holds at most 2^32 - 1 work items (16777215 workgroups of
+    # 256): 10 sequences of 65536 tokens fit the merge grid (15.7M query
+    # rows), 11 do not (17.3M) and are refused before anything is enqueued
+    for n_seq, want_unsupported in ((10, False), (11, True)):
+        n = pb.prefill_workspace_size(n_seq, 65536, 0)
+        ext = pb.make_ext(4096, 64, 0.0, None, 1 << 30, n)
+        got = pb.prefill_status(a, a, a, a, a, n_seq, 65536, kvq, 16, a, 0, ext)
+        assert (got == pb.ERR_UNSUPPORTED) == want_unsupported, (n_seq, got)
+        assert got != pb.ERR_INVALID
 
 
 def test_workspace_size_is_accepted_and_needed():
