@@ -351,8 +351,19 @@ pa_status pa_split_workgroups_per_cu(int32_t kv_type, int32_t n_qtok, uint32_t f
  * bitwise-equal outputs), and a merge kernel for sequences split in several
  * chunks.  Errors: PA_ERR_INVALID (null pointers, n_qtok outside 1..8,
  * misaligned K/V (16 bytes) or q/out (16 bytes), workspace too small,
- * page_size or kv_type different from the pool's), PA_ERR_UNSUPPORTED,
- * PA_ERR_NOT_FOUND (ext NULL and k_pool not a pool), PA_ERR_HIP. */
+ * page_size or kv_type different from the pool's), PA_ERR_UNSUPPORTED (a
+ * split or merge grid past 2^32 - 1 work items), PA_ERR_NOT_FOUND (ext NULL
+ * and k_pool not a pool), PA_ERR_HIP.
+ * Numeric range of the matrix-core path (the default): products take f16
+ * operands (bf16 for BF16 K or V), split into hi + lo parts.  Two limits
+ * follow.  (1) Each dequantised Q8_0 / Q4_0 V value |code x d| must be at
+ * most 65504, the f16 range: Q8_0 scales up to 515 and Q4_0 scales up to
+ * 8188 always are, and rows encoded from data within the f16 range (scale
+ * max|x| / 127 or / 8) never exceed it.  (2) For F16 / Q8_0 / Q4_0 K, each
+ * |q x scale x log2(e)| must be at most 65504.  Past either limit the query
+ * rows that see such a value come out non-finite; other rows are
+ * unaffected.  The vector path (PA_DECODE_VECTOR_REFERENCE, fp32 throughout)
+ * has neither limit. */
 pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
                     const int32_t *block_table, const int32_t *seq_lens,
                     int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,

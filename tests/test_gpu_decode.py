@@ -192,3 +192,67 @@ def test_mixed_paged_equals_contiguous_bitwise(kv, P):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     assert np.array_equal(al.view(np.uint32), bl.view(np.uint32))
     parity(a, _oracle(w)[0], what=f"mixed pc K={k} V={v} P={P}")
+
+
+def _plant_v_block(w, s, pos, d, code):
+    """Sets V block 0 of sequence s's row `pos` (every KV head) to scale d and
+    all 32 codes `code` (stored code for Q8_0; code + 8 nibbles for Q4_0)."""
+    P = w["page_size"]
+    page = int(w["block_table"][s][pos // P])
+    v = w["v_pool"]
+    dbytes = np.float16(d).tobytes()
+    for h in range(4):
+        row = v[page, h, pos % P]
+        row[0:2] = np.frombuffer(dbytes, np.uint8)
+        if w["v_kind"] == "q8_0":
+            row[2:34] = np.uint8(code & 0xFF)
+        else:
+            nib = code + 8
+            row[2:18] = np.uint8(nib | (nib << 4))
+
+
+@pytest.mark.parametrize("v_kind,d_ok,d_over,code", [("q8_0", 515.5, 600.0, 127), ("q4_0", 8188.0, 9000.0, -8)])
+def test_v_values_at_the_f16_range_limit(v_kind, d_ok, d_over, code):
+    # The matrix-core path forms a quantised V value code x d as an f16 pair:
+    # exact up to |code x d| = 65504, the f16 range (rows encoded from data in
+    # the f16 range never exceed it).  At the limit the output matches the
+    # oracle; past it the rows that see the value are non-finite (documented
+    # in pa.h), the other sequence is unaffected, and the fp32 vector path
+    # still matches the oracle.
+    for d, finite in ((d_ok, True), (d_over, False)):
+        w = synth.make_workload(f"vlimit_{v_kind}", [40, 70], 1, "q8_0", v_kind, 16, table="shuffled", seed=31)
+        _plant_v_block(w, 0, 5, d, code)
+        ref, _ = _oracle(w)
+        log(f"[case] V {v_kind} value {code} x {d} = {abs(code) * d:.0f} (finite expected: {finite})")
+        out, _, err = run(w)
+        assert err == 0
+        if finite:
+            parity(out, ref, what=f"V {v_kind} at the f16 limit")
+        else:
+            assert not np.isfinite(out[0]).all()
+            parity(out[1:], ref[1:], what=f"V {v_kind} past the limit, other sequence")
+        out_v, _, err = run(w, engine="valu")
+        assert err == 0
+        parity(out_v, ref, what=f"V {v_kind} value {abs(code) * d:.0f}, fp32 vector path")
+
+
+@pytest.mark.parametrize("qv,finite", [(40000.0, True), (50000.0, False)])
+def test_q_at_the_f16_range_limit(qv, finite):
+    # q x scale x log2(e) is split into f16 hi + lo for F16 / Q8_0 / Q4_0 K:
+    # within the f16 range the result matches the oracle, past it the query
+    # row's outputs are non-finite; the fp32 vector path matches either way
+    w = synth.make_workload("qlimit", [40, 33], 1, "q8_0", "q8_0", 16, table="shuffled", seed=32,
+                            scale=1.0, value_scale=1e-3)
+    w["q"][0, 0, 7, 3] = qv                                 # sequence 0, query head 7
+    ref, _ = _oracle(w)
+    log(f"[case] q element {qv} x log2(e) = {qv * 1.4427:.0f} (finite expected: {finite})")
+    out, _, err = run(w)
+    assert err == 0
+    if finite:
+        parity(out, ref, what="q at the f16 limit")
+    else:
+        assert not np.isfinite(out[0, 0, 7]).all()
+        parity(out[1:], ref[1:], what="q past the limit, other sequence")
+    out_v, _, err = run(w, engine="valu")
+    assert err == 0
+    parity(out_v, ref, what=f"q {qv}, fp32 vector path")
