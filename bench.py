@@ -41,11 +41,11 @@ def parse():
                          "(encoded to BF16 into its page) followed by the decode; prefill: one --ctx-position "
                          "sequence, Q8_0 K and Q4_0 V, whose last --qtok positions are the new tokens (pa_prefill)")
     ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp / prefill")
-    ap.add_argument("--append", default="device", choices=["device", "host"],
-                    help="serving: the per-step append of one row per stream; device: pa_append_kv_device (float32 "
-                         "rows already on the GPU, encoded into the pool's BF16 on the way in); host: pa_append_kv "
-                         "(rows already BF16-encoded in host memory, one packed upload through pinned staging and a "
-                         "scatter kernel)")
+    ap.add_argument("--append", default="host", choices=["device", "host"],
+                    help="serving: the per-step append of one row per stream; host: pa_append_kv (rows already "
+                         "BF16-encoded in host memory, one packed upload through pinned staging and a scatter "
+                         "kernel); device: pa_append_kv_device (float32 rows already on the GPU, encoded into the "
+                         "pool's BF16 on the way in)")
     ap.add_argument("--ctx", type=int, default=16384, help="context for --workload prefill")
     ap.add_argument("--nseq", type=int, default=8, help="sequences of 4096 positions for --workload uniform")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
@@ -261,7 +261,7 @@ def main():
     elif args.workload == "mtp":
         w = synth.config4(ctx=131072, n_qtok=args.qtok)
     elif args.workload == "serving":
-        w = synth.config5()
+        w = synth.config5_rolling()
     elif args.workload == "prefill":
         w = synth.prefill_workload(ctx=args.ctx, n_qtok=args.qtok)
     else:
@@ -269,11 +269,21 @@ def main():
     print(f"[bench] workload {w['name']} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     n_seq, T, P = len(w["seq_lens"]), w["n_qtok"], w["page_size"]
     kv = pb.kv_type(w["k_kind"], w["v_kind"])
-    kv_bytes = w.kv_bytes
+    # serving: `roll` consecutive decode steps; step k appends one row per
+    # stream at position L0 + k and decodes at L0 + k + 1 (pages fill up and
+    # new ones start); the timed steps cycle through them
+    roll = int(w.get("steps", 1))
+    if roll > 1:
+        base = w["seq_lens"].astype(np.int64)
+        lens_steps = [(base + k + 1).astype(np.int32) for k in range(roll)]
+    else:
+        lens_steps = [w["seq_lens"]]
+    row_kv = synth_row_bytes(w["k_kind"]) + synth_row_bytes(w["v_kind"])
+    kv_bytes = float(np.mean([int(np.sum(x)) for x in lens_steps])) * 4 * row_kv
     pool_bytes = w["k_pool"].nbytes + w["v_pool"].nbytes
     reps = args.replicas or max(1, min(16, int(np.ceil(2 * 2 * 256e6 / pool_bytes))))
     dq = torch.from_numpy(w["q"]).cuda()
-    dlens = torch.from_numpy(w["seq_lens"]).cuda()
+    dlens_steps = [torch.from_numpy(x).cuda() for x in lens_steps]
     k0 = torch.from_numpy(w["k_pool"]).cuda()
     v0 = torch.from_numpy(w["v_pool"]).cuda()
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
@@ -327,44 +337,50 @@ def main():
     lib = pb.lib()
     stream = torch.cuda.current_stream().cuda_stream
 
-    # serving: every step first appends one new float32 K/V row per stream at
-    # its last position (the row the decode then attends to), encoded on the
-    # device into the pool's encoding
+    # serving: every step first appends one new K/V row per stream at the
+    # position the step adds, then decodes.  Default: pa_append_kv, the rows
+    # already BF16-encoded in host memory, one packed upload through pinned
+    # staging and a scatter kernel; --append device: pa_append_kv_device,
+    # float32 rows already on the GPU encoded into the pool on the way in
     serving = args.workload == "serving"
     append = None
     if serving:
-        last = w["seq_lens"].astype(np.int64) - 1
-        dst_block = torch.from_numpy(w["block_table"][np.arange(n_seq), last // P].astype(np.int32)).cuda()
-        dst_slot = torch.from_numpy((last % P).astype(np.int32)).cuda()
-        xk = torch.from_numpy(synth.normal((n_seq, 4, 256), seed=505)).cuda()
-        xv = torch.from_numpy(synth.normal((n_seq, 4, 256), seed=506)).cuda()
+        nk, nv = synth.normal((n_seq, 4, 256), seed=505), synth.normal((n_seq, 4, 256), seed=506)
+        h_k = np.ascontiguousarray(synth.encode(nk, w["k_kind"]))
+        h_v = np.ascontiguousarray(synth.encode(nv, w["v_kind"]))
+        xk, xv = torch.from_numpy(nk).cuda(), torch.from_numpy(nv).cuda()
+        dst = []                          # per step: (host block, host slot, device block, device slot)
+        for k in range(roll):
+            pos = lens_steps[k].astype(np.int64) - 1
+            hb = w["block_table"][np.arange(n_seq), pos // P].astype(np.int32)
+            hs = (pos % P).astype(np.int32)
+            dst.append((hb, hs, torch.from_numpy(hb).cuda(), torch.from_numpy(hs).cuda()))
         append_pools = [pb.Pool(nblocks, P, kv, k_pool=kp, v_pool=vp, max_seqs=1, max_blocks_per_seq=bt_stride)
                         for kp, vp in pools]
         for ap_pool in append_pools:      # every page of the pool is in use (allocated through pa_alloc_blocks)
             ap_pool.alloc(nblocks)
-        append = {"rows": n_seq, "src": "f32" if args.append == "device" else "bf16 rows in host memory",
+        append = {"rows": n_seq, "steps_rolled": roll,
+                  "src": "f32 on the device" if args.append == "device" else "bf16 rows in host memory",
                   "entry": "pa_append_kv_device" if args.append == "device" else "pa_append_kv",
-                  "keep": (dst_block, dst_slot, xk, xv)}
-        # host route: the same rows, encoded to the pool's BF16 on the host
-        h_block = w["block_table"][np.arange(n_seq), last // P].astype(np.int32)
-        h_slot = (last % P).astype(np.int32)
-        h_k = synth.encode(xk.cpu().numpy(), w["k_kind"])
-        h_v = synth.encode(xv.cpu().numpy(), w["v_kind"])
+                  "keep": (xk, xv, dst)}
 
-    def make_call(kp, vp, bt, nb, pool=None, plan=args.plan):
-        """A step with every pointer and the ext struct prepared up front, so
-        that the timed loop is one ctypes call per step (two with an append)."""
+    def make_call(kp, vp, bt, nb, pool=None, plan=args.plan, k=0):
+        """Step k of the length cycle with every pointer and the ext struct
+        prepared up front, so that the timed loop is one ctypes call per step
+        (two with an append)."""
         ext = pb.make_ext(bt_stride, nb, w["scale"], None, ws, ws.numel() * 4,
-                          seq_lens_host=w["seq_lens"] if plan == "host" else None)
+                          seq_lens_host=lens_steps[k] if plan == "host" else None)
         ext_ref = ctypes.byref(ext)
         a = (dq.data_ptr(), kp.data_ptr(), vp.data_ptr(), bt.data_ptr() if bt is not None else None,
-             dlens.data_ptr(), n_seq, T, kv, P, out.data_ptr(), stream)
+             dlens_steps[k].data_ptr(), n_seq, T, kv, P, out.data_ptr(), stream)
         ap = None
-        if pool is not None and args.append == "device":
-            ap = (pool._h, n_seq, dst_block.data_ptr(), dst_slot.data_ptr(), xk.data_ptr(), xv.data_ptr(), pb.F32,
-                  ws.data_ptr(), stream)
-        elif pool is not None:
-            ap = (pool._h, n_seq, h_block.ctypes.data, h_slot.ctypes.data, h_k.ctypes.data, h_v.ctypes.data, stream)
+        if pool is not None:
+            hb, hs, db, ds = dst[k]
+            if args.append == "device":
+                ap = (pool._h, n_seq, db.data_ptr(), ds.data_ptr(), xk.data_ptr(), xv.data_ptr(), pb.F32,
+                      ws.data_ptr(), stream)
+            else:
+                ap = (pool._h, n_seq, hb.ctypes.data, hs.ctypes.data, h_k.ctypes.data, h_v.ctypes.data, stream)
         append_fn = lib.pa_append_kv_device if args.append == "device" else lib.pa_append_kv
 
         entry = lib.pa_prefill if prefill else lib.pa_decode
@@ -381,20 +397,25 @@ def main():
         f.keep = (ext, kp, vp, bt, pool)
         return f
 
-    def paged_call(r, with_append=True, plan=args.plan):
-        return make_call(pools[r][0], pools[r][1], bts[r], nblocks,
-                         append_pools[r] if (serving and with_append) else None, plan)
+    def cycle(make, rs):
+        """Calls over replicas rs and the length steps: consecutive calls
+        rotate the replicas, each replica walks the steps in order."""
+        return [make(rs[i % len(rs)], (i // len(rs)) % roll) for i in range(len(rs) * roll)]
+
+    def paged_calls(rs, with_append=True, plan=args.plan):
+        return cycle(lambda r, k: make_call(pools[r][0], pools[r][1], bts[r], nblocks,
+                                            append_pools[r] if (serving and with_append) else None, plan, k), rs)
 
     other = "device" if args.plan == "host" else "host"
-    o_ms, o_k, _ = timed([paged_call(r, plan=other) for r in range(reps)], args.steps, args.warmup)
+    o_ms, o_k, _ = timed(paged_calls(list(range(reps)), plan=other), args.steps, args.warmup)
     res_other = out.clone()
-    cold_ms, cold_k, cold_k_med = timed([paged_call(r) for r in range(reps)], args.steps, args.warmup)
+    cold_ms, cold_k, cold_k_med = timed(paged_calls(list(range(reps))), args.steps, args.warmup)
     other_plan = {"plan": other, "ms_per_step": round(o_ms, 4), "split_kernel_ms": round(o_k, 4),
                   "bitwise_equal": bool(torch.equal(out.view(torch.int32), res_other.view(torch.int32)))}
-    hot_ms, hot_k, _ = timed([paged_call(0)], args.steps, args.warmup)
+    hot_ms, hot_k, _ = timed(paged_calls([0]), args.steps, args.warmup)
     decode_only_ms = None
     if serving:
-        decode_only_ms, _, _ = timed([paged_call(r, False) for r in range(reps)], args.steps, args.warmup)
+        decode_only_ms, _, _ = timed(paged_calls(list(range(reps)), False), args.steps, args.warmup)
         append["ms_per_step_decode_only"] = round(decode_only_ms, 4)
         append["append_ms_est"] = round(cold_ms - decode_only_ms, 4)
     err = pb.device_error(ws)
@@ -405,11 +426,13 @@ def main():
     contig = None
     if not args.no_contiguous:
         max_len = bt_stride * P
-        # with appends, the pools now hold the appended rows: copy those
+        # with appends, the pools now hold the appended rows (replica 0 has
+        # walked every step of the cycle): copy those, up to the last step's
+        # lengths
         hk = k0.cpu().numpy() if serving else w["k_pool"]
         hv = v0.cpu().numpy() if serving else w["v_pool"]
-        kc = synth.contiguous_from_table(hk, w["block_table"], w["seq_lens"], max_len)
-        vc = synth.contiguous_from_table(hv, w["block_table"], w["seq_lens"], max_len)
+        kc = synth.contiguous_from_table(hk, w["block_table"], lens_steps[-1], max_len)
+        vc = synth.contiguous_from_table(hv, w["block_table"], lens_steps[-1], max_len)
         del hk, hv
         # as many replicas as the paged pools: the step reads the same live
         # rows either way, so the same rotation keeps both cold
@@ -419,11 +442,12 @@ def main():
         del kc, vc
         cpools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(creps - 1)]
 
-        def contig_call(r):
-            return make_call(cpools[r][0], cpools[r][1], None, 0)
-        c_ms, c_k, _ = timed([contig_call(r) for r in range(creps)], args.steps, args.warmup)
+        def contig_calls(rs):
+            return cycle(lambda r, k: make_call(cpools[r][0], cpools[r][1], None, 0, None, args.plan, k), rs)
+        c_ms, c_k, _ = timed(contig_calls(list(range(creps))), args.steps, args.warmup)
+        # the last step of both runs used the same lengths when the step count is a multiple of the cycle
         same = bool(torch.equal(out.view(torch.int32), res_paged.view(torch.int32)))
-        ch_ms, ch_k, _ = timed([contig_call(0)], args.steps, args.warmup)
+        ch_ms, ch_k, _ = timed(contig_calls([0]), args.steps, args.warmup)
         contig = {"ms_per_step": round(c_ms, 4), "split_kernel_ms": round(c_k, 4), "replicas": creps,
                   "bitwise_equal_to_paged": same,
                   "hot": {"ms_per_step": round(ch_ms, 4), "split_kernel_ms": round(ch_k, 4)}}
@@ -431,8 +455,9 @@ def main():
 
     gbps = kv_bytes / (cold_ms * 1e-3) / 1e9
     achieved = kv_bytes / (cold_k * 1e-3) / 1e9
-    # algorithmic flops: QK^T and PV, 2 x 2 x 256 per (query row, visible key)
-    vis = sum(max(0, min(int(L), int(L) - T + t + 1)) for L in w["seq_lens"] for t in range(T))
+    # algorithmic flops: QK^T and PV, 2 x 2 x 256 per (query row, visible
+    # key), the mean over the steps of the cycle like kv_bytes
+    vis = np.mean([sum(max(0, min(int(L), int(L) - T + t + 1)) for L in ls for t in range(T)) for ls in lens_steps])
     flops = 4.0 * 256 * 24 * vis
     roofline = {"kernel": SPLIT_KERNEL, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(w["name"]),
@@ -464,9 +489,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w["name"], "n_seq": n_seq,
+        "config": {"workload": w["name"] + (f"_{roll}steps" if roll > 1 else ""), "n_seq": n_seq,
                    "seq_lens": ("131072+7x8192" if args.workload.startswith("ragged") else
-                                "U{512..8192}+1" if serving else ",".join(str(int(x)) for x in w["seq_lens"])),
+                                f"U{{512..8192}}+1..{roll} (each step appends one row per stream; {roll} steps)"
+                                if serving else ",".join(str(int(x)) for x in w["seq_lens"])),
                    "entry": "pa_prefill" if prefill else "pa_decode",
                    "n_qtok": T, "kv": w["k_kind"] if w["k_kind"] == w["v_kind"] else f"K {w['k_kind']} V {w['v_kind']}",
                    "page_size": P, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "kv_bytes": int(kv_bytes)},
@@ -489,7 +515,9 @@ def main():
         "host": host_info(),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        w0 = synth.Workload(w)            # the first step's lengths (the same as w's without an append cycle)
+        w0["seq_lens"] = lens_steps[0]
+        line["cpu_baseline"] = cpu_baseline(w0, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -273,3 +273,18 @@ def config5(seed=5, n_seq=128):
     lens = config5_lengths(seed, n_seq) + 1
     return make_workload("bf16_128streams_512-8192_p64_shuffled", lens, 1, "bf16", "bf16", 64,
                          table="shuffled", seed=seed)
+
+
+def config5_rolling(seed=5, n_seq=128, steps=16):
+    """The many-stream serving step over `steps` consecutive decode steps:
+    stream s holds L0_s ~ U{512..8192} rows before the first step; step k
+    appends one row at position L0_s + k and decodes at length L0_s + k + 1,
+    so pages fill up and new pages start within the window.  The table and
+    pool cover L0_s + steps positions (the rows past L0_s are written by the
+    appends); seq_lens holds L0_s, the lengths before the first step."""
+    base = config5_lengths(seed, n_seq)
+    w = make_workload("bf16_128streams_512-8192_p64_shuffled", base + steps, 1, "bf16", "bf16", 64,
+                      table="shuffled", seed=seed)
+    w["seq_lens"] = base.copy()
+    w["steps"] = steps
+    return w

@@ -1,8 +1,9 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (pa_decode with an explicit workspace, the same plan), on the
 whole output: uniform 8 x 4096 Q4_0; the ragged 131072 + 7 x 8192 Q4_0 step,
-the single-sequence Q8_0 verify contexts and the 128-stream BF16 serving step
-(device append, then decode), whose oracle output is assembled one
+the single-sequence Q8_0 verify contexts and the 128-stream BF16 serving
+steps (16 steps of pa_append_kv then decode; one device append then decode),
+whose oracle output is assembled one
 (sequence, KV head) block at a time to bound host memory.  Each block is also
 held to the bar against its own RMS (stricter for long sequences, whose
 outputs are small).  Also batches of more than 64 / 256 / 1022 sequences,
@@ -22,12 +23,12 @@ pytestmark = pytest.mark.gpu
 
 def _oracle_head(w, s, h, patch=None):
     """Oracle output [T][6][256] of sequence s, KV head h (its 6 query heads).
-    ``patch`` = (position, K row bytes, V row bytes) replaces one stored row."""
+    ``patch``: a list of (position, K row bytes, V row bytes), each replacing
+    one stored row."""
     L = int(w["seq_lens"][s])
     kb = pool_model.gather_rows(w["k_pool"][:, h:h + 1], w["block_table"][s], L)
     vb = pool_model.gather_rows(w["v_pool"][:, h:h + 1], w["block_table"][s], L)
-    if patch is not None:
-        pos, krow, vrow = patch
+    for pos, krow, vrow in (patch or []):
         kb[0, pos] = krow
         vb[0, pos] = vrow
     k = quant.decode(kb, w["k_kind"])
@@ -95,9 +96,52 @@ def test_mtp_q8_0_whole(ctx, T):
     _whole(out, w, f"mtp ctx={ctx} T={T}")
 
 
-def test_serving_128_streams_append_then_decode_whole():
-    # the benchmark's serving step: one float32 row per stream appended on the
-    # device at its last position, then the decode
+def test_serving_128_streams_16_steps_whole():
+    # the benchmark's serving cycle: 16 consecutive steps, each appending one
+    # BF16 row per stream at its next position with pa_append_kv (one packed
+    # upload and a scatter kernel), then decoding at the new lengths, so that
+    # pages fill up and new pages start inside the window.  Each step's rows
+    # differ.  Steps 0 and 15 are checked on the whole output, the others on
+    # eight sequences.
+    w = synth.config5_rolling()
+    n_seq, P, roll = len(w["seq_lens"]), w["page_size"], w["steps"]
+    base = w["seq_lens"].astype(np.int64)
+    kp, vp = dev(w["k_pool"]), dev(w["v_pool"])
+    nb = w["k_pool"].shape[0]
+    pool = pb.Pool(nb, P, "bf16", k_pool=kp, v_pool=vp, max_seqs=1, max_blocks_per_seq=w["block_table"].shape[1])
+    pool.alloc(nb)
+    rows = []                               # per step: (positions, K rows, V rows)
+    few = np.random.default_rng(15).choice(n_seq, size=8, replace=False)
+    for k in range(roll):
+        pos = base + k
+        blocks = w["block_table"][np.arange(n_seq), pos // P].astype(np.int32)
+        slots = (pos % P).astype(np.int32)
+        krows = synth.encode(synth.normal((n_seq, 4, 256), seed=700 + k), "bf16")
+        vrows = synth.encode(synth.normal((n_seq, 4, 256), seed=800 + k), "bf16")
+        rows.append((pos, krows, vrows))
+        log(f"[case] 128-stream BF16 serving, step {k}: pa_append_kv at L0+{k}, decode at L0+{k + 1}")
+        assert pool.append_kv(blocks, slots, krows, vrows) == pb.OK
+        wk = synth.Workload(w)
+        wk["seq_lens"] = (base + k + 1).astype(np.int32)
+        out, _, err = _bench_route(wk, dk=kp, dv=vp) if k in (0, roll - 1) else run(wk, dk=kp, dv=vp, host_plan=True)
+        assert err == 0
+        assert pool.device_error() == 0
+
+        def patches(s, h, k=k):
+            return [(int(rows[j][0][s]), rows[j][1][s][h], rows[j][2][s][h]) for j in range(k + 1)]
+        if k in (0, roll - 1):
+            _whole(out, wk, f"serving step {k}", patches=patches)
+        else:
+            for s in few:
+                ref = np.stack([_oracle_head(wk, s, h, patch=patches(s, h)) for h in range(4)], axis=1)
+                parity(out[s][None], ref.reshape(1, 1, 24, 256),
+                       what=f"serving step {k} seq {s}")
+    pool.destroy()
+
+
+def test_serving_128_streams_device_append_then_decode_whole():
+    # the other append route: float32 rows already on the device, encoded to
+    # BF16 by pa_append_kv_device on the way into the pages
     w = synth.config5()
     n_seq, P = len(w["seq_lens"]), w["page_size"]
     log("[case] 128-stream BF16 serving step (device append + decode), whole output")
@@ -116,7 +160,7 @@ def test_serving_128_streams_append_then_decode_whole():
     assert err == 0
     # the oracle's rows: the generated pages, with the appended row encoded by the oracle encoder
     _whole(out, w, "serving",
-           patches=lambda s, h: (int(last[s]), encode.encode(xk[s][h], "bf16"), encode.encode(xv[s][h], "bf16")))
+           patches=lambda s, h: [(int(last[s]), encode.encode(xk[s][h], "bf16"), encode.encode(xv[s][h], "bf16"))])
     pool.destroy()
 
 
