@@ -278,7 +278,8 @@ struct Half {
 // when its block-table entry lies outside the pool; entries past the chunk
 // end are 0 (in bounds, masked).  A tile reads both of its entries with one
 // 8-byte LDS read, issued a tile ahead.  Otherwise (contiguous storage, the
-// chunk's first tile, or chunks of more than kGrpCap groups) the row comes
+// chunk's first tile, or chunks of more groups than the LDS list holds:
+// kGrpCap, half that for three or more tokens) the row comes
 // from the block table through the constant address space (scalar loads).
 // Either way the values are wave-uniform and never wait behind tile loads.
 typedef __attribute__((address_space(3))) const int lds_int;
@@ -985,8 +986,15 @@ __device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wa
 template <int KT, int VT, int T>
 constexpr bool kDoubleBuffer = (KT == kQ4_0 && VT == kQ4_0 && T == 1);
 
+// Workgroups per compute unit the kernel is compiled for: two (8 waves per
+// CU, at most 256 registers per lane) up to two tokens, and up to four
+// tokens with quantized V, whose per-wave LDS buffers are small enough for
+// two workgroups (with 16-bit V the buffers take one workgroup's share).
 template <int KT, int VT, int T>
-__global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(DecodeParams p) {
+constexpr int kMinWgs = (T <= 2 || (T <= 4 && Fmt<VT>::kQuant)) ? 2 : 1;
+
+template <int KT, int VT, int T>
+__global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(DecodeParams p) {
   using F = Fmt<KT>;
   using FV = Fmt<VT>;
   using C = Cols<T>;
@@ -994,19 +1002,24 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   constexpr int NT = C::NT;
   // per wave: one V buffer, or two when PV runs one tile behind QK; then the K area
   constexpr int kWaveBytes = (kDoubleBuffer<KT, VT, T> ? 2 : 1) * FV::kVbuf + F::kKarea;
-  // the combine, one B tile of rows at a time: [4 waves][kRT rows][256 + 4]
-  // floats (the pad puts the rows a column group writes in different banks
-  // and keeps them 16-byte aligned for vector writes; only a tile's live rows
-  // are kept, so one or two tokens leave room for a second workgroup per
-  // compute unit)
+  // the combine, kRT rows at a time: [4 waves][kRT rows][256 + 4] floats
+  // (the pad puts the rows a column group writes in different banks and
+  // keeps them 16-byte aligned for vector writes).  One or two tokens take
+  // their live rows in one pass; more tokens pass 8 rows at a time, which
+  // keeps the buffer within the per-wave tile buffers it reuses.
   constexpr int kRedStride = kHeadDim + 4;
-  constexpr int kRT = (R < 16) ? R : 16;
+  constexpr int kRT = (R < 16) ? R : 8;
+  constexpr int kPasses = (R + kRT - 1) / kRT;
   constexpr int kRed = 4 * kRT * kRedStride * 4;
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
   constexpr int kQLds = NT * C::kParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
-  __shared__ __attribute__((aligned(16))) int grp_lds[kGrpCap];
+  // the group list: half as long (chunks up to 8192 positions) for three or
+  // more tokens, whose LDS must leave room for a second workgroup; longer
+  // chunks read the block table directly
+  constexpr int kGrpN = (T <= 2) ? kGrpCap : kGrpCap / 2;
+  __shared__ __attribute__((aligned(16))) int grp_lds[kGrpN];
   __shared__ float ml_lds[4][R][2];
   __shared__ float row_stat[2][R];                   // per row: 1 / sum of weights, log2-sum-exp
   __shared__ long long sh_sum[kPlanShared];
@@ -1087,9 +1100,9 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   // indices are int32: pools of fewer than 2^31 rows per KV-head set.
   Pages pg{(lds_int*)(grp_lds), false};
   const int n_grp = 2 * n_tiles;                        // the tiles' groups (the last may lie past k1)
-  const bool grp_fits = p.bt != nullptr && n_grp <= kGrpCap &&
+  const bool grp_fits = p.bt != nullptr && n_grp <= kGrpN &&
                         static_cast<long long>(p.n_pool_blocks) * kKvHeads * p.page_size < (1ll << 31);
-  constexpr int kGrpPer = kGrpCap / kThreads;
+  constexpr int kGrpPer = kGrpN / kThreads;
   int grp_v[kGrpPer];
   auto page_of = [&](int pos) { return (p.page_shift >= 0) ? (pos >> p.page_shift) : pos / p.page_size; };
   if (grp_fits) {
@@ -1259,15 +1272,16 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
   const bool any_bad = (sh_bad[0] | sh_bad[1] | sh_bad[2] | sh_bad[3]) != 0;
   const float nan = __builtin_nanf("");
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (nt > 0) __syncthreads();                     // the previous tile's rows have been read
+  for (int q = 0; q < kPasses; ++q) {
+    if (q > 0) __syncthreads();                      // the previous pass's rows have been read
+    const int nt = (q * kRT) >> 4;                   // the B tile holding this pass's rows
     const int r = 16 * nt + n;
-    if (r < R) {
+    if (r < R && r >= q * kRT && r < q * kRT + kRT) {
       float M = kNegInf;
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][r][0]);
       const float a = (m_run[nt] == kNegInf) ? 0.f : exp2f(m_run[nt] - M);
-      float* dst = red + (wave * kRT + n) * kRedStride;
+      float* dst = red + (wave * kRT + (r - q * kRT)) * kRedStride;
 #pragma unroll
       for (int mt = 0; mt < 16; ++mt) {
         const f4 v = o[nt][mt] * a;
@@ -1282,8 +1296,8 @@ __global__ __launch_bounds__(256, (T <= 2) ? 2 : 1) void split_mfma_kernel(Decod
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int rr = 16 * nt + j;
+    for (int j = 0; j < kRT; ++j) {
+      const int rr = q * kRT + j;
       if (rr >= R) break;
       const int t = rr / 6, gq = rr % 6;
       const float sum = red[(0 * kRT + j) * kRedStride + tid] + red[(1 * kRT + j) * kRedStride + tid] +
