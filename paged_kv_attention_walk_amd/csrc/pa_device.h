@@ -377,6 +377,7 @@ __device__ inline int plan_prefix(const int32_t* __restrict__ lens, int s, int c
 // `shi` 4 ints.
 struct PlanWG {
   int chunk, s, c, prefix;
+  int len;      // seq_lens[s] when the host plan supplied it, else -1
 };
 
 __device__ inline long long wave_sum_ll(long long v) {
@@ -393,7 +394,7 @@ __device__ inline int wave_sum_i(int v) {
 
 __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
                                  int split, int slots, int j, int s_pref, long long* sh, int* shi) {
-  PlanWG r{0, -1, 0, 0};
+  PlanWG r{0, -1, 0, 0, -1};
   if (n_seq > 64) {
     r.chunk = plan_chunk(lens, n_seq, cap, target, budget, split, slots, sh);
     if (j >= 0) {
@@ -463,19 +464,53 @@ __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, in
 
 // The plan as plan_wg gives it, taken from the launch arguments when the
 // host computed it (no load, no barrier), else computed from seq_lens.
+// Lookup in the host plan's tables (launch arguments, n <= kHostPlanSeqs
+// entries): the last s in [0, n) with key[s] <= j, for a non-decreasing key
+// with key[0] <= j, and key[s], a[s], b[s].  Every lane reads its entries of
+// all three tables at once and a ballot counts the keys <= j: one round
+// trip to the argument memory instead of a binary search's chain of
+// dependent loads.  Called by whole waves.
+struct HostHit {
+  int s, key, a, b;
+};
+
+__device__ inline HostHit host_lookup(const int32_t* key, const int32_t* a, const int32_t* b, int n, int j) {
+  constexpr int kR = kHostPlanSeqs / 64;
+  const int lane = threadIdx.x & 63;
+  int kv[kR], av[kR], bv[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const int i = 64 * k + lane;
+    const bool in = i < n;
+    kv[k] = in ? key[i] : 0x7FFFFFFF;
+    av[k] = in ? a[i] : 0;
+    bv[k] = in ? b[i] : 0;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kR; ++k) cnt += __popcll(__ballot(kv[k] <= j));
+  HostHit r{cnt - 1, 0, 0, 0};
+  const int src = r.s & 63;
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    if ((r.s >> 6) == k) {
+      r.key = __builtin_amdgcn_readlane(kv[k], src);
+      r.a = __builtin_amdgcn_readlane(av[k], src);
+      r.b = __builtin_amdgcn_readlane(bv[k], src);
+    }
+  }
+  return r;
+}
+
 __device__ inline PlanWG plan_of(const DecodeParams& p, int cap, int j, int s_pref, long long* sh, int* shi) {
   if (p.hp.on) {
-    PlanWG r{p.hp.chunk, -1, 0, 0};
+    PlanWG r{p.hp.chunk, -1, 0, 0, -1};
     if (j >= 0 && j < p.hp.first[p.n_seq]) {
-      // the last s with first[s] <= j (first[] increases: every sequence has a pair)
-      int s = 0, hi = p.n_seq - 1;
-      while (s < hi) {
-        const int mid = (s + hi + 1) >> 1;
-        if (p.hp.first[mid] <= j) s = mid;
-        else hi = mid - 1;
-      }
-      r.s = s;
-      r.c = j - p.hp.first[s];
+      // first[] increases (every sequence has a chunk), so s owns item j
+      const HostHit hit = host_lookup(p.hp.first, p.hp.len, p.hp.len, p.n_seq, j);
+      r.s = hit.s;
+      r.c = j - hit.key;
+      r.len = hit.a;
     }
     if (s_pref >= 0) r.prefix = p.hp.first[s_pref];
     return r;
@@ -602,19 +637,16 @@ __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int cap = p.bt_stride * p.page_size;
   if (p.hp.on) {                                         // the host's plan, in the launch arguments
     const int j = blockIdx.x;
-    // the last s with mfirst[s] <= j (it owns workgroup j)
-    int s = 0, hi = p.n_seq - 1;
-    while (s < hi) {
-      const int mid = (s + hi + 1) >> 1;
-      if (p.hp.mfirst[mid] <= j) s = mid;
-      else hi = mid - 1;
-    }
-    const int nc = n_chunks_of(p.hp.len[s], cap, p.hp.chunk);
-    const int local = j - p.hp.mfirst[s];
+    // the last s with mfirst[s] <= j owns workgroup j (sequences without
+    // merge work repeat the next one's mfirst)
+    const HostHit hit = host_lookup(p.hp.mfirst, p.hp.len, p.hp.first, p.n_seq, j);
+    const int s = hit.s;
+    const int nc = n_chunks_of(hit.a, cap, p.hp.chunk);
+    const int local = j - hit.key;
     const bool one_wave = nc <= kMergeBatch;
     const int row = one_wave ? 4 * local + wave : local;
     if (row >= rows) return;
-    merge_one_row(p, s, row / R, row % R, nc, p.hp.first[s], one_wave, sh);
+    merge_one_row(p, s, row / R, row % R, nc, hit.b, one_wave, sh);
     return;
   }
   const int row_id = blockIdx.x;                         // one workgroup per row

@@ -974,7 +974,7 @@ __device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wa
   }
 }
 
-// Issue priority (set per tile in the double-buffered loop) follows the
+// Issue priority (set per tile in both loops below) follows the
 // share of this wave's tiles still to do.  Two workgroups share each compute
 // unit and the hardware favours the older wave of a SIMD; a wave that falls
 // behind its SIMD partner (which has the same share of work) gets ahead in
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
     if (s < kHdrSeqs) hdr[2 + s] = jj;
     if (s == 0) hdr[1] = chunk;
   }
-  const int L = seq_len_of(p, s);
+  const int L = p.hp.on ? pl.len : seq_len_of(p, s);
   const int nc = n_chunks_of(L, cap, chunk);
   // this chunk's partial rows in the workspace
   const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
@@ -1132,6 +1132,21 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
       }
     }
   };
+  // issue priority 3, 2, 1, 0 by the quarter of this wave's tiles still to
+  // do: it drops after own tile k = ((4 - j) total - 1) / 4, j = 3, 2, 1.
+  // Only when the grid is one round of resident workgroups: with more
+  // rounds, a workgroup that finishes early makes room for the next one.
+  const int my_total = (n_tiles - wave + 3) / 4;
+  const int kq3 = (my_total - 1) >> 2, kq2 = (2 * my_total - 1) >> 2, kq1 = (3 * my_total - 1) >> 2;
+  const bool one_round = p.max_items <= p.plan_slots;
+  auto set_prio = [&](int k) {                          // k: own index of the tile about to be staged
+    if (!one_round) return;
+    const int q = (k <= kq1) + (k <= kq2) + (k <= kq3);
+    if (q >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (q == 2) __builtin_amdgcn_s_setprio(2);
+    else if (q == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  };
   if constexpr (kDoubleBuffer<KT, VT, T>) {
     // Registers hold the next tile's loads while the current one is worked
     // on, and PV runs one tile behind: while tile i is staged, its QK^T and
@@ -1141,17 +1156,6 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
     uint8_t* wk = wl + 2 * FV::kVbuf;
     Tile<KT, VT> ta, tb2;
     int ti = wave;
-    // issue priority 3, 2, 1, 0 by the quarter of this wave's tiles still to
-    // do: it drops after own tile k = ((4 - j) total - 1) / 4, j = 3, 2, 1
-    const int my_total = (n_tiles - wave + 3) / 4;
-    const int kq3 = (my_total - 1) >> 2, kq2 = (2 * my_total - 1) >> 2, kq1 = (3 * my_total - 1) >> 2;
-    auto set_prio = [&](int k) {                        // k: own index of the tile about to be staged
-      const int q = (k <= kq1) + (k <= kq2) + (k <= kq3);
-      if (q >= 3) __builtin_amdgcn_s_setprio(3);
-      else if (q == 2) __builtin_amdgcn_s_setprio(2);
-      else if (q == 1) __builtin_amdgcn_s_setprio(1);
-      else __builtin_amdgcn_s_setprio(0);
-    };
     int kown = 1;
     QLoad<T> ql;
     i2 nrows = {0, 0};                    // LDS entries of this wave's next tile to load
@@ -1221,7 +1225,9 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
     __syncthreads();
     pg.in_lds = grp_fits;
     i2 nrows = (wave < n_tiles) ? read_rows(pg, wave) : i2{0, 0};
+    int kown = 0;
     for (int ti = wave; ti < n_tiles; ti += 4) {
+      set_prio(kown++);
       Tile<KT, VT> tt;
       load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * ti, k0, k1, tt, bad);
       if (ti + 4 < n_tiles) nrows = read_rows(pg, ti + 4);

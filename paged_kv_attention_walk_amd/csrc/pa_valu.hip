@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
     if (s < kHdrSeqs) hdr[2 + s] = j;
     if (s == 0) hdr[1] = chunk;
   }
-  const int L = seq_len_of(p, s);
+  const int L = p.hp.on ? pl.len : seq_len_of(p, s);
   const int nc = n_chunks_of(L, cap, chunk);
   const size_t part = (static_cast<size_t>(tok0 / 8) * p.part_items + item_id) * p.part_rows;
   const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of the group's token 0
