@@ -583,16 +583,22 @@ __device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT, VT>& t
 // QK result (lane (r, g) holds keys 4g..4g+3 of each 16-key half).
 __device__ inline int sigma(int g, int k) { return (k < 4) ? 4 * g + k : 16 + 4 * g + (k - 4); }
 
-// Query-row columns of the 16-wide B tiles.  With one token (6 rows) the hi
-// and lo halves share one tile: lane n < 8 carries the hi part of row n, lane
-// n + 8 the lo part of the same row, and the two partial results are added
-// across lanes n, n ^ 8.  With more tokens hi and lo take separate tiles.
+// Query-row columns of the 16-wide B tiles: tile nt holds rows 16 nt ..
+// 16 nt + 15, the hi and lo halves of q (and of the weights) in separate
+// MFMAs.  A last tile of at most 8 rows (one, three, four or six tokens) is
+// packed instead: lane n < 8 carries the hi part of row 16 nt + n, lane
+// n + 8 the lo part of the same row, one MFMA takes both, and the two
+// partial results are added across lanes n, n ^ 8.
 template <int T>
 struct Cols {
-  static constexpr bool kPack = (T == 1);
   static constexpr int R = 6 * T;
-  static constexpr int NT = kPack ? 1 : (R + 15) / 16;   // B tiles per part
-  static constexpr int kParts = kPack ? 1 : 2;          // hi / lo in separate MFMAs
+  static constexpr int NT = (R + 15) / 16;
+  static constexpr bool kPackLast = (R - 16 * (NT - 1)) <= 8;
+  static constexpr bool packed(int nt) { return kPackLast && nt == NT - 1; }
+  // q operand tiles per 32-dim block in LDS: two per tile, one if packed
+  static constexpr int kQParts = 2 * (NT - 1) + (kPackLast ? 1 : 2);
+  // query row of column n of tile nt
+  static constexpr int row(int nt, int n) { return 16 * nt + (packed(nt) ? (n & 7) : n); }
 };
 
 // Source of the QK^T B operands: an LDS copy laid out per (tile, part,
@@ -632,11 +638,12 @@ __device__ inline void qk_block(int b, const Tile<KT, VT>& t, const uint8_t* wk,
   constexpr int NT = C::NT;
   constexpr bool BF = F::kBf;
   const int g = (threadIdx.x & 63) >> 4;
-  u4 qb[NT][C::kParts];
+  u4 qb[NT][2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int part = 0; part < C::kParts; ++part) qb[nt][part] = qs.get(nt, part, b);
+  for (int nt = 0; nt < NT; ++nt) {
+    qb[nt][0] = qs.get(nt, 0, b);
+    if (!C::packed(nt)) qb[nt][1] = qs.get(nt, 1, b);
+  }
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     const u4 a = k_operand<KT, VT>(t, wk, hf, b);
@@ -645,14 +652,14 @@ __device__ inline void qk_block(int b, const Tile<KT, VT>& t, const uint8_t* wk,
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f4 cb = mma(a, qb[nt][0], f4{0.f, 0.f, 0.f, 0.f}, false);
-        if constexpr (C::kParts == 2) cb = mma(a, qb[nt][1], cb, false);
+        if (!C::packed(nt)) cb = mma(a, qb[nt][1], cb, false);
         sacc[nt][hf] += dk * cb;       // per-key block scale on the exact-code product
       }
     } else {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         sacc[nt][hf] = mma(a, qb[nt][0], sacc[nt][hf], BF);
-        if constexpr (C::kParts == 2) sacc[nt][hf] = mma(a, qb[nt][1], sacc[nt][hf], BF);
+        if (!C::packed(nt)) sacc[nt][hf] = mma(a, qb[nt][1], sacc[nt][hf], BF);
       }
     }
   }
@@ -660,11 +667,12 @@ __device__ inline void qk_block(int b, const Tile<KT, VT>& t, const uint8_t* wk,
 
 template <int T>
 __device__ inline void qk_finish(f4 (&sacc)[Cols<T>::NT][2]) {
-  if constexpr (Cols<T>::kPack) {
+  if constexpr (Cols<T>::kPackLast) {
+    constexpr int nt = Cols<T>::NT - 1;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[0][hf][i] += lane_xor8(sacc[0][hf][i]);
+      for (int i = 0; i < 4; ++i) sacc[nt][hf][i] += lane_xor8(sacc[nt][hf][i]);
   }
 }
 
@@ -760,11 +768,11 @@ __device__ inline bool softmax_tile(const f4 (&sacc)[Cols<T>::NT][2], const Tile
     }
     if constexpr (Fmt<VT>::kBf) {
       split8(x, bh[nt], bl[nt], true);
-      if constexpr (C::kPack) {
+      if (C::packed(nt)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) bh[nt][k] = lo_lane ? bl[nt][k] : bh[nt][k];
       }
-    } else if constexpr (C::kPack) {
+    } else if (C::packed(nt)) {
       u4 h, l;
       split8_rtz(x, h, l, -1.f);
 #pragma unroll
@@ -805,7 +813,7 @@ __device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>
           f4& acc = o[nt][2 * b + hm];
           acc = mma(ah[hm], bh[nt], acc, false);
           acc = mma(al[hm], bh[nt], acc, false);
-          if constexpr (C::kParts == 2) acc = mma(ah[hm], bl[nt], acc, false);
+          if (!C::packed(nt)) acc = mma(ah[hm], bl[nt], acc, false);
         }
       }
     } else {
@@ -821,7 +829,7 @@ __device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>
           f4& acc = o[nt][2 * b + hm];
           acc = mma(ah, bh[nt], acc, false);
           acc = mma(al, bh[nt], acc, false);
-          if constexpr (C::kParts == 2) acc = mma(ah, bl[nt], acc, false);
+          if (!C::packed(nt)) acc = mma(ah, bl[nt], acc, false);
         }
       }
     }
@@ -838,7 +846,7 @@ __device__ inline void pv_block(int b, const uint8_t* wv, const u4 (&bh)[Cols<T>
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         o[nt][mt] = mma(a, bh[nt], o[nt][mt], BF);
-        if constexpr (C::kParts == 2) o[nt][mt] = mma(a, bl[nt], o[nt][mt], BF);
+        if (!C::packed(nt)) o[nt][mt] = mma(a, bl[nt], o[nt][mt], BF);
       }
     }
   }
@@ -917,7 +925,7 @@ __device__ inline void load_q(const DecodeParams& p, int s, int h, int tok0, int
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
-    const int r = C::kPack ? (n & 7) : 16 * nt + n;
+    const int r = C::row(nt, n);
     const bool live = r < R;
     const float* qrow = p.q + ((static_cast<size_t>(s) * p.tok_total + tok0 + (live ? r / 6 : 0)) * kQHeads +
                                h * kGroup + (live ? r % 6 : 0)) * kHeadDim;
@@ -942,7 +950,7 @@ __device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wa
   const int lane = threadIdx.x & 63, n = lane & 15;
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
-    const int r = C::kPack ? (n & 7) : 16 * nt + n;
+    const int r = C::row(nt, n);
     const bool live = r < R;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -964,8 +972,8 @@ __device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wa
       for (int i = 0; i < 8; ++i) x[i] = live ? x[i] * p.scale_log2 : 0.f;
       u4 hi, lo;
       split8(x, hi, lo, Fmt<KT>::kBf);
-      if constexpr (C::kPack) {
-        *reinterpret_cast<u4*>(q_lds + b * 1024 + lane * 16) = (n & 8) ? lo : hi;
+      if (C::packed(nt)) {
+        *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 0) * 8 + b) * 1024 + lane * 16) = (n & 8) ? lo : hi;
       } else {
         *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 0) * 8 + b) * 1024 + lane * 16) = hi;
         *reinterpret_cast<u4*>(q_lds + ((nt * 2 + 1) * 8 + b) * 1024 + lane * 16) = lo;
@@ -1012,7 +1020,7 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
   constexpr int kPasses = (R + kRT - 1) / kRT;
   constexpr int kRed = 4 * kRT * kRedStride * 4;
   constexpr int kLds = (4 * kWaveBytes > kRed) ? 4 * kWaveBytes : kRed;
-  constexpr int kQLds = NT * C::kParts * 8 * 1024;
+  constexpr int kQLds = C::kQParts * 8 * 1024;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds];
   // the group list: half as long (chunks up to 8192 positions) for three or
@@ -1074,7 +1082,7 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
   const int lim_min = lim_base;                        // the first token's limit: every row sees <= lim_min
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int r = C::kPack ? (n & 7) : 16 * nt + n;    // query row of this lane's column
+    const int r = C::row(nt, n);                       // query row of this lane's column
     lim[nt] = lim_base + r / 6;                        // its token sees positions <= lim
   }
 
@@ -1237,11 +1245,11 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
       wave_lds_sync();
     }
   }
-  if constexpr (C::kPack) {     // add the lo-part columns into the hi-part columns
+  if constexpr (C::kPackLast) {     // add the lo-part columns into the hi-part columns
 #pragma unroll
     for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[0][mt][i] += lane_xor8(o[0][mt][i]);
+      for (int i = 0; i < 4; ++i) o[NT - 1][mt][i] += lane_xor8(o[NT - 1][mt][i]);
   }
 
   __builtin_amdgcn_s_setprio(0);
