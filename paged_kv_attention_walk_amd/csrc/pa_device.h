@@ -378,6 +378,7 @@ __device__ inline int plan_prefix(const int32_t* __restrict__ lens, int s, int c
 struct PlanWG {
   int chunk, s, c, prefix;
   int len;      // seq_lens[s] when the host plan supplied it, else -1
+  int item;     // plan index of chunk c of s (where its partial rows go)
 };
 
 __device__ inline long long wave_sum_ll(long long v) {
@@ -394,7 +395,7 @@ __device__ inline int wave_sum_i(int v) {
 
 __device__ inline PlanWG plan_wg(const int32_t* __restrict__ lens, int n_seq, int cap, int target, int budget,
                                  int split, int slots, int j, int s_pref, long long* sh, int* shi) {
-  PlanWG r{0, -1, 0, 0, -1};
+  PlanWG r{0, -1, 0, 0, -1, -1};
   if (n_seq > 64) {
     r.chunk = plan_chunk(lens, n_seq, cap, target, budget, split, slots, sh);
     if (j >= 0) {
@@ -502,21 +503,80 @@ __device__ inline HostHit host_lookup(const int32_t* key, const int32_t* a, cons
   return r;
 }
 
+// Chunk j of the grid's order in the host plan -> (sequence, chunk of it,
+// plan index).  In plan order, s is the last sequence with first[s] <= j.
+// In longest-first order (a grid of several rounds), chunk j < n_full is
+// the j-th full-length chunk: the last s with key[s] <= j, where key[s] =
+// first[s] - (sequences before s ending in a short chunk) counts the full
+// chunks before s; chunk j >= n_full is the short last chunk of sequence
+// ord[j - n_full].  Every lane reads its entries of first and len and the
+// mask words at once, whatever the order, so the common case takes one round
+// trip to the argument memory.  Called by whole waves.
+__device__ inline void host_plan_of(const HostPlan& hp, int n, int j, PlanWG& r) {
+  constexpr int kR = kHostPlanSeqs / 64, kW = kHostPlanSeqs / 32;
+  const int lane = threadIdx.x & 63;
+  int fv[kR], lv[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const int i = 64 * k + lane;
+    fv[k] = (i < n) ? hp.first[i] : 0;
+    lv[k] = (i < n) ? hp.len[i] : 0;
+  }
+  uint32_t mw[kW];
+#pragma unroll
+  for (int w = 0; w < kW; ++w) mw[w] = hp.pmask[w];
+  const bool lpt = hp.lpt != 0;
+  int kv[kR];
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    const int i = 64 * k + lane;
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const uint32_t bits = (w < (i >> 5)) ? mw[w] : (w == (i >> 5)) ? (mw[w] & ((1u << (i & 31)) - 1u)) : 0u;
+      before += __builtin_popcount(bits);
+    }
+    kv[k] = (i < n) ? fv[k] - (lpt ? before : 0) : 0x7FFFFFFF;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kR; ++k) cnt += __popcll(__ballot(kv[k] <= j));
+  const int s = cnt - 1, src = s & 63;
+  int key = 0, len = 0, f0 = 0;
+#pragma unroll
+  for (int k = 0; k < kR; ++k) {
+    if ((s >> 6) == k) {
+      key = __builtin_amdgcn_readlane(kv[k], src);
+      len = __builtin_amdgcn_readlane(lv[k], src);
+      f0 = __builtin_amdgcn_readlane(fv[k], src);
+    }
+  }
+  r.s = s;
+  r.c = j - key;
+  r.len = len;
+  r.item = f0 + r.c;
+  if (lpt && j >= hp.n_full && j < hp.first[n]) {        // a short last chunk, longest first
+    const int t = hp.ord[j - hp.n_full];
+    const int t0 = hp.first[t], nc = hp.first[t + 1] - t0;
+    r.s = t;
+    r.c = nc - 1;
+    r.len = hp.len[t];
+    r.item = t0 + nc - 1;
+  }
+  if (j < 0 || j >= hp.first[n]) r.s = -1;                 // no chunk
+}
+
 __device__ inline PlanWG plan_of(const DecodeParams& p, int cap, int j, int s_pref, long long* sh, int* shi) {
   if (p.hp.on) {
-    PlanWG r{p.hp.chunk, -1, 0, 0, -1};
-    if (j >= 0 && j < p.hp.first[p.n_seq]) {
-      // first[] increases (every sequence has a chunk), so s owns item j
-      const HostHit hit = host_lookup(p.hp.first, p.hp.len, p.hp.len, p.n_seq, j);
-      r.s = hit.s;
-      r.c = j - hit.key;
-      r.len = hit.a;
-    }
+    PlanWG r{p.hp.chunk, -1, 0, 0, -1, -1};
+    host_plan_of(p.hp, p.n_seq, j, r);
     if (s_pref >= 0) r.prefix = p.hp.first[s_pref];
     return r;
   }
-  return plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, p.split_target, p.plan_slots, j, s_pref,
-                 sh, shi);
+  PlanWG r = plan_wg(p.seq_lens, p.n_seq, cap, p.target_items, p.plan_budget, p.split_target, p.plan_slots, j,
+                     s_pref, sh, shi);
+  r.item = j;
+  return r;
 }
 
 // seq_lens[s], from the launch arguments with a host plan.

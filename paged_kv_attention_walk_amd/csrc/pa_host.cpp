@@ -3,6 +3,7 @@
 // extension struct, append staging, and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -186,6 +187,27 @@ void host_plan(const int32_t* lens, int n_seq, int cap, int target, int budget, 
     hp.len[i] = lens[i];
     if (nc > 1) hp.any_multi = 1;
   }
+  // longest-first order when the grid takes more than one round of resident
+  // workgroups
+  hp.lpt = (static_cast<long long>(kKvHeads) * hp.first[n_seq] > slots) ? 1 : 0;
+  hp.n_full = 0;
+  for (int w = 0; w < kHostPlanSeqs / 32; ++w) hp.pmask[w] = 0;
+  int order[kHostPlanSeqs], last_len[kHostPlanSeqs], n_short = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int L = lens[i];
+    const int nc = n_chunks(L, hp.chunk);
+    const int last = (L <= 0 || L > cap) ? 0 : L - (nc - 1) * hp.chunk;   // an empty sequence: one empty chunk
+    if (last == hp.chunk) {
+      hp.n_full += nc;
+    } else {
+      hp.n_full += nc - 1;
+      hp.pmask[i >> 5] |= 1u << (i & 31);
+      last_len[i] = last;
+      order[n_short++] = i;
+    }
+  }
+  std::stable_sort(order, order + n_short, [&](int a, int b) { return last_len[a] > last_len[b]; });
+  for (int k = 0; k < n_short; ++k) hp.ord[k] = static_cast<uint8_t>(order[k]);
 }
 
 }  // namespace pa

@@ -57,6 +57,16 @@ struct HostPlan {
   int32_t first[kHostPlanSeqs + 1]; // plan index of sequence s's first chunk; first[n_seq] = all pairs
   int32_t len[kHostPlanSeqs];       // seq_lens
   int32_t mfirst[kHostPlanSeqs + 1];// first merge workgroup of sequence s; mfirst[n_seq] = the merge grid
+  // Longest-first order of a grid of several rounds (lpt = 1): the split
+  // workgroups take every full-length chunk first (in plan order), then the
+  // shorter last chunks by decreasing length, so the last round holds the
+  // shortest work.  pmask bit s: sequence s ends in a chunk shorter than
+  // `chunk` (or is empty); n_full: chunks of full length; ord: the sequences
+  // with a short last chunk, longest first.  Results do not depend on it.
+  int32_t lpt;
+  int32_t n_full;
+  uint32_t pmask[kHostPlanSeqs / 32];
+  uint8_t ord[kHostPlanSeqs];
 };
 
 // Everything one decode launch needs.  Device pointers unless noted.

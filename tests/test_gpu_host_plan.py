@@ -32,6 +32,12 @@ CASES = [
     ("bf16", "bf16", 2, [333, 2048, 17], 64, "shuffled"),
     ("f16", "q8_0", 8, [4000, 300, 8], 32, "shuffled"),
     ("q4_0", "q4_0", 5, [2000] * 3, 16, "round_robin"),
+    # more work items than resident workgroups: the host plan hands out the
+    # full-length chunks first, then the short last chunks longest first
+    ("q4_0", "q8_0", 1, [int(x) for x in np.random.default_rng(31).integers(1, 4000, 200)] + [0, 1024, 2048, 3072],
+     32, "shuffled"),
+    ("bf16", "bf16", 2, [int(x) for x in np.random.default_rng(32).integers(500, 3000, 150)] + [4096] * 3 + [2304, 3456], 64,
+     "shuffled"),
 ]
 
 
