@@ -626,6 +626,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.plan_budget = static_cast<int32_t>(pp.budget);
   prm.split_target = static_cast<int32_t>(pp.split);
   prm.plan_slots = static_cast<int32_t>(pp.slots);
+  prm.n_cu = cu > 0 ? cu : 256;
   prm.tok_total = n_qtok;
   prm.tok0 = 0;
   prm.n_groups = 1;

@@ -87,6 +87,7 @@ struct DecodeParams {
   int32_t plan_budget;     // > 0: the plan takes the shortest chunk whose items fit in it
   int32_t split_target;    // > 0: the target of a ragged many-sequence batch (split_target)
   int32_t plan_slots;      // co-resident split workgroups (for ragged_split)
+  int32_t n_cu;            // compute units: the first n_cu workgroups of a grid land one per unit
   int32_t max_items;       // work items of the plan the grid covers (per token group)
   // Token groups: q / out / lse_out hold tok_total tokens per sequence; a
   // launch covers n_groups groups of the kernel's token count starting at

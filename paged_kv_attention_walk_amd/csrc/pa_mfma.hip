@@ -982,11 +982,16 @@ __device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wa
   }
 }
 
-// Issue priority (set per tile in both loops below) follows the
-// share of this wave's tiles still to do.  Two workgroups share each compute
-// unit and the hardware favours the older wave of a SIMD; a wave that falls
-// behind its SIMD partner (which has the same share of work) gets ahead in
-// issue instead of finishing alone at the end.  Results do not depend on it.
+// Issue priority (set per tile in both loops below).  Two workgroups share
+// each compute unit, and the hardware favours the older wave of a SIMD: with
+// equal work the second workgroup to arrive finishes several microseconds
+// after the first, and the kernel waits for it.  A wave takes priority 3, 2,
+// 1, 0 by the share of its tiles still to do, so that one that falls behind
+// its SIMD partner gets ahead in issue.  In the double-buffered loop the
+// first workgroup of each unit (the first n_cu of the grid) stays at 0
+// instead, which measured better there (the second one then catches up);
+// in the single-buffer loop both follow their share.  Results do not depend
+// on it.
 
 // Register double-buffering of the next tile pays for the compact quant rows;
 // the 16-bit rows use a single buffer (their loads are large enough that the
@@ -1142,15 +1147,17 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
     }
   };
   // issue priority 3, 2, 1, 0 by the quarter of this wave's tiles still to
-  // do: it drops after own tile k = ((4 - j) total - 1) / 4, j = 3, 2, 1.
-  // Only when the grid is one round of resident workgroups: with more
-  // rounds, a workgroup that finishes early makes room for the next one.
+  // do (it drops after own tile k = ((4 - j) total - 1) / 4, j = 3, 2, 1);
+  // with double buffering the first workgroup of a unit stays at 0.  Only
+  // when the grid is one round of resident workgroups: with more rounds, a
+  // workgroup that finishes early makes room for the next one.
   const int my_total = (n_tiles - wave + 3) / 4;
   const int kq3 = (my_total - 1) >> 2, kq2 = (2 * my_total - 1) >> 2, kq1 = (3 * my_total - 1) >> 2;
   const bool one_round = p.max_items <= p.plan_slots;
+  const bool follow = !kDoubleBuffer<KT, VT, T> || static_cast<int>(blockIdx.x) >= p.n_cu;
   auto set_prio = [&](int k) {                          // k: own index of the tile about to be staged
     if (!one_round) return;
-    const int q = (k <= kq1) + (k <= kq2) + (k <= kq3);
+    const int q = follow ? (k <= kq1) + (k <= kq2) + (k <= kq3) : 0;
     if (q >= 3) __builtin_amdgcn_s_setprio(3);
     else if (q == 2) __builtin_amdgcn_s_setprio(2);
     else if (q == 1) __builtin_amdgcn_s_setprio(1);
