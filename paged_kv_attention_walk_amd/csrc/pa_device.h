@@ -479,14 +479,16 @@ __device__ inline HostHit host_lookup(const int32_t* key, const int32_t* a, cons
   constexpr int kR = kHostPlanSeqs / 64;
   const int lane = threadIdx.x & 63;
   int kv[kR], av[kR], bv[kR];
+  // the reads do not wait for n: every table holds kHostPlanSeqs entries
 #pragma unroll
   for (int k = 0; k < kR; ++k) {
     const int i = 64 * k + lane;
-    const bool in = i < n;
-    kv[k] = in ? key[i] : 0x7FFFFFFF;
-    av[k] = in ? a[i] : 0;
-    bv[k] = in ? b[i] : 0;
+    kv[k] = key[i];
+    av[k] = a[i];
+    bv[k] = b[i];
   }
+#pragma unroll
+  for (int k = 0; k < kR; ++k) kv[k] = (64 * k + lane < n) ? kv[k] : 0x7FFFFFFF;
   int cnt = 0;
 #pragma unroll
   for (int k = 0; k < kR; ++k) cnt += __popcll(__ballot(kv[k] <= j));
@@ -516,11 +518,11 @@ __device__ inline void host_plan_of(const HostPlan& hp, int n, int j, PlanWG& r)
   constexpr int kR = kHostPlanSeqs / 64, kW = kHostPlanSeqs / 32;
   const int lane = threadIdx.x & 63;
   int fv[kR], lv[kR];
+  // the reads do not wait for n: the tables hold kHostPlanSeqs entries
 #pragma unroll
   for (int k = 0; k < kR; ++k) {
-    const int i = 64 * k + lane;
-    fv[k] = (i < n) ? hp.first[i] : 0;
-    lv[k] = (i < n) ? hp.len[i] : 0;
+    fv[k] = hp.first[64 * k + lane];
+    lv[k] = hp.len[64 * k + lane];
   }
   uint32_t mw[kW];
 #pragma unroll
@@ -566,8 +568,12 @@ __device__ inline void host_plan_of(const HostPlan& hp, int n, int j, PlanWG& r)
   if (j < 0 || j >= hp.first[n]) r.s = -1;                 // no chunk
 }
 
+// kSrc: 0 = the host plan if p.hp.on, else the device plan; 1 = the host
+// plan (a kernel instantiated for it reads the plan tables at once, without
+// first waiting on the flag); 2 = the device plan.
+template <int kSrc = 0>
 __device__ inline PlanWG plan_of(const DecodeParams& p, int cap, int j, int s_pref, long long* sh, int* shi) {
-  if (p.hp.on) {
+  if (kSrc == 1 || (kSrc == 0 && p.hp.on)) {
     PlanWG r{p.hp.chunk, -1, 0, 0, -1, -1};
     host_plan_of(p.hp, p.n_seq, j, r);
     if (s_pref >= 0) r.prefix = p.hp.first[s_pref];
@@ -690,12 +696,13 @@ __device__ inline void merge_one_row(const DecodeParams& p, int s, int h, int r,
   }
 }
 
+template <bool kHost>
 __device__ inline void merge_row(const DecodeParams& p, MergeShared& sh) {
   const int R = 6 * p.tok_total;                         // query rows of one (sequence, KV head)
   const int rows = kKvHeads * R;                         // query rows of a sequence
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int cap = p.bt_stride * p.page_size;
-  if (p.hp.on) {                                         // the host's plan, in the launch arguments
+  if constexpr (kHost) {                                 // the host's plan, in the launch arguments
     const int j = blockIdx.x;
     // the last s with mfirst[s] <= j owns workgroup j (sequences without
     // merge work repeat the next one's mfirst)

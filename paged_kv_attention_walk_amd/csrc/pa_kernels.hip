@@ -137,9 +137,12 @@ __global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint4* __res
 
 // ------------------------------------------------------------- dispatch
 
+// One instantiation per plan source, so that a host-planned merge reads its
+// plan tables without first waiting on the flag that selects them.
+template <bool kHost>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
   __shared__ MergeShared sh;
-  merge_row(p, sh);
+  merge_row<kHost>(p, sh);
 }
 
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
@@ -148,7 +151,10 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
                                : static_cast<unsigned>(p.n_seq) * kKvHeads * 6 * static_cast<unsigned>(p.tok_total);
   if (wgs == 0) return hipSuccess;
   const dim3 grid(wgs), block(kThreads);
-  hipLaunchKernelGGL(merge_kernel, grid, block, 0, stream, p);
+  if (p.hp.on)
+    hipLaunchKernelGGL(merge_kernel<true>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

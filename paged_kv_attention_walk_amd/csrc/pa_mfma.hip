@@ -1006,7 +1006,9 @@ constexpr bool kDoubleBuffer = (KT == kQ4_0 && VT == kQ4_0 && T == 1);
 template <int KT, int VT, int T>
 constexpr int kMinWgs = (T <= 2 || (T <= 4 && Fmt<VT>::kQuant)) ? 2 : 1;
 
-template <int KT, int VT, int T>
+// kHost: instantiated for a host-planned launch (p.hp.on), whose plan
+// lookup then starts without waiting on the flag.
+template <int KT, int VT, int T, bool kHost>
 __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(DecodeParams p) {
   using F = Fmt<KT>;
   using FV = Fmt<VT>;
@@ -1049,17 +1051,17 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
   const int item_id = blockIdx.x / p.n_groups;
   const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
   const int jj = item_id / kKvHeads, h = item_id % kKvHeads;
-  const PlanWG pl = plan_of(p, cap, jj, -1, sh_sum, sh_loc);
+  const PlanWG pl = plan_of<kHost ? 1 : 2>(p, cap, jj, -1, sh_sum, sh_loc);
   // every value that places loads is wave-uniform (scalar registers)
   const int chunk = __builtin_amdgcn_readfirstlane(pl.chunk);
   const int s = __builtin_amdgcn_readfirstlane(pl.s), c = __builtin_amdgcn_readfirstlane(pl.c);
   if (s < 0) return;
-  if (!p.hp.on && tid == 0 && c == 0 && h == 0 && tok0 == 0) {   // the plan, for the merge kernel
+  if (!kHost && tid == 0 && c == 0 && h == 0 && tok0 == 0) {     // the plan, for the merge kernel
     int32_t* hdr = reinterpret_cast<int32_t*>(p.err);
     if (s < kHdrSeqs) hdr[2 + s] = jj;
     if (s == 0) hdr[1] = chunk;
   }
-  const int L = p.hp.on ? pl.len : seq_len_of(p, s);
+  const int L = kHost ? pl.len : __builtin_amdgcn_readfirstlane(p.seq_lens[s]);
   const int nc = n_chunks_of(L, cap, chunk);
   // this chunk's partial rows in the workspace
   const size_t part =
@@ -1346,8 +1348,9 @@ template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, const SplitLaunch& l) {
   const dim3 grid(static_cast<unsigned>(grid_items(p)) * static_cast<unsigned>(p.n_groups));
   void* args[] = {const_cast<DecodeParams*>(&p)};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&split_mfma_kernel<KT, VT, PA_T>), grid, dim3(kThreads), args, 0,
-                            l.stream, l.start, l.stop, 0);
+  const void* f = p.hp.on ? reinterpret_cast<const void*>(&split_mfma_kernel<KT, VT, PA_T, true>)
+                          : reinterpret_cast<const void*>(&split_mfma_kernel<KT, VT, PA_T, false>);
+  return hipExtLaunchKernel(f, grid, dim3(kThreads), args, 0, l.stream, l.start, l.stop, 0);
 }
 
 template <int KT>
@@ -1366,8 +1369,14 @@ template <int KT, int VT>
 int wgs_per_cu() {
   static const int n = [] {
     int r = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, VT, PA_T>, kThreads, 0) != hipSuccess)
-      r = 1;
+    // both plan sources' instantiations: the smaller of the two
+    int r2 = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, split_mfma_kernel<KT, VT, PA_T, false>, kThreads, 0) !=
+            hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&r2, split_mfma_kernel<KT, VT, PA_T, true>, kThreads, 0) !=
+            hipSuccess)
+      r = r2 = 1;
+    r = r < r2 ? r : r2;
     return r < 1 ? 1 : (r > 4 ? 4 : r);
   }();
   return n;
