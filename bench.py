@@ -35,18 +35,20 @@ def parse():
     ap.add_argument("--workload", default="ragged",
                     choices=["ragged", "ragged_q8k_q4v", "uniform", "mtp", "f16", "serving", "prefill"],
                     help="ragged: 131072 + 7 x 8192 Q4_0 (the headline); ragged_q8k_q4v: same with Q8_0 K and Q4_0 V; "
-                         "uniform: 8 x 4096 Q4_0; mtp: one 131072-position Q8_0 sequence, --qtok query tokens; "
-                         "f16: one 1024-position F16 sequence; serving: 128 BF16 streams of 512..8192 positions in "
-                         "64-position pages, each step a device append of one float32 K/V row per stream "
-                         "(encoded to BF16 into its page) followed by the decode; prefill: one --ctx-position "
-                         "sequence, Q8_0 K and Q4_0 V, whose last --qtok positions are the new tokens (pa_prefill)")
+                         "uniform: --nseq x 4096 Q4_0; mtp: one --ctx-position Q8_0 sequence (default 131072), --qtok "
+                         "query tokens; f16: one 1024-position F16 sequence; serving: 128 BF16 streams of "
+                         "512..8192 positions in 64-position pages over 16 consecutive steps, each step an append "
+                         "of one K/V row per stream (see --append) followed by the decode; prefill: one "
+                         "--ctx-position sequence (default 16384), Q8_0 K and Q4_0 V, whose last --qtok positions "
+                         "are the new tokens (pa_prefill)")
     ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp / prefill")
     ap.add_argument("--append", default="host", choices=["device", "host"],
                     help="serving: the per-step append of one row per stream; host: pa_append_kv (rows already "
                          "BF16-encoded in host memory, one packed upload through pinned staging and a scatter "
                          "kernel); device: pa_append_kv_device (float32 rows already on the GPU, encoded into the "
                          "pool's BF16 on the way in)")
-    ap.add_argument("--ctx", type=int, default=16384, help="context for --workload prefill")
+    ap.add_argument("--ctx", type=int, default=None, help="context for --workload mtp (default 131072) and prefill "
+                                                          "(default 16384)")
     ap.add_argument("--nseq", type=int, default=8, help="sequences of 4096 positions for --workload uniform")
     ap.add_argument("--replicas", type=int, default=0, help="pool replicas for cold timing (0: auto)")
     ap.add_argument("--plan", default="host", choices=["host", "device"],
@@ -153,7 +155,7 @@ def ceiling_sweep(steps=10):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("pa_mfma.hip", "pa_kernels.hip", "pa_device.h", "pa_internal.h"):
+    for f in ("pa_mfma.hip", "pa_kernels.hip", "pa_device.h", "pa_internal.h", "pa_host.cpp"):
         h.update(open(os.path.join(ROOT, "paged_kv_attention_walk_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -259,11 +261,11 @@ def main():
     elif args.workload == "uniform":
         w = synth.config2(n_seq=args.nseq)
     elif args.workload == "mtp":
-        w = synth.config4(ctx=131072, n_qtok=args.qtok)
+        w = synth.config4(ctx=args.ctx or 131072, n_qtok=args.qtok)
     elif args.workload == "serving":
         w = synth.config5_rolling()
     elif args.workload == "prefill":
-        w = synth.prefill_workload(ctx=args.ctx, n_qtok=args.qtok)
+        w = synth.prefill_workload(ctx=args.ctx or 16384, n_qtok=args.qtok)
     else:
         w = synth.config1()
     print(f"[bench] workload {w['name']} generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
