@@ -39,7 +39,7 @@ inline int row_bytes_of(int t) {
 // workgroups the compact merge grid gives a sequence of nc chunks and `rows`
 // query rows (a row of up to kMergeBatch chunks is merged by one wave, four
 // rows per workgroup; a longer row by a workgroup; one chunk needs none).
-constexpr int kMergeBatch = 24;
+constexpr int kMergeBatch = 32;
 PA_HD inline int merge_wgs(int nc, int rows) {
   if (nc <= 1) return 0;
   return nc > kMergeBatch ? rows : (rows + 3) / 4;
