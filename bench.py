@@ -154,9 +154,15 @@ def ceiling_sweep(steps=10):
 
 
 def kernel_source_hash():
+    """Hash of the code (comments and blank space removed) of the sources that
+    decide what the split and merge kernels do and how they are launched."""
+    import re
     h = hashlib.sha256()
     for f in ("pa_mfma.hip", "pa_kernels.hip", "pa_device.h", "pa_internal.h", "pa_host.cpp"):
-        h.update(open(os.path.join(ROOT, "paged_kv_attention_walk_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "paged_kv_attention_walk_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

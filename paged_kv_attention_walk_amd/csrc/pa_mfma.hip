@@ -14,7 +14,7 @@
 //    16-byte pieces, are kept raw in LDS and read from there) and converted
 //    in-register to exact f16 values (codes for Q8_0 / Q4_0); the B operand
 //    is the 6*T query rows of the
-//    KV head (padded to 16 or 32), split as q = q_hi + q_lo in f16 (bf16 for
+//    KV head (in 16-column tiles), split as q = q_hi + q_lo in f16 (bf16 for
 //    BF16 K) so the products carry ~22 bits.  For Q8_0 / Q4_0 the block scale
 //    is applied per key to the fp32 result of each block's MFMA, so codes
 //    stay exact (llama.cpp pull 2, LDS-read commit, converts quants in
@@ -32,8 +32,9 @@
 // Accumulation is fp32 throughout.
 //
 // This source is built once per query-token count T (-DPA_T=T, 1..8): the
-// 6T query rows of a KV head take ceil(6T/16) B tiles of 16 columns (one
-// token packs hi and lo parts into one tile).
+// 6T query rows of a KV head take ceil(6T/16) B tiles of 16 columns, and a
+// last tile of at most 8 rows packs the hi and lo parts into one tile (one,
+// three, four and six tokens).
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
