@@ -260,3 +260,13 @@ def test_decode_scratch_rejects_bad_arguments():
     for T in (0, pb.MAX_QTOK + 1):
         assert pb.decode_scratch_status(a, a, a, a, a, 2, T, pb.kv_type("q4_0"), 16, a, 0, ext) == pb.ERR_INVALID
     assert pb.decode_scratch_status(a, a, a, a, a, -1, 1, pb.kv_type("q4_0"), 16, a, 0, ext) == pb.ERR_INVALID
+
+
+def test_header_constants_match_binding():
+    # the binding's copies of pa.h's flag and size macros
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    defs = {m[0]: int(m[1]) << int(m[2] or 0)
+            for m in re.findall(r"#define (PA_\w+) +\(?([0-9]+)u?(?: *<< *([0-9]+)\))?", text)}
+    assert defs["PA_DECODE_VECTOR_REFERENCE"] == pb.DECODE_VECTOR_REFERENCE
+    assert defs["PA_SCRATCH_BYTES"] == pb.SCRATCH_BYTES
+    assert defs["PA_MAX_QTOK"] == pb.MAX_QTOK
