@@ -383,8 +383,8 @@ pa_status pa_decode(const float *q, const void *k_pool, const void *v_pool,
  * read it with pa_get_device_error(NULL, NULL, stream, ...).
  * Errors: as pa_decode; PA_ERR_INVALID without ext or with a workspace in
  * it; PA_ERR_UNSUPPORTED when pa_decode_workspace_size(n_seq, n_qtok) on the
- * device exceeds PA_SCRATCH_BYTES (on 256 compute units: up to 2400
- * sequences of one token, 424 of four, 84 of eight). */
+ * device exceeds PA_SCRATCH_BYTES (on 256 compute units: up to 2463
+ * sequences of one token, 423 of four, 83 of eight). */
 #define PA_SCRATCH_BYTES (64u << 20)
 pa_status pa_decode_scratch(const float *q, const void *k_pool, const void *v_pool,
                             const int32_t *block_table, const int32_t *seq_lens,

@@ -270,3 +270,14 @@ def test_header_constants_match_binding():
     assert defs["PA_DECODE_VECTOR_REFERENCE"] == pb.DECODE_VECTOR_REFERENCE
     assert defs["PA_SCRATCH_BYTES"] == pb.SCRATCH_BYTES
     assert defs["PA_MAX_QTOK"] == pb.MAX_QTOK
+
+
+def test_scratch_batch_limits_documented():
+    # pa.h states the largest batches pa_decode_scratch takes on 256 compute
+    # units; they follow from pa_decode_workspace_size (256 CUs is also the
+    # size the library assumes without a device)
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    m = re.search(r"up to (\d+)\s+\*\s+sequences of one token, (\d+) of four, (\d+) of eight", text)
+    assert m, "scratch limits sentence not found in pa.h"
+    for n, T in zip(map(int, m.groups()), (1, 4, 8)):
+        assert pb.workspace_size(n, T, 0) <= pb.SCRATCH_BYTES < pb.workspace_size(n + 1, T, 0), (n, T)
