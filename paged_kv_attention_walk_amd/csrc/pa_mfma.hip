@@ -1001,11 +1001,13 @@ template <int KT, int VT, int T>
 constexpr bool kDoubleBuffer = (KT == kQ4_0 && VT == kQ4_0 && T == 1);
 
 // Workgroups per compute unit the kernel is compiled for: two (8 waves per
-// CU, at most 256 registers per lane) up to two tokens, and up to four
+// CU, at most 256 registers per lane) up to two tokens, and up to five
 // tokens with quantized V, whose per-wave LDS buffers are small enough for
 // two workgroups (with 16-bit V the buffers take one workgroup's share).
+// Six or more tokens hold three 16-column output tiles (192 registers) and
+// run one workgroup per CU.
 template <int KT, int VT, int T>
-constexpr int kMinWgs = (T <= 2 || (T <= 4 && Fmt<VT>::kQuant)) ? 2 : 1;
+constexpr int kMinWgs = (T <= 2 || (T <= 5 && Fmt<VT>::kQuant)) ? 2 : 1;
 
 // kHost: instantiated for a host-planned launch (p.hp.on), whose plan
 // lookup then starts without waiting on the flag.
