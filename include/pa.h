@@ -349,7 +349,12 @@ pa_status pa_split_workgroups_per_cu(int32_t kv_type, int32_t n_qtok, uint32_t f
  * work items, whose count and chunk sizes depend only on seq_lens, n_qtok and
  * the device's compute-unit count (so paged and contiguous storage give
  * bitwise-equal outputs), and a merge kernel for sequences split in several
- * chunks.  Errors: PA_ERR_INVALID (null pointers, n_qtok outside 1..8,
+ * chunks.  A call enqueues only these kernel launches on `stream` (no
+ * allocation, copy or memset), so it may be captured in a HIP graph.  With
+ * seq_lens_host the plan is fixed at capture and a replay must see the same
+ * lengths; without it the kernels read seq_lens when they run, so one
+ * capture serves every step of the same n_seq whose lengths fit the table.
+ * Calls with separate workspaces may run on several streams at once.  Errors: PA_ERR_INVALID (null pointers, n_qtok outside 1..8,
  * misaligned K/V (16 bytes) or q/out (16 bytes), workspace too small,
  * page_size or kv_type different from the pool's), PA_ERR_UNSUPPORTED (a
  * split or merge grid past 2^32 - 1 work items), PA_ERR_NOT_FOUND (ext NULL
