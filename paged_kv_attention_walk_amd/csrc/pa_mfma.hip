@@ -336,7 +336,10 @@ __device__ inline Half from_entry(int e, int pos0, int k1, bool& bad) {
 // 8g..8g+7 of every block of key m, as aligned dwords (blocks that start
 // 2 bytes off a dword boundary take one dword more and are funnel-shifted
 // when used); K scales: the dwords holding the scales of blocks 2g and 2g+1;
-// V: lane (j, seg) holds bytes [seg * 4 kVw, +4 kVw) of row j.  K and V
+// V: quant rows, lane (j, seg) holds bytes [seg * 4 kVw, +4 kVw) of row j
+// (whole blocks, split into codes and scales when staged); 16-bit rows,
+// load i brings rows 2i and 2i + 1 whole, lane l the 16 bytes at 16 (l % 32)
+// of row 2i + l / 32, so each load covers two rows contiguously.  K and V
 // may be of different types.
 template <int KT, int VT>
 struct Tile {
@@ -417,10 +420,10 @@ __device__ inline void load_tile(const DecodeParams& p, const Pages& pg, i2 rows
       t.ks[hf][1] = ld32(rk, m * F::kRow + 68 * g + 32);
     }
     if constexpr (VT == kF16 || VT == kBF16) {
-      const uint32_t o = j * FV::kRow + 128 * seg;
+      const uint32_t o = (lane >> 5) * FV::kRow + 16 * (lane & 31);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const u4a x = ld128(rv, o + 16 * i);
+        const u4a x = ld128(rv, o + 2 * i * FV::kRow);
         t.v[hf][4 * i] = x[0]; t.v[hf][4 * i + 1] = x[1]; t.v[hf][4 * i + 2] = x[2]; t.v[hf][4 * i + 3] = x[3];
       }
     } else {
@@ -488,9 +491,10 @@ __device__ inline void stage_tile(uint8_t* w, uint8_t* wk, const Tile<KT, VT>& t
     if constexpr (VT == kF16 || VT == kBF16) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        const int kr = 16 * hf + 2 * i + (lane >> 5);          // row of this lane's piece in load i
         u4 x = {t.v[hf][4 * i], t.v[hf][4 * i + 1], t.v[hf][4 * i + 2], t.v[hf][4 * i + 3]};
-        if (!valid) x = u4{0, 0, 0, 0};
-        *reinterpret_cast<u4*>(w + key * FV::kVks + 128 * seg + 16 * i) = x;
+        if (!(t.live[hf] && tb + kr < k1)) x = u4{0, 0, 0, 0};
+        *reinterpret_cast<u4*>(w + kr * FV::kVks + 16 * (lane & 31)) = x;
       }
     } else {
       float* vsc = reinterpret_cast<float*>(w + FV::kVtile);             // V scales: [8 blocks][4 groups][8] fp16
