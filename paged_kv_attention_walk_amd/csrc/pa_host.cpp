@@ -609,8 +609,13 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   // The plan aims at one round of resident workgroups (shared among the
   // token groups of a prefill); the workspace check above used the larger
   // capacity target, so these items always fit.
-  const int groups = prefill ? n_groups_of(n_qtok) : 1;
-  const int kernel_tok = n_qtok < kGroupTokens ? n_qtok : kGroupTokens;
+  // Tokens per split launch group: decode holds every token in one group up
+  // to five and halves six to eight (at most four tokens' output tiles per
+  // kernel, so two workgroups fit a compute unit); prefill takes eight.
+  // `groups` of them share one launch's grid.
+  const int group_tok = prefill ? kGroupTokens : ((engine == 0 && n_qtok >= 6) ? (n_qtok + 1) / 2 : n_qtok);
+  const int groups = prefill ? n_groups_of(n_qtok) : n_qtok / group_tok;
+  const int kernel_tok = n_qtok < group_tok ? n_qtok : group_tok;
   const int cu = cu_count(device);
   const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, kernel_tok, engine);
   const int64_t per_group_slots = slots / groups > 0 ? slots / groups : 1;
@@ -630,6 +635,7 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   prm.tok_total = n_qtok;
   prm.tok0 = 0;
   prm.n_groups = 1;
+  prm.group_tok = group_tok;
   prm.part_rows = 6 * workspace_rows_tokens(n_qtok, prefill);
   prm.part_items = prm.max_items;
   prm.k_type = kt;

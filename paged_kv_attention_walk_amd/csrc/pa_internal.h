@@ -89,13 +89,17 @@ struct DecodeParams {
   int32_t plan_slots;      // co-resident split workgroups (for ragged_split)
   int32_t n_cu;            // compute units: the first n_cu workgroups of a grid land one per unit
   int32_t max_items;       // work items of the plan the grid covers (per token group)
-  // Token groups: q / out / lse_out hold tok_total tokens per sequence; a
-  // launch covers n_groups groups of the kernel's token count starting at
-  // token tok0 (decode: one group, tok0 = 0, tok_total = n_qtok).  The grid is
-  // max_items x n_groups workgroups, the group index varying fastest.
-  int32_t tok_total, tok0, n_groups;
-  // Chunk partials of token group g (tokens 8g..) and plan item i start at
-  // row (g * part_items + i) * part_rows of part_o / part_lse.
+  // Token groups: q / out / lse_out hold tok_total tokens per sequence,
+  // taken group_tok at a time: the full groups in one launch (n_groups of
+  // them from token tok0, the group index varying fastest in a grid of
+  // max_items x n_groups workgroups), the rest in a second.  Decode takes
+  // every token in one group up to five tokens and two groups from six (so
+  // each kernel holds at most four tokens' output tiles); prefill groups of
+  // eight.
+  int32_t tok_total, tok0, n_groups, group_tok;
+  // Chunk partials of the tokens 8g.. 8g+7 and plan item i start at row
+  // (g * part_items + i) * part_rows of part_o / part_lse; token t's six
+  // rows sit 6 (t % 8) rows in.
   int32_t part_rows, part_items;
   int32_t k_type, v_type;
   int32_t engine;          // 0: matrix-core path, 1: fp32 vector reference path

@@ -190,32 +190,28 @@ int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine) {
 }
 
 // ev_begin / ev_end (optional) are attached to the split launches: begin to
-// the first, end to the last (the prefill takes two when its token count is
-// not a multiple of 8), so they time the split kernels' execution.
+// the first, end to the last (two launches when the token count is not a
+// multiple of the group size), so they time the split kernels' execution.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.n_seq <= 0) return hipSuccess;
+  const int gt = (p.group_tok >= 1 && p.group_tok <= kMaxQtok) ? p.group_tok
+                                                                  : (p.tok_total < kMaxQtok ? p.tok_total : kMaxQtok);
+  // the full groups in one launch, the rest in another
+  const int full = p.tok_total / gt, rest = p.tok_total % gt;
   hipError_t e = hipSuccess;
-  if (p.tok_total <= kMaxQtok) {
+  if (full > 0) {
     DecodeParams a = p;
-    a.n_qtok = p.tok_total;
-    a.n_groups = 1;
-    a.tok0 = 0;
-    e = launch_split(a, SplitLaunch{stream, ev_begin, ev_end});
-  } else {
-    // prefill: full groups of kMaxQtok tokens in one launch, the rest in another
-    const int full = p.tok_total / kMaxQtok, rest = p.tok_total % kMaxQtok;
-    DecodeParams a = p;
-    a.n_qtok = kMaxQtok;
+    a.n_qtok = gt;
     a.n_groups = full;
     a.tok0 = 0;
     e = launch_split(a, SplitLaunch{stream, ev_begin, rest > 0 ? nullptr : ev_end});
-    if (e == hipSuccess && rest > 0) {
-      DecodeParams b = p;
-      b.n_qtok = rest;
-      b.n_groups = 1;
-      b.tok0 = full * kMaxQtok;
-      e = launch_split(b, SplitLaunch{stream, nullptr, ev_end});
-    }
+  }
+  if (e == hipSuccess && rest > 0) {
+    DecodeParams b = p;
+    b.n_qtok = rest;
+    b.n_groups = 1;
+    b.tok0 = full * gt;
+    e = launch_split(b, SplitLaunch{stream, full > 0 ? nullptr : ev_begin, ev_end});
   }
   if (e != hipSuccess) return e;
   if (p.hp.on && !p.hp.any_multi) return hipSuccess;   // every sequence wrote its rows directly

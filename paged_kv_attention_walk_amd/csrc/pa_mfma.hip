@@ -1072,7 +1072,8 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
   const int nc = n_chunks_of(L, cap, chunk);
   // this chunk's partial rows in the workspace
   const size_t part =
-      (static_cast<size_t>(tok0 / 8) * p.part_items + static_cast<size_t>(pl.item) * kKvHeads + h) * p.part_rows;
+      (static_cast<size_t>(tok0 / 8) * p.part_items + static_cast<size_t>(pl.item) * kKvHeads + h) * p.part_rows +
+      6 * (tok0 % 8);
   const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of token 0 of the group
 
   if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read

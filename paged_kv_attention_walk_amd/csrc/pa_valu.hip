@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kThreads) void split_valu_kernel(DecodeParams p) {
   const int L = p.hp.on ? pl.len : seq_len_of(p, s);
   const int nc = n_chunks_of(L, cap, chunk);
   const size_t part =
-      (static_cast<size_t>(tok0 / 8) * p.part_items + static_cast<size_t>(pl.item) * kKvHeads + h) * p.part_rows;
+      (static_cast<size_t>(tok0 / 8) * p.part_items + static_cast<size_t>(pl.item) * kKvHeads + h) * p.part_rows +
+      6 * (tok0 % 8);
   const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of the group's token 0
 
   if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
