@@ -413,8 +413,8 @@ pa_status pa_decode_workspace_size(int32_t n_seq, int32_t n_qtok, int32_t device
  * lse_out hold n_qtok tokens per sequence, and the K/V rows of all n_qtok new
  * tokens must already be in the pages (pa_append_kv / pa_append_kv_device).
  *
- * The tokens are taken in groups of 8 (48 query rows of a KV head per
- * workgroup).  Work items are (sequence, KV head, context chunk, token
+ * The tokens are taken in groups of 4 on the matrix-core path (24 query rows
+ * of a KV head per workgroup; 8 on the vector path).  Work items are (sequence, KV head, context chunk, token
  * group), the groups of one chunk run side by side so its K/V bytes are
  * shared through the caches, and a group skips the keys past its last token.
  * Chunk partials of every group are merged as in pa_decode.  The workspace

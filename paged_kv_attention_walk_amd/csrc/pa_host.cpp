@@ -511,8 +511,8 @@ PlanParams plan_params(int64_t n_seq, int64_t slots, int64_t cap_target) {
   return r;
 }
 
-// Decode and prefill: one implementation, the prefill taking its query
-// tokens in groups of 8 (one token group per workgroup).
+// Decode and prefill: one implementation, the query tokens taken in groups
+// (one token group per workgroup; see group_tok below).
 pa_status attend(const float* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
                  const int32_t* seq_lens, int32_t n_seq, int32_t n_qtok, int32_t kv_type, int32_t page_size,
                  float* out, hipStream_t stream, const pa_decode_ext* ext, bool prefill) {
@@ -609,12 +609,15 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   // The plan aims at one round of resident workgroups (shared among the
   // token groups of a prefill); the workspace check above used the larger
   // capacity target, so these items always fit.
-  // Tokens per split launch group: decode holds every token in one group up
-  // to five and halves six to eight (at most four tokens' output tiles per
-  // kernel, so two workgroups fit a compute unit); prefill takes eight.
-  // `groups` of them share one launch's grid.
-  const int group_tok = prefill ? kGroupTokens : ((engine == 0 && n_qtok >= 6) ? (n_qtok + 1) / 2 : n_qtok);
-  const int groups = prefill ? n_groups_of(n_qtok) : n_qtok / group_tok;
+  // Tokens per split launch group.  On the matrix-core path a kernel holds
+  // at most four tokens' output tiles from six tokens up, so two workgroups
+  // fit a compute unit: decode keeps up to five tokens in one group and
+  // halves six to eight, prefill takes groups of four.  The vector path
+  // takes decode whole and prefill in groups of eight.  `groups` of them
+  // share one launch's grid.
+  const int group_tok = prefill ? (engine == 0 ? 4 : kGroupTokens)
+                                : ((engine == 0 && n_qtok >= 6) ? (n_qtok + 1) / 2 : n_qtok);
+  const int groups = prefill ? (n_qtok + group_tok - 1) / group_tok : n_qtok / group_tok;
   const int kernel_tok = n_qtok < group_tok ? n_qtok : group_tok;
   const int cu = cu_count(device);
   const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, kernel_tok, engine);

@@ -92,10 +92,11 @@ struct DecodeParams {
   // Token groups: q / out / lse_out hold tok_total tokens per sequence,
   // taken group_tok at a time: the full groups in one launch (n_groups of
   // them from token tok0, the group index varying fastest in a grid of
-  // max_items x n_groups workgroups), the rest in a second.  Decode takes
-  // every token in one group up to five tokens and two groups from six (so
-  // each kernel holds at most four tokens' output tiles); prefill groups of
-  // eight.
+  // max_items x n_groups workgroups), the rest in a second.  On the
+  // matrix-core path decode takes every token in one group up to five
+  // tokens and two groups from six, prefill groups of four (so each kernel
+  // holds at most four tokens' output tiles); the vector path takes decode
+  // whole and prefill in groups of eight.
   int32_t tok_total, tok0, n_groups, group_tok;
   // Chunk partials of the tokens 8g.. 8g+7 and plan item i start at row
   // (g * part_items + i) * part_rows of part_o / part_lse; token t's six

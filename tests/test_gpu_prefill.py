@@ -1,5 +1,5 @@
 """GPU parity of pa_prefill (paged chunked prefill: more query tokens than a
-decode step, taken in groups of 8) against the float64 oracle, through the
+decode step, taken in token groups) against the float64 oracle, through the
 C ABI."""
 
 import numpy as np
