@@ -307,9 +307,12 @@ pa_status pa_split_plan(const int32_t *seq_lens_host, int32_t n_seq, int32_t cap
                         int32_t wgs_per_cu, int32_t *chunk, int32_t *n_items, int32_t *first);
 
 /* Resident split workgroups per compute unit that pa_decode / pa_prefill
- * plan with for `kv_type`, `n_qtok` query tokens (1..PA_MAX_QTOK; prefill
- * uses 8 per group) and `flags` (pa_decode_ext.flags) on the current device:
- * the runtime's occupancy query for the kernel the call launches.  Pass it
+ * plan with for `kv_type`, `n_qtok` query tokens (1..PA_MAX_QTOK) and `flags`
+ * (pa_decode_ext.flags) on the current device: the runtime's occupancy query
+ * for the kernel the call launches.  On the matrix-core path a decode call
+ * of 6..8 tokens runs as two token groups of at most four and a prefill in
+ * groups of four (pass 4 for it); the vector path runs a decode whole and a
+ * prefill in groups of eight.  Pass it
  * to pa_split_plan to reproduce a call's partition.
  * Errors: PA_ERR_INVALID (null wgs, a bad kv_type, n_qtok or flags);
  * PA_ERR_HIP (no usable device). */

@@ -26,7 +26,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-function"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
-MAX_QTOK = 8   # query tokens per sequence (one split-kernel object per count)
+MAX_QTOK = 8        # query tokens per decode call (one vector-path split-kernel object per count)
+MFMA_MAX_QTOK = 5   # tokens of one matrix-core launch group (larger calls run as groups)
 
 
 def _run(cmd, verbose):
@@ -63,8 +64,8 @@ def build(verbose: bool = True) -> str:
         o = os.path.join(BUILD_DIR, name + ".o")
         cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
         objs.append(o)
-    for name in ("pa_mfma", "pa_valu"):
-        for t in range(1, MAX_QTOK + 1):
+    for name, top in (("pa_mfma", MFMA_MAX_QTOK), ("pa_valu", MAX_QTOK)):
+        for t in range(1, top + 1):
             o = os.path.join(BUILD_DIR, f"{name}_t{t}.o")
             cmds.append([hipcc, *HIP_FLAGS, *inc, f"-DPA_T={t}", "-c", os.path.join(CSRC, name + ".hip"), "-o", o])
             objs.append(o)

@@ -166,9 +166,10 @@ hipError_t launch_split(const DecodeParams& p, const SplitLaunch& l) {
     case 3: return valu ? launch_split_valu_t<3>(p, l) : launch_split_mfma_t<3>(p, l);
     case 4: return valu ? launch_split_valu_t<4>(p, l) : launch_split_mfma_t<4>(p, l);
     case 5: return valu ? launch_split_valu_t<5>(p, l) : launch_split_mfma_t<5>(p, l);
-    case 6: return valu ? launch_split_valu_t<6>(p, l) : launch_split_mfma_t<6>(p, l);
-    case 7: return valu ? launch_split_valu_t<7>(p, l) : launch_split_mfma_t<7>(p, l);
-    case 8: return valu ? launch_split_valu_t<8>(p, l) : launch_split_mfma_t<8>(p, l);
+    // the matrix-core path runs at most five tokens per launch group
+    case 6: return valu ? launch_split_valu_t<6>(p, l) : hipErrorInvalidValue;
+    case 7: return valu ? launch_split_valu_t<7>(p, l) : hipErrorInvalidValue;
+    case 8: return valu ? launch_split_valu_t<8>(p, l) : hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -183,9 +184,8 @@ int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine) {
     case 3: return split_mfma_wgs_t<3>(k_type, v_type);
     case 4: return split_mfma_wgs_t<4>(k_type, v_type);
     case 5: return split_mfma_wgs_t<5>(k_type, v_type);
-    case 6: return split_mfma_wgs_t<6>(k_type, v_type);
-    case 7: return split_mfma_wgs_t<7>(k_type, v_type);
-    default: return split_mfma_wgs_t<8>(k_type, v_type);
+    case 6: return split_mfma_wgs_t<3>(k_type, v_type);   // two groups of three
+    default: return split_mfma_wgs_t<4>(k_type, v_type);  // seven and eight: groups of four
   }
 }
 
@@ -194,8 +194,8 @@ int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine) {
 // multiple of the group size), so they time the split kernels' execution.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.n_seq <= 0) return hipSuccess;
-  const int gt = (p.group_tok >= 1 && p.group_tok <= kMaxQtok) ? p.group_tok
-                                                                  : (p.tok_total < kMaxQtok ? p.tok_total : kMaxQtok);
+  const int gt = p.group_tok;
+  if (gt < 1 || gt > kMaxQtok) return hipErrorInvalidValue;
   // the full groups in one launch, the rest in another
   const int full = p.tok_total / gt, rest = p.tok_total % gt;
   hipError_t e = hipSuccess;

@@ -31,10 +31,11 @@
 //    probabilities are split hi + lo like q.
 // Accumulation is fp32 throughout.
 //
-// This source is built once per query-token count T (-DPA_T=T, 1..8): the
-// 6T query rows of a KV head take ceil(6T/16) B tiles of 16 columns, and a
-// last tile of at most 8 rows packs the hi and lo parts into one tile (one,
-// three, four and six tokens).
+// This source is built once per query-token count T (-DPA_T=T, 1..5; a call
+// of more tokens runs as token groups of at most four): the 6T query rows of
+// a KV head take ceil(6T/16) B tiles of 16 columns, and a last tile of at
+// most 8 rows packs the hi and lo parts into one tile (one, three and four
+// tokens).
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -46,6 +47,7 @@
 #ifndef PA_T
 #error "build with -DPA_T=<query tokens>"
 #endif
+static_assert(PA_T >= 1 && PA_T <= 5, "matrix-core launch groups hold 1..5 tokens");
 
 namespace pa {
 namespace {
