@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import attention
+from paged_kv_attention_walk_amd import binding as pb
 from paged_kv_attention_walk_amd import synth
 from gpu_util import log, parity, run
 from test_gpu_prefill import run_prefill
@@ -149,3 +150,17 @@ def test_device_plan_equals_host_plan(seed):
     chunk, items, first = pb.split_plan(w["seq_lens"], w["block_table"].shape[1] * 16, n_cu, wgs)
     assert hdr[1] == chunk, (hdr[1], chunk)
     assert list(hdr[2:2 + n]) == list(first[:n])
+
+
+def test_occupancy_query_follows_the_launch_groups():
+    # on the matrix-core path a call of 6..8 tokens runs as two groups of at
+    # most four: the occupancy it plans with is the group kernel's; and the
+    # kernels of up to five tokens with quantized V fit two workgroups per
+    # compute unit (Q4_0 K with Q8_0 V only at one token)
+    for kv in ("q8_0", "q4_0", "bf16", "f16", pb.kv_type("q8_0", "q4_0")):
+        w = {t: pb.split_workgroups_per_cu(kv, t) for t in range(1, 9)}
+        log(f"[occupancy] {kv}: {w}")
+        assert w[6] == w[3] and w[7] == w[4] and w[8] == w[4], w
+    for kv in ("q8_0", "q4_0", pb.kv_type("q8_0", "q4_0"), pb.kv_type("f16", "q4_0")):
+        assert all(pb.split_workgroups_per_cu(kv, t) == 2 for t in range(1, 6)), kv
+    assert pb.split_workgroups_per_cu("bf16", 1) == 2
