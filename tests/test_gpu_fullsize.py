@@ -86,7 +86,7 @@ def test_ragged_128k_7x8k_q4_0_whole(engine):
     _whole(out, w, "ragged")
 
 
-@pytest.mark.parametrize("ctx,T", [(32768, 1), (32768, 4), (131072, 1), (131072, 2), (131072, 3), (131072, 4), (131072, 5),
+@pytest.mark.parametrize("ctx,T", [(32768, 1), (32768, 4), (131072, 1), (131072, 2), (131072, 3), (131072, 4), (131072, 5), (131072, 8), (32768, 6),
                                    (262144, 1), (262144, 3)])
 def test_mtp_q8_0_whole(ctx, T):
     w = synth.config4(ctx=ctx, n_qtok=T)

@@ -54,6 +54,7 @@ CASES = [
     (("bf16", "bf16"), 64, [64, 1000, 130], 48),
     (("f16", "q8_0"), 100, [100, 2100], 256),
     (("q4_0", "bf16"), 23, [1, 23, 1500, 777], 32),
+    (("q8_0", "q8_0"), 10, [10, 3000, 6], 16),             # groups of four and a rest of two
 ]
 
 
