@@ -42,6 +42,8 @@ def parse():
                          "--ctx-position sequence (default 16384), Q8_0 K and Q4_0 V, whose last --qtok positions "
                          "are the new tokens (pa_prefill)")
     ap.add_argument("--qtok", type=int, default=4, help="query tokens for --workload mtp / prefill")
+    ap.add_argument("--kv", default="q8_0", choices=["q8_0", "q4_0", "bf16", "f16"],
+                    help="K and V encoding of --workload mtp (default q8_0)")
     ap.add_argument("--append", default="host", choices=["device", "host"],
                     help="serving: the per-step append of one row per stream; host: pa_append_kv (rows already "
                          "BF16-encoded in host memory, one packed upload through pinned staging and a scatter "
@@ -267,7 +269,7 @@ def main():
     elif args.workload == "uniform":
         w = synth.config2(n_seq=args.nseq)
     elif args.workload == "mtp":
-        w = synth.config4(ctx=args.ctx or 131072, n_qtok=args.qtok)
+        w = synth.config4(ctx=args.ctx or 131072, n_qtok=args.qtok, kind=args.kv)
     elif args.workload == "serving":
         w = synth.config5_rolling()
     elif args.workload == "prefill":

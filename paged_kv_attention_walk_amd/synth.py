@@ -248,10 +248,10 @@ def ragged_mixed(seed=3, k_kind="q8_0", v_kind="q4_0"):
                          table="round_robin", seed=seed)
 
 
-def config4(ctx=32768, n_qtok=1, seed=4):
-    """One sequence, 1-4 query tokens with a causal mask among them, Q8_0 K/V,
-    256-token shuffled pages."""
-    return make_workload(f"q8_0_1x{ctx}_t{n_qtok}_p256_shuffled", [ctx], n_qtok, "q8_0", "q8_0", 256,
+def config4(ctx=32768, n_qtok=1, seed=4, kind="q8_0"):
+    """One sequence, 1-4 query tokens with a causal mask among them, Q8_0 K/V
+    (or `kind` for both), 256-token shuffled pages."""
+    return make_workload(f"{kind}_1x{ctx}_t{n_qtok}_p256_shuffled", [ctx], n_qtok, kind, kind, 256,
                          table="shuffled", seed=seed)
 
 
