@@ -627,7 +627,8 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   // plan's items per token group times the groups; merge: one workgroup per
   // query row at most) must fit before anything is enqueued.
   const int64_t max_wgs = ((1ll << 32) - 1) / 256;
-  if (pp.max_items * groups > max_wgs || static_cast<int64_t>(n_seq) * PA_N_Q_HEADS * n_qtok > max_wgs)
+  const int64_t items_padded = groups > 1 ? (pp.max_items + 7) / 8 * 8 : pp.max_items;   // blocks of 8 with groups
+  if (items_padded * groups > max_wgs || static_cast<int64_t>(n_seq) * PA_N_Q_HEADS * n_qtok > max_wgs)
     return PA_ERR_UNSUPPORTED;
   prm.target_items = static_cast<int32_t>(pp.target);
   prm.max_items = static_cast<int32_t>(pp.max_items);

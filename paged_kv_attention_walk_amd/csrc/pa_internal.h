@@ -91,8 +91,9 @@ struct DecodeParams {
   int32_t max_items;       // work items of the plan the grid covers (per token group)
   // Token groups: q / out / lse_out hold tok_total tokens per sequence,
   // taken group_tok at a time: the full groups in one launch (n_groups of
-  // them from token tok0, the group index varying fastest in a grid of
-  // max_items x n_groups workgroups), the rest in a second.  On the
+  // them from token tok0; the groups of one item sit 8 workgroups apart on
+  // one XCD, in a grid of max_items, rounded up to 8 with several groups, x
+  // n_groups workgroups), the rest in a second.  On the
   // matrix-core path decode takes every token in one group up to five
   // tokens and two groups from six, prefill groups of four (so each kernel
   // holds at most four tokens' output tiles); the vector path takes decode

@@ -1055,9 +1055,12 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
   const int n = lane & 15, g = lane >> 4;
   const int cap = p.bt_stride * p.page_size;
 
-  // token group fastest: the groups of one chunk run side by side
-  const int grp = blockIdx.x % p.n_groups;
-  const int item_id = blockIdx.x / p.n_groups;
+  // Token groups: workgroup b takes item 8 (b / 8G) + b % 8 and group
+  // (b / 8) % G, so the G groups of one chunk are dispatched 8 apart with the
+  // same b % 8: on one XCD, sharing its L2 for the chunk's K/V, side by side
+  const int bx = static_cast<int>(blockIdx.x);
+  const int grp = (p.n_groups == 1) ? 0 : (bx / 8) % p.n_groups;
+  const int item_id = (p.n_groups == 1) ? bx : (bx / (8 * p.n_groups)) * 8 + bx % 8;
   const int tok0 = p.tok0 + T * grp;                   // first token of this workgroup's rows
   const int jj = item_id / kKvHeads, h = item_id % kKvHeads;
   const PlanWG pl = plan_of<kHost ? 1 : 2>(p, cap, jj, -1, sh_sum, sh_loc);
@@ -1356,7 +1359,10 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
 
 template <int KT, int VT>
 hipError_t launch_kvt(const DecodeParams& p, const SplitLaunch& l) {
-  const dim3 grid(static_cast<unsigned>(grid_items(p)) * static_cast<unsigned>(p.n_groups));
+  // with token groups, items in whole blocks of 8 (the padding workgroups
+  // find no plan item and return)
+  const unsigned items = static_cast<unsigned>(grid_items(p));
+  const dim3 grid(p.n_groups == 1 ? items : (items + 7) / 8 * 8 * static_cast<unsigned>(p.n_groups));
   void* args[] = {const_cast<DecodeParams*>(&p)};
   const void* f = p.hp.on ? reinterpret_cast<const void*>(&split_mfma_kernel<KT, VT, PA_T, true>)
                           : reinterpret_cast<const void*>(&split_mfma_kernel<KT, VT, PA_T, false>);
