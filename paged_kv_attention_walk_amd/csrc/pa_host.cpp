@@ -612,12 +612,15 @@ pa_status attend(const float* q, const void* k_pool, const void* v_pool, const i
   // Tokens per split launch group.  On the matrix-core path a kernel holds
   // at most four tokens' output tiles from six tokens up, so two workgroups
   // fit a compute unit: decode keeps up to five tokens in one group and
-  // halves six to eight, prefill takes groups of four.  The vector path
-  // takes decode whole and prefill in groups of eight.  `groups` of them
-  // share one launch's grid.
-  const int group_tok = prefill ? (engine == 0 ? 4 : kGroupTokens)
-                                : ((engine == 0 && n_qtok >= 6) ? (n_qtok + 1) / 2 : n_qtok);
-  const int groups = prefill ? (n_qtok + group_tok - 1) / group_tok : n_qtok / group_tok;
+  // halves six to eight (seven: a group of four and one of three in the
+  // four-token kernel), prefill takes groups of four, the last possibly
+  // partial.  The vector path takes decode whole and prefill in groups of
+  // eight.  `groups` of them share one launch's grid (the vector path runs a
+  // partial last group in a launch of its own).
+  int group_tok = prefill ? (engine == 0 ? 4 : kGroupTokens)
+                          : ((engine == 0 && n_qtok >= 6) ? (n_qtok + 1) / 2 : n_qtok);
+  if (group_tok > n_qtok) group_tok = n_qtok;
+  const int groups = (n_qtok + group_tok - 1) / group_tok;
   const int kernel_tok = n_qtok < group_tok ? n_qtok : group_tok;
   const int cu = cu_count(device);
   const int64_t slots = static_cast<int64_t>(cu > 0 ? cu : 256) * pa::split_wgs_per_cu(kt, vt, kernel_tok, engine);

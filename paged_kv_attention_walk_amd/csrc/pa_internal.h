@@ -90,14 +90,15 @@ struct DecodeParams {
   int32_t n_cu;            // compute units: the first n_cu workgroups of a grid land one per unit
   int32_t max_items;       // work items of the plan the grid covers (per token group)
   // Token groups: q / out / lse_out hold tok_total tokens per sequence,
-  // taken group_tok at a time.  The full groups run in one launch (n_groups
-  // of them from token tok0, in a grid of max_items x n_groups workgroups,
-  // max_items rounded up to 8 when there are several groups, whose groups of
-  // one item sit 8 workgroups apart on one XCD); the rest in a second.  On
-  // the matrix-core path decode takes up to five tokens in one group and six
-  // to eight in two, prefill groups of four (so no kernel holds more than
-  // four tokens' output tiles from six tokens up); the vector path takes
-  // decode whole and prefill in groups of eight.
+  // taken group_tok at a time.  On the matrix-core path every group runs
+  // in one launch (n_groups of them from token tok0, in a grid of max_items
+  // x n_groups workgroups, max_items rounded up to 8 when there are several
+  // groups, whose groups of one item sit 8 workgroups apart on one XCD), a
+  // partial last group masking its missing tokens; decode takes up to five
+  // tokens in one group and six to eight in two, prefill groups of four (so
+  // no kernel holds more than four tokens' output tiles from six tokens up).
+  // The vector path takes decode whole and prefill in groups of eight, the
+  // full groups in one launch and the rest in a second.
   int32_t tok_total, tok0, n_groups, group_tok;
   // Chunk partials of the tokens 8g.. 8g+7 and plan item i start at row
   // (g * part_items + i) * part_rows of part_o / part_lse; token t's six

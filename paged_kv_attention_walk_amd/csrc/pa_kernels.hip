@@ -196,8 +196,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t e
   if (p.n_seq <= 0) return hipSuccess;
   const int gt = p.group_tok;
   if (gt < 1 || gt > kMaxQtok) return hipErrorInvalidValue;
-  // the full groups in one launch, the rest in another
-  const int full = p.tok_total / gt, rest = p.tok_total % gt;
+  // the matrix-core kernels mask the missing tokens of a partial last group:
+  // every group in one launch; the vector path runs the full groups in one
+  // launch and the rest in another
+  const bool whole = p.engine == 0;
+  const int full = whole ? (p.tok_total + gt - 1) / gt : p.tok_total / gt;
+  const int rest = whole ? 0 : p.tok_total % gt;
   hipError_t e = hipSuccess;
   if (full > 0) {
     DecodeParams a = p;

@@ -925,15 +925,17 @@ struct QLoad {
   float4 v[Cols<T>::NT][2][2];
 };
 
+// Rv: the query rows of the group's tokens (6 per token; fewer than 6T in
+// a last group that holds fewer tokens than the kernel).  Other rows read
+// row 0 and are zero.
 template <int KT, int T>
-__device__ inline void load_q(const DecodeParams& p, int s, int h, int tok0, int wave, QLoad<T>& ql) {
+__device__ inline void load_q(const DecodeParams& p, int s, int h, int tok0, int wave, int Rv, QLoad<T>& ql) {
   using C = Cols<T>;
-  constexpr int R = C::R;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
     const int r = C::row(nt, n);
-    const bool live = r < R;
+    const bool live = r < Rv;
     const float* qrow = p.q + ((static_cast<size_t>(s) * p.tok_total + tok0 + (live ? r / 6 : 0)) * kQHeads +
                                h * kGroup + (live ? r % 6 : 0)) * kHeadDim;
 #pragma unroll
@@ -951,14 +953,13 @@ __device__ inline void load_q(const DecodeParams& p, int s, int h, int tok0, int
 }
 
 template <int KT, int T>
-__device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wave, uint8_t* q_lds) {
+__device__ inline void build_q(const DecodeParams& p, const QLoad<T>& ql, int wave, int Rv, uint8_t* q_lds) {
   using C = Cols<T>;
-  constexpr int R = C::R;
   const int lane = threadIdx.x & 63, n = lane & 15;
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) {
     const int r = C::row(nt, n);
-    const bool live = r < R;
+    const bool live = r < Rv;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int b = 2 * wave + bb;
@@ -1080,14 +1081,18 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
       (static_cast<size_t>(tok0 / 8) * p.part_items + static_cast<size_t>(pl.item) * kKvHeads + h) * p.part_rows +
       6 * (tok0 % 8);
   const size_t orow = static_cast<size_t>(s) * p.tok_total + tok0;   // output row of token 0 of the group
+  // rows of the group's tokens: a last group may hold fewer tokens than the
+  // kernel (matrix-core launches cover every token in whole groups); the
+  // rows past them are computed on a zero query and never written
+  const int Rv = 6 * min(T, p.tok_total - tok0);
 
   if (!len_ok(L, cap)) {   // corrupt length: NaN rows, nothing read
     const float nan = __builtin_nanf("");
-    for (int i = tid; i < R * kHeadDim; i += kThreads) {
+    for (int i = tid; i < Rv * kHeadDim; i += kThreads) {
       const int r = i / kHeadDim, d = i % kHeadDim, t = r / 6, gq = r % 6;
       p.out[((orow + t) * kQHeads + h * kGroup + gq) * kHeadDim + d] = nan;
     }
-    if (p.lse_out && tid < R) p.lse_out[(orow + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
+    if (p.lse_out && tid < Rv) p.lse_out[(orow + tid / 6) * kQHeads + h * kGroup + tid % 6] = nan;
     if (tid == 0) atomicOr(p.err, 2u);
     return;
   }
@@ -1190,10 +1195,10 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
     int kown = 1;
     QLoad<T> ql;
     i2 nrows = {0, 0};                    // LDS entries of this wave's next tile to load
-    load_q<KT, T>(p, s, h, tok0, wave, ql);
+    load_q<KT, T>(p, s, h, tok0, wave, Rv, ql);
     if (ti < n_tiles) load_tile<KT, VT>(p, pg, nrows, s, h, k0 + 32 * ti, k0, k1, ta, bad);
     stage_rows();
-    build_q<KT, T>(p, ql, wave, q_lds);
+    build_q<KT, T>(p, ql, wave, Rv, q_lds);
     __syncthreads();
     pg.in_lds = grp_fits;
     if (ti + 4 < n_tiles) nrows = read_rows(pg, ti + 4);
@@ -1249,9 +1254,9 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
     uint8_t* wk = wl + FV::kVbuf;
     {
       QLoad<T> ql;
-      load_q<KT, T>(p, s, h, tok0, wave, ql);
+      load_q<KT, T>(p, s, h, tok0, wave, Rv, ql);
       stage_rows();
-      build_q<KT, T>(p, ql, wave, q_lds);
+      build_q<KT, T>(p, ql, wave, Rv, q_lds);
     }
     __syncthreads();
     pg.in_lds = grp_fits;
@@ -1335,7 +1340,7 @@ __global__ __launch_bounds__(256, (kMinWgs<KT, VT, T>)) void split_mfma_kernel(D
 #pragma unroll
     for (int j = 0; j < kRT; ++j) {
       const int rr = q * kRT + j;
-      if (rr >= R) break;
+      if (rr >= Rv) break;                            // rows of tokens past the call's last
       const int t = rr / 6, gq = rr % 6;
       const float sum = red[(0 * kRT + j) * kRedStride + tid] + red[(1 * kRT + j) * kRedStride + tid] +
                         red[(2 * kRT + j) * kRedStride + tid] + red[(3 * kRT + j) * kRedStride + tid];
