@@ -190,8 +190,9 @@ int split_wgs_per_cu(int k_type, int v_type, int n_qtok, int engine) {
 }
 
 // ev_begin / ev_end (optional) are attached to the split launches: begin to
-// the first, end to the last (two launches when the token count is not a
-// multiple of the group size), so they time the split kernels' execution.
+// the first, end to the last (the vector path takes two when the token
+// count is not a multiple of its group size), so they time the split
+// kernels' execution.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (p.n_seq <= 0) return hipSuccess;
   const int gt = p.group_tok;
